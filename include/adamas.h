@@ -1,0 +1,155 @@
+/*
+ * adamas.h -- C ABI of the Adamas decode-step library (libadamas.so, gfx950).
+ *
+ * What the library computes (sources cited by page title and section):
+ *   "Adamas: Hadamard Sparse Attention for Efficient Long-Context Inference"
+ *   (arXiv 2510.18413), v1 and v2 abstracts: each query and key vector is
+ *   Hadamard-transformed, bucketized and compressed to 2 bits; a distance
+ *   estimate between the query's code and every key's code (Manhattan distance in
+ *   v1) picks the top-k positions under a token budget; the original K/V rows at
+ *   those positions are gathered and attended with exact softmax attention.
+ *   "ADAMAS：稀疏注意力优化技术解析与应用实践" (jsqmd.com blog): section 2.1 (the
+ *   transform, computed in O(n log n)), section 2.2 (dynamic thresholds
+ *   -t, 0, +t with t = half the largest magnitude, strict "<" tests),
+ *   section 2.3 (Manhattan distance on the integer codes), section 3.1 (key codes
+ *   are kept in a cache that is updated as keys are appended).
+ *
+ * Fixed readings where the pages are silent or garbled:
+ *   - head_dim is 128; the transform is the unnormalised Sylvester-Hadamard
+ *     matrix in natural order, computed in fp32 by butterflies of half-width
+ *     1, 2, 4, ..., 64 in that order (this fixes every rounding);
+ *   - t is computed per head vector (one 128-dimension group);
+ *   - codes are packed planar: bytes 0..15 hold the low bit of every code and
+ *     bytes 16..31 the high bit, code i at bit i%8 of byte i/8 of each plane;
+ *   - distance = sum over coordinates of |code_q - code_k|, in 0..384;
+ *   - top-k keeps the min(budget, kv_len) positions with the smallest
+ *     (distance, position) -- among equal distances the lower position wins;
+ *   - attention uses the original bf16 q (not the transformed one) and a
+ *     caller-supplied softmax scale (normally 1/sqrt(128));
+ *   - query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are caller-owned DEVICE pointers to contiguous,
+ *     row-major memory on the current HIP device.  bf16 tensors are passed as
+ *     their raw 16-bit storage.  `stream` is a hipStream_t passed as void*
+ *     (NULL = the null stream).
+ *   - Calls only enqueue work on `stream` and return; results are ready when the
+ *     stream reaches them.  No call allocates or frees device memory; scratch
+ *     memory is the caller's `workspace`.
+ *   - Arguments the host can check are validated before any HIP call; on failure
+ *     the call returns a status and enqueues nothing.  Values that live in
+ *     device memory (kv_len, start, end) are preconditions and are not checked.
+ *   - A failed launch returns ADAMAS_ERR_HIP.  The library keeps no mutable
+ *     global state; calls on different streams with different workspaces may
+ *     run concurrently.  Two calls that share a workspace must be ordered.
+ */
+#ifndef ADAMAS_H
+#define ADAMAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADAMAS_ABI_VERSION 1
+#define ADAMAS_HEAD_DIM 128
+#define ADAMAS_CODE_BYTES 32
+
+typedef enum adamas_status {
+  ADAMAS_OK = 0,
+  ADAMAS_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, budget < 1, ...          */
+  ADAMAS_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. head_dim != 128)  */
+  ADAMAS_ERR_WORKSPACE = 3,        /* workspace pointer NULL or smaller than required   */
+  ADAMAS_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed        */
+} adamas_status;
+
+/* Shapes shared by every call.  head_dim must be 128.  num_q_heads must be a
+ * multiple of num_kv_heads, and the group size num_q_heads / num_kv_heads must be
+ * 1, 2, 4 or 8.  capacity = allocated positions per (batch, kv head). */
+typedef struct adamas_dims {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+} adamas_dims;
+
+/*
+ * Key-code maintenance (prefill and append).  For every batch entry b and KV head
+ * g, encode the keys at positions start[b] <= p < end[b]: transform, bucketize
+ * and pack each key vector into 32 bytes.  Codes of other positions are not
+ * touched.  Because thresholds are per vector, appending a key needs only that
+ * key: after writing K[b][g][len-1], call with start = len-1, end = len.
+ *   k      bf16 [batch][num_kv_heads][capacity][128]
+ *   start  int32 [batch] device array, or NULL for all zeros
+ *   end    int32 [batch] device array; precondition 0 <= start[b] <= end[b] <= capacity
+ *   codes  uint8 [batch][num_kv_heads][capacity][32] (output)
+ * num_q_heads is ignored here.  Errors: INVALID_ARGUMENT (null k/end/codes, bad
+ * dims), UNSUPPORTED (head_dim != 128), HIP.
+ */
+adamas_status adamas_encode_keys(const adamas_dims* d, const void* k, const int32_t* start,
+                                 const int32_t* end, uint8_t* codes, void* stream);
+
+/* Bytes of workspace adamas_decode_step needs for these dims and budget (0 if
+ * the arguments are invalid).  Any alignment of 256 bytes is sufficient. */
+size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget);
+
+/*
+ * One Adamas decode step for every (b, query head h), with g = h / (Hq/Hkv):
+ *   1. encode q[b][h] exactly as adamas_encode_keys encodes a key;
+ *   2. dist[p] = sum_i |code_q[i] - code_k[b][g][p][i]| for p < kv_len[b];
+ *   3. select the k_b = min(budget, kv_len[b]) positions with the smallest
+ *      (dist, position);
+ *   4. out[b][h] = sum_{p in S} softmax_p(scale * q.K[b][g][p]) V[b][g][p], exact
+ *      softmax over the selected original bf16 rows, fp32 accumulation.
+ * Arguments:
+ *   q          bf16 [batch][num_q_heads][128]
+ *   k, v       bf16 [batch][num_kv_heads][capacity][128] (the original cache)
+ *   codes      uint8 [batch][num_kv_heads][capacity][32], valid for p < kv_len[b]
+ *   kv_len     int32 [batch] device array; precondition 1 <= kv_len[b] <= capacity
+ *   budget     token budget k >= 1 (may exceed kv_len[b]: then every position is kept)
+ *   scale      softmax scale
+ *   out        fp32 [batch][num_q_heads][128] (output)
+ *   sel_idx    optional (NULL = not written): int32 [batch][num_q_heads][budget];
+ *              the selected positions in ascending order, then -1 padding
+ *   dist       optional debug output (NULL = not written): uint16
+ *              [batch][num_q_heads][capacity]; entries p >= kv_len[b] untouched
+ *   q_codes    optional debug output (NULL = not written): uint8 [batch][num_q_heads][32]
+ *   workspace  device scratch of at least adamas_decode_workspace_size(d, budget)
+ *              bytes, 256-byte aligned; its contents need no initialisation and
+ *              are meaningless after the call.
+ * Codes, distances and sel_idx are deterministic integers; out is deterministic
+ * for fixed inputs.  Errors: INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE, HIP.
+ */
+adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                 const uint8_t* codes, const int32_t* kv_len, int32_t budget,
+                                 float scale, float* out, int32_t* sel_idx, uint16_t* dist,
+                                 uint8_t* q_codes, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Bytes of workspace dense_decode_attention needs (0 if the dims are invalid). */
+size_t dense_decode_workspace_size(const adamas_dims* d);
+
+/*
+ * Dense decode attention, the comparison baseline the pages measure Adamas
+ * against: out[b][h] = softmax attention of q[b][h] over every position
+ * p < kv_len[b] of KV head g = h / (Hq/Hkv).  Same layouts, preconditions and
+ * errors as adamas_decode_step.
+ */
+adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                     const int32_t* kv_len, float scale, float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* adamas_status_string(adamas_status s);
+
+/* ADAMAS_ABI_VERSION of the built library. */
+int32_t adamas_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAMAS_H */

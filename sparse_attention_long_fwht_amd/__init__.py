@@ -1,0 +1,159 @@
+"""Python binding of libadamas.so (the Adamas decode step on gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind
+the C ABI declared in include/adamas.h.  Tensors are torch tensors on the current
+HIP device; bf16 tensors may be torch.bfloat16 or any 2-byte dtype holding the
+bf16 bit patterns.  Calls enqueue on the current torch stream unless `stream` is
+given.  There is no CPU fallback: importing this package fails if the library has
+not been built (python -c "import __graft_entry__ as g; g.build()").
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libadamas.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libadamas.so is not built at %s; build it with sparse_attention_long_fwht_amd/build.py"
+                      % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+HEAD_DIM = 128
+CODE_BYTES = 32
+
+OK = 0
+ERR_INVALID_ARGUMENT = 1
+ERR_UNSUPPORTED = 2
+ERR_WORKSPACE = 3
+ERR_HIP = 4
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_dims_p = ctypes.POINTER(Dims)
+_lib.adamas_encode_keys.argtypes = [_dims_p, _vp, _vp, _vp, _vp, _vp]
+_lib.adamas_encode_keys.restype = ctypes.c_int
+_lib.adamas_decode_workspace_size.argtypes = [_dims_p, ctypes.c_int32]
+_lib.adamas_decode_workspace_size.restype = ctypes.c_size_t
+_lib.adamas_decode_step.argtypes = [_dims_p, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp, _vp,
+                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.adamas_decode_step.restype = ctypes.c_int
+_lib.dense_decode_workspace_size.argtypes = [_dims_p]
+_lib.dense_decode_workspace_size.restype = ctypes.c_size_t
+_lib.dense_decode_attention.argtypes = [_dims_p, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
+                                        _vp]
+_lib.dense_decode_attention.restype = ctypes.c_int
+_lib.adamas_status_string.argtypes = [ctypes.c_int]
+_lib.adamas_status_string.restype = ctypes.c_char_p
+_lib.adamas_abi_version.argtypes = []
+_lib.adamas_abi_version.restype = ctypes.c_int32
+
+EXPORTED_SYMBOLS = ("adamas_encode_keys", "adamas_decode_workspace_size", "adamas_decode_step",
+                    "dense_decode_workspace_size", "dense_decode_attention", "adamas_status_string",
+                    "adamas_abi_version")
+
+
+class AdamasError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def status_string(status: int) -> str:
+    return _lib.adamas_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.adamas_abi_version())
+
+
+def dims(batch: int, num_q_heads: int, num_kv_heads: int, capacity: int, head_dim: int = HEAD_DIM) -> Dims:
+    return Dims(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(capacity))
+
+
+def _ptr(t, name, itemsize=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if itemsize is not None and t.element_size() != itemsize:
+        raise ValueError("%s must have %d-byte elements" % (name, itemsize))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status, where):
+    if status != OK:
+        raise AdamasError(status, where)
+
+
+def encode_keys(k, end, codes, start=None, stream=None, num_q_heads=None):
+    """Encode keys at positions [start[b], end[b]) of k [B][Hkv][cap][128] into codes [B][Hkv][cap][32]."""
+    B, Hkv, cap, hd = k.shape
+    d = dims(B, num_q_heads or Hkv, Hkv, cap, hd)
+    st = _lib.adamas_encode_keys(ctypes.byref(d), _ptr(k, "k", 2), _ptr(start, "start", 4, optional=True),
+                                 _ptr(end, "end", 4), _ptr(codes, "codes", 1), _stream(stream))
+    _check(st, "adamas_encode_keys")
+
+
+def decode_workspace_size(B, Hq, Hkv, cap, budget, head_dim=HEAD_DIM) -> int:
+    return int(_lib.adamas_decode_workspace_size(ctypes.byref(dims(B, Hq, Hkv, cap, head_dim)), int(budget)))
+
+
+def dense_workspace_size(B, Hq, Hkv, cap, head_dim=HEAD_DIM) -> int:
+    return int(_lib.dense_decode_workspace_size(ctypes.byref(dims(B, Hq, Hkv, cap, head_dim))))
+
+
+def alloc_workspace(nbytes, device=None):
+    """A device byte tensor usable as workspace (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device or "cuda")
+
+
+def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=None, dist=None, q_codes=None,
+                stream=None):
+    """One Adamas decode step; writes out [B][Hq][128] fp32 (and the optional outputs)."""
+    B, Hq, hd = q.shape
+    _, Hkv, cap, _ = k.shape
+    d = dims(B, Hq, Hkv, cap, hd)
+    st = _lib.adamas_decode_step(ctypes.byref(d), _ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2),
+                                 _ptr(codes, "codes", 1), _ptr(kv_len, "kv_len", 4), int(budget), float(scale),
+                                 _ptr(out, "out", 4), _ptr(sel_idx, "sel_idx", 4, optional=True),
+                                 _ptr(dist, "dist", 2, optional=True), _ptr(q_codes, "q_codes", 1, optional=True),
+                                 _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    _check(st, "adamas_decode_step")
+
+
+def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None):
+    """Dense decode attention over every position < kv_len[b]; writes out [B][Hq][128] fp32."""
+    B, Hq, hd = q.shape
+    _, Hkv, cap, _ = k.shape
+    d = dims(B, Hq, Hkv, cap, hd)
+    st = _lib.dense_decode_attention(ctypes.byref(d), _ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2),
+                                     _ptr(kv_len, "kv_len", 4), float(scale), _ptr(out, "out", 4),
+                                     _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
+    _check(st, "dense_decode_attention")
+
+
+def raw_library():
+    """The ctypes handle of libadamas.so (for callers that pass raw pointers)."""
+    return _lib

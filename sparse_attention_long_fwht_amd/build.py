@@ -1,0 +1,45 @@
+"""Build libadamas.so (HIP, gfx950 only) in-tree with hipcc.
+
+Flags: -ffp-contract=off (no silent fma contraction: the key/query encode must
+round each add once, exactly as specified), denormals kept
+(-fno-gpu-flush-denormals-to-zero), and packed fp32 instructions disabled.
+"""
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libadamas.so")
+SOURCES = [os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "kernels.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; that
+    # line is expected and harmless, everything else is shown.
+    noise = "packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + msg)
+    if msg.strip() and verbose:
+        print(msg)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,110 @@
+// api.hip -- the extern "C" entry points of libadamas.so (declared in
+// include/adamas.h): argument checks, workspace sizing and kernel dispatch.
+// Every host-checkable error is reported before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "adamas.h"
+#include "plan.h"
+
+using adamas::Plan;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared shape checks.  need_q: num_q_heads participates.
+adamas_status check_dims(const adamas_dims* d, bool need_q) {
+  if (!d) return ADAMAS_ERR_INVALID_ARGUMENT;
+  if (d->batch < 1 || d->num_kv_heads < 1 || d->capacity < 1 || d->head_dim < 1)
+    return ADAMAS_ERR_INVALID_ARGUMENT;
+  if (need_q) {
+    if (d->num_q_heads < 1 || d->num_q_heads % d->num_kv_heads != 0) return ADAMAS_ERR_INVALID_ARGUMENT;
+  }
+  if (d->head_dim != ADAMAS_HEAD_DIM) return ADAMAS_ERR_UNSUPPORTED;
+  if ((int64_t)d->capacity > adamas::kMaxCapacity) return ADAMAS_ERR_UNSUPPORTED;
+  if ((int64_t)d->batch * d->num_kv_heads > 65535) return ADAMAS_ERR_UNSUPPORTED;
+  if (need_q) {
+    const int R = d->num_q_heads / d->num_kv_heads;
+    if (R != 1 && R != 2 && R != 4 && R != 8) return ADAMAS_ERR_UNSUPPORTED;
+    if ((int64_t)d->batch * d->num_q_heads > 65535) return ADAMAS_ERR_UNSUPPORTED;
+  }
+  return ADAMAS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* adamas_status_string(adamas_status s) {
+  switch (s) {
+    case ADAMAS_OK: return "ok";
+    case ADAMAS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ADAMAS_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case ADAMAS_ERR_WORKSPACE: return "workspace missing or too small";
+    case ADAMAS_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t adamas_abi_version(void) { return ADAMAS_ABI_VERSION; }
+
+adamas_status adamas_encode_keys(const adamas_dims* d, const void* k, const int32_t* start, const int32_t* end,
+                                 uint8_t* codes, void* stream) {
+  adamas_status st = check_dims(d, false);
+  if (st != ADAMAS_OK) return st;
+  if (!k || !end || !codes) return ADAMAS_ERR_INVALID_ARGUMENT;
+  if (!aligned(k, 16) || !aligned(codes, 16) || !aligned(end, 4) || (start && !aligned(start, 4)))
+    return ADAMAS_ERR_INVALID_ARGUMENT;
+  hipError_t e = adamas::launch_encode_keys(d->batch, d->num_kv_heads, d->capacity,
+                                            static_cast<const uint16_t*>(k), start, end, codes,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
+}
+
+size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget) {
+  if (check_dims(d, true) != ADAMAS_OK || budget < 1) return 0;
+  return adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false).total;
+}
+
+adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                 const uint8_t* codes, const int32_t* kv_len, int32_t budget, float scale,
+                                 float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  adamas_status st = check_dims(d, true);
+  if (st != ADAMAS_OK) return st;
+  if (!q || !k || !v || !codes || !kv_len || !out || budget < 1) return ADAMAS_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(codes, 16) || !aligned(kv_len, 4) ||
+      !aligned(out, 4) || (sel_idx && !aligned(sel_idx, 4)) || (dist && !aligned(dist, 2)) ||
+      (q_codes && !aligned(q_codes, 4)))
+    return ADAMAS_ERR_INVALID_ARGUMENT;
+  const Plan p = adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false);
+  if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return ADAMAS_ERR_WORKSPACE;
+  hipError_t e = adamas::launch_decode(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                       static_cast<const uint16_t*>(v), codes, kv_len, scale, out, sel_idx, dist,
+                                       q_codes, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
+}
+
+size_t dense_decode_workspace_size(const adamas_dims* d) {
+  if (check_dims(d, true) != ADAMAS_OK) return 0;
+  return adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, 1, true).total;
+}
+
+adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                     const int32_t* kv_len, float scale, float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  adamas_status st = check_dims(d, true);
+  if (st != ADAMAS_OK) return st;
+  if (!q || !k || !v || !kv_len || !out) return ADAMAS_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(kv_len, 4) || !aligned(out, 4))
+    return ADAMAS_ERR_INVALID_ARGUMENT;
+  const Plan p = adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, 1, true);
+  if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return ADAMAS_ERR_WORKSPACE;
+  hipError_t e = adamas::launch_dense(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                      static_cast<const uint16_t*>(v), kv_len, scale, out,
+                                      static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/adamas.h declares, sizes workspaces, and rejects invalid arguments with
+the documented status before any HIP call (so no GPU is needed here).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adamas.h")
+
+
+@pytest.fixture(scope="module")
+def A():
+    import sparse_attention_long_fwht_amd as A
+    return A
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("adamas_encode_keys", "adamas_decode_step", "dense_decode_attention", "adamas_decode_workspace_size",
+              "dense_decode_workspace_size", "adamas_status_string", "adamas_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(A):
+    lib = A.raw_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert sorted(A.EXPORTED_SYMBOLS) == declared_functions()
+
+
+def test_version_and_status_strings(A):
+    assert A.abi_version() == 1
+    assert A.status_string(0) == "ok"
+    for s in range(1, 5):
+        assert A.status_string(s) not in ("ok", "unknown status")
+    assert A.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes(A):
+    s128 = A.decode_workspace_size(1, 32, 8, 32768, 128)
+    assert s128 > 0 and s128 % 256 == 0
+    assert A.decode_workspace_size(1, 32, 8, 65536, 128) > s128
+    assert A.decode_workspace_size(2, 32, 8, 32768, 128) > s128
+    assert A.dense_workspace_size(1, 32, 8, 32768) > 0
+    # invalid shapes give 0
+    assert A.decode_workspace_size(1, 32, 8, 32768, 0) == 0
+    assert A.decode_workspace_size(1, 30, 8, 32768, 8) == 0
+    assert A.decode_workspace_size(1, 32, 8, 32768, 8, head_dim=64) == 0
+    assert A.decode_workspace_size(1, 48, 8, 32768, 8) == 0  # group of 6 is not supported
+    assert A.decode_workspace_size(1, 32, 8, (1 << 20) + 1, 8) == 0
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
+
+
+def call_decode(A, d, budget=8, ws_bytes=1 << 30, ptrs=None, ws=FAKE):
+    lib = A.raw_library()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, codes=FAKE, kv_len=FAKE, out=FAKE)
+    if ptrs:
+        p.update(ptrs)
+    return lib.adamas_decode_step(ctypes.byref(d), p["q"], p["k"], p["v"], p["codes"], p["kv_len"], budget,
+                                  ctypes.c_float(0.088), p["out"], None, None, None, ws, ws_bytes, None)
+
+
+def test_decode_rejects_invalid_arguments(A):
+    lib = A.raw_library()
+    good = A.dims(1, 32, 8, 32768)
+    assert lib.adamas_decode_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(1.0), FAKE, None, None,
+                                  None, FAKE, 1 << 30, None) == A.ERR_INVALID_ARGUMENT
+    assert call_decode(A, good, budget=0) == A.ERR_INVALID_ARGUMENT
+    assert call_decode(A, good, ptrs=dict(q=None)) == A.ERR_INVALID_ARGUMENT
+    assert call_decode(A, good, ptrs=dict(out=None)) == A.ERR_INVALID_ARGUMENT
+    assert call_decode(A, good, ptrs=dict(k=FAKE + 2)) == A.ERR_INVALID_ARGUMENT  # misaligned
+    assert call_decode(A, A.dims(0, 32, 8, 32768)) == A.ERR_INVALID_ARGUMENT
+    assert call_decode(A, A.dims(1, 30, 8, 32768)) == A.ERR_INVALID_ARGUMENT
+    assert call_decode(A, A.dims(1, 32, 8, 0)) == A.ERR_INVALID_ARGUMENT
+    assert call_decode(A, A.dims(1, 32, 8, 32768, head_dim=64)) == A.ERR_UNSUPPORTED
+    assert call_decode(A, A.dims(1, 24, 2, 32768)) == A.ERR_UNSUPPORTED  # group of 12
+    assert call_decode(A, A.dims(1, 32, 8, (1 << 20) + 1)) == A.ERR_UNSUPPORTED
+    need = A.decode_workspace_size(1, 32, 8, 32768, 8)
+    assert call_decode(A, good, ws_bytes=need - 1) == A.ERR_WORKSPACE
+    assert call_decode(A, good, ws=None) == A.ERR_WORKSPACE
+    assert call_decode(A, good, ws=FAKE + 128) == A.ERR_WORKSPACE  # not 256-byte aligned
+
+
+def test_encode_and_dense_reject_invalid_arguments(A):
+    lib = A.raw_library()
+    d = A.dims(1, 8, 8, 1024)
+    assert lib.adamas_encode_keys(ctypes.byref(d), None, None, FAKE, FAKE, None) == A.ERR_INVALID_ARGUMENT
+    assert lib.adamas_encode_keys(ctypes.byref(d), FAKE, None, None, FAKE, None) == A.ERR_INVALID_ARGUMENT
+    assert lib.adamas_encode_keys(ctypes.byref(A.dims(1, 8, 8, 1024, head_dim=256)), FAKE, None, FAKE, FAKE,
+                                  None) == A.ERR_UNSUPPORTED
+    assert lib.dense_decode_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE, 0,
+                                      None) == A.ERR_WORKSPACE
+    assert lib.dense_decode_attention(ctypes.byref(d), FAKE, None, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE,
+                                      1 << 30, None) == A.ERR_INVALID_ARGUMENT
+
+
+def test_package_has_no_cpu_fallback():
+    """The product package must not reach the oracle or any host implementation."""
+    pkg = os.path.join(ROOT, "sparse_attention_long_fwht_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text, f

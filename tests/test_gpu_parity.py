@@ -1,0 +1,220 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Every call goes through the C ABI (ctypes binding).  Integer results (key codes,
+query codes, distances, selected indices) must match the oracle exactly; the
+attention output must be within 2e-3 of the oracle relative to the row norm.
+Cases span several chunks and a ragged tail, the GQA group sizes 1/2/4/8, the
+edge cases (kv_len 1, budget 1, budget >= kv_len, heavy ties, boundary values of
+the bucketing), and the full configurations: tiny (1K), Llama-shaped 32K with
+budgets 128 and 1024, the batched ragged 16 x [16K, 32K] case and 512K.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from helpers import DeviceCase, assert_out_close, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import sparse_attention_long_fwht_amd as A
+    import oracle
+    return A, torch, oracle
+
+
+def check_decode(case, oracle, budget=None, threads=8, check_dist=True):
+    wl = case.wl
+    budget = wl.budget if budget is None else budget
+    codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
+    codes_gpu = from_dev(case.codes)
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        assert np.array_equal(codes_gpu[b, :, :L], codes_ref[b, :, :L]), "key codes differ (b=%d)" % b
+    out_r, sel_r, dist_r, qc_r = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, budget, wl.scale,
+                                                    threads=threads, want_dist=check_dist)
+    out, sel, dist, qc = case.decode(budget, want_debug=True)
+    assert np.array_equal(qc, qc_r), "query codes differ"
+    if check_dist:
+        for b in range(wl.B):
+            L = int(wl.kv_len[b])
+            assert np.array_equal(dist[b, :, :L], dist_r[b, :, :L]), "distances differ (b=%d)" % b
+    assert np.array_equal(sel, sel_r), "selected indices differ"
+    return assert_out_close(out, out_r)
+
+
+# ---------------------------------------------------------------- key encode
+
+
+def test_encode_keys_tiny(env):
+    A, torch, oracle = env
+    wl = W.tiny()
+    case = DeviceCase(wl, A, torch)
+    assert np.array_equal(from_dev(case.codes), oracle.encode_keys(wl.k, wl.kv_len))
+
+
+def test_encode_keys_boundary_values(env):
+    """Keys whose transform lands exactly on -t, 0 and +t, all-zero and -0 keys,
+    subnormal keys: codes must match bit for bit."""
+    A, torch, oracle = env
+    rng = np.random.default_rng(30)
+    H = np.array([[(-1) ** bin(i & j).count("1") for j in range(128)] for i in range(128)], np.int64)
+    rows = []
+    for _ in range(200):
+        z = np.zeros(128, np.int64)
+        idx = rng.choice(128, 6, replace=False)
+        z[idx] = rng.choice([-2, -1, 1, 2], 6)
+        rows.append((H @ z).astype(np.float32))      # transform = 128 z exactly: values 0, +-t, +-2t
+    rows.append(np.zeros(128, np.float32))
+    rows.append(np.full(128, -0.0, np.float32))
+    sub = np.zeros(128, np.float32)
+    sub[:5] = np.array([1e-39, -2e-39, 3e-40, 0.0, -1e-38], np.float32)
+    rows.append(sub)
+    for _ in range(20):
+        rows.append((rng.standard_normal(128) * 1e-38).astype(np.float32))
+    kb = W.f32_to_bf16(np.stack(rows)).reshape(1, 1, -1, 128)
+    n = kb.shape[2]
+    kv_len = np.array([n], np.int32)
+    k = to_dev(kb, torch)
+    codes = torch.zeros((1, 1, n, 32), dtype=torch.uint8, device="cuda")
+    A.encode_keys(k, to_dev(kv_len, torch), codes)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(codes), oracle.encode_keys(kb, kv_len))
+
+
+def test_encode_keys_llama32k(env):
+    A, torch, oracle = env
+    wl = W.llama(0, cap=32768, budget=128)
+    case = DeviceCase(wl, A, torch)
+    assert np.array_equal(from_dev(case.codes), oracle.encode_keys(wl.k, wl.kv_len))
+
+
+def test_encode_append_matches_prefill(env):
+    A, torch, oracle = env
+    wl = W.llama(31, cap=3000, budget=64, B=3, Hq=8, Hkv=2, kv_len=np.array([3000, 1537, 1], np.int32))
+    case = DeviceCase(wl, A, torch)
+    start = to_dev(wl.kv_len - 1, torch)
+    appended = torch.zeros_like(case.codes)
+    A.encode_keys(case.k, case.kv_len, appended, start=start)
+    torch.cuda.synchronize()
+    full, app = from_dev(case.codes), from_dev(appended)
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        assert np.array_equal(app[b, :, L - 1], full[b, :, L - 1])
+        assert not app[b, :, : L - 1].any() and not app[b, :, L:].any()
+
+
+# ---------------------------------------------------------------- decode step
+
+
+def test_decode_tiny(env):
+    A, torch, oracle = env
+    case = DeviceCase(W.tiny(), A, torch)
+    check_decode(case, oracle)
+
+
+@pytest.mark.parametrize("budget", [1, 7, 64, 700, 5000])
+def test_decode_ragged_multi_chunk(env, budget):
+    """3000-slot cache (several chunks + ragged tail), lengths 3000 / 1537 / 1."""
+    A, torch, oracle = env
+    wl = W.llama(32, cap=3000, budget=budget, B=3, Hq=8, Hkv=2, kv_len=np.array([3000, 1537, 1], np.int32))
+    check_decode(DeviceCase(wl, A, torch), oracle)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (8, 1), (16, 2)])
+def test_decode_group_sizes(env, Hq, Hkv):
+    A, torch, oracle = env
+    wl = W.llama(33, cap=2100, budget=96, B=2, Hq=Hq, Hkv=Hkv, kv_len=np.array([2100, 999], np.int32))
+    check_decode(DeviceCase(wl, A, torch), oracle)
+
+
+def test_decode_heavy_ties(env):
+    """Many keys share one code, so the threshold bin holds hundreds of ties:
+    the lower positions must win."""
+    A, torch, oracle = env
+    wl = W.llama(34, cap=4096, budget=300, B=1, Hq=4, Hkv=1)
+    rep = wl.k[0, 0, :8].copy()
+    wl.k[0, 0] = np.tile(rep, (512, 1))
+    check_decode(DeviceCase(wl, A, torch), oracle)
+
+
+def test_decode_full_budget_equals_dense(env):
+    A, torch, oracle = env
+    wl = W.llama(35, cap=1500, budget=2000, B=2, Hq=8, Hkv=2, kv_len=np.array([1500, 733], np.int32))
+    case = DeviceCase(wl, A, torch)
+    out, sel, _, _ = case.decode(2000)
+    dense = case.dense()
+    ref = oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale)
+    assert_out_close(out, ref)
+    assert_out_close(dense, ref)
+    assert np.array_equal(sel[0, :, :1500], np.broadcast_to(np.arange(1500), (8, 1500)))
+    assert np.all(sel[1, :, 733:] == -1)
+
+
+def test_decode_is_deterministic(env):
+    A, torch, oracle = env
+    wl = W.llama(36, cap=8192, budget=256, B=1)
+    case = DeviceCase(wl, A, torch)
+    a = case.decode()
+    b = case.decode()
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("budget", [128, 1024])
+def test_decode_llama32k(env, budget):
+    """Llama-3.1-8B-shaped layer: 32 q heads / 8 kv heads, 32K context."""
+    A, torch, oracle = env
+    wl = W.llama(0, cap=32768, budget=budget)
+    err = check_decode(DeviceCase(wl, A, torch), oracle, threads=16)
+    print("llama32k budget %d: worst relative error %.2e" % (budget, err))
+
+
+def test_decode_batched16(env):
+    """16 sequences with ragged lengths in [16K, 32K], budget 256."""
+    A, torch, oracle = env
+    wl = W.batched(0)
+    err = check_decode(DeviceCase(wl, A, torch), oracle, threads=16)
+    print("batched16: worst relative error %.2e" % err)
+
+
+def test_decode_long512k_sampled_groups(env):
+    """512K context, budget 1024: the whole step runs on the GPU at full size; the
+    oracle recomputes two KV groups (8 q heads) end to end."""
+    A, torch, oracle = env
+    wl = W.llama(0, cap=524288, budget=1024, name="long512k")
+    case = DeviceCase(wl, A, torch)
+    out, sel, dist, qc = case.decode(want_debug=True)
+    codes_gpu = from_dev(case.codes)
+    R = wl.Hq // wl.Hkv
+    for g in (0, 5):
+        kg, vg = wl.k[:, g:g + 1], wl.v[:, g:g + 1]
+        codes_ref = oracle.encode_keys(kg, wl.kv_len)
+        assert np.array_equal(codes_gpu[:, g:g + 1], codes_ref)
+        qg = wl.q[:, g * R:(g + 1) * R]
+        o_r, s_r, d_r, q_r = oracle.decode_step(qg, kg, vg, codes_ref, wl.kv_len, wl.budget, wl.scale, threads=16)
+        hs = slice(g * R, (g + 1) * R)
+        assert np.array_equal(qc[:, hs], q_r)
+        assert np.array_equal(dist[:, hs], d_r)
+        assert np.array_equal(sel[:, hs], s_r)
+        assert_out_close(out[:, hs], o_r)
+
+
+# ---------------------------------------------------------------- dense baseline
+
+
+def test_dense_tiny_and_ragged(env):
+    A, torch, oracle = env
+    for wl in (W.tiny(), W.llama(37, cap=5000, budget=1, B=2, Hq=8, Hkv=2, kv_len=np.array([5000, 2049], np.int32))):
+        case = DeviceCase(wl, A, torch, encode=False)
+        assert_out_close(case.dense(), oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale))
+
+
+def test_dense_llama32k(env):
+    A, torch, oracle = env
+    wl = W.llama(0, cap=32768, budget=128)
+    case = DeviceCase(wl, A, torch, encode=False)
+    assert_out_close(case.dense(), oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale, threads=16))
