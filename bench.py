@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the Adamas decode step on one MI355X.
+
+Workload: one Llama-3.1-8B-shaped attention layer at decode time -- batch 1,
+32 query heads / 8 KV heads, head_dim 128, 32768 cached positions, token budget
+128 (budget 1024 is reported alongside) -- synthetic seeded data (workloads.py).
+
+One step = the whole hot path, one adamas_append_decode_step call: encode the
+newly appended key of every KV head (transform + bucketize + pack, position
+len-1), encode the queries, scan every packed key code (Manhattan distance),
+select the top-k, gather the original K/V rows and run exact softmax attention.
+The same step issued as adamas_encode_keys + adamas_decode_step is reported too.  Steps are replayed from a HIP graph (the launch
+sequence of each step is captured once), over R rotating copies of the cache so
+that successive steps do not hit data left in the 256 MB last-level cache by
+the previous ones ("cold"); a warm figure (one copy) is reported as well.
+
+Printed: one JSON line.  `value` is the mean decode-step latency in microseconds
+(lower is better).  `roofline` covers the dominant kernel of the step: its
+algorithmic bytes per launch divided by its mean duration, measured with HIP
+events recorded by the kernel dispatch itself (adamas_profile_events).
+`cpu_baseline` is the CPU oracle (oracle/) timed on this host for a bounded
+number of steps of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-step sparse-attn latency (us) and achieved HBM GB/s vs peak, 32K ctx"
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--budget", type=int, default=128)
+    ap.add_argument("--context", type=int, default=32768)
+    ap.add_argument("--copies", type=int, default=64, help="rotating cache copies (cold-cache timing)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+class Hip:
+    """Raw HIP events through libamdhip64 (the library's kernels are timed by
+    events its own dispatches record)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, "hipEventElapsedTime failed (%d)" % rc
+        return ms.value
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the Adamas decode step is built and timed on a single MI355X; "
+              "multi-GPU runs are not part of this build (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_long_fwht_amd as A
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    hip = Hip()
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    cap = args.context
+    budget = args.budget
+    t0 = time.time()
+    wl = W.llama(args.seed, cap=cap, budget=budget)
+    B, Hq, Hkv = wl.B, wl.Hq, wl.Hkv
+    log("[bench] generated %s in %.1fs" % (wl.name, time.time() - t0))
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+
+    q0, k0, v0 = up(wl.q), up(wl.k), up(wl.v)
+    kv_len = up(wl.kv_len)
+    start = up(wl.kv_len - 1)
+    codes0 = torch.zeros((B, Hkv, cap, 32), dtype=torch.uint8, device=dev)
+    A.encode_keys(k0, kv_len, codes0)
+    R = max(1, args.copies)
+    copies = [(q0, k0, v0, codes0)] + [(q0.clone(), k0.clone(), v0.clone(), codes0.clone()) for _ in range(R - 1)]
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    ws = A.alloc_workspace(A.decode_workspace_size(B, Hq, Hkv, cap, budget), dev)
+    ws_dense = A.alloc_workspace(A.dense_workspace_size(B, Hq, Hkv, cap), dev)
+    torch.cuda.synchronize()
+    log("[bench] %d cache copies resident (%.1f GiB)" % (R, R * (2 * k0.numel() * 2 + codes0.numel()) / 2 ** 30))
+
+    def step(c, bud=budget, work=ws):
+        # append the key at len-1 and decode, one call (adamas_append_decode_step)
+        q, k, v, codes = c
+        A.decode_step(q, k, v, codes, kv_len, bud, wl.scale, out, work, append=True)
+
+    def step_unfused(c):
+        q, k, v, codes = c
+        A.encode_keys(k, kv_len, codes, start=start)
+        A.decode_step(q, k, v, codes, kv_len, budget, wl.scale, out, ws)
+
+    def dense_step(c):
+        q, k, v, _ = c
+        A.dense_decode_attention(q, k, v, kv_len, wl.scale, out, ws_dense)
+
+    def graph_of(fn, cs):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for c in cs:  # eager pass on the capture stream first
+                fn(c)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for c in cs:
+                fn(c)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, n_per_replay, steps, warmup):
+        reps = max(1, (steps + n_per_replay - 1) // n_per_replay)
+        wreps = max(1, (warmup + n_per_replay - 1) // n_per_replay)
+        for _ in range(wreps):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * n_per_replay), reps * n_per_replay
+
+    # ---- headline: cold-cache decode step, graph replay
+    g_cold = graph_of(step, copies)
+    ms_step, steps_done = time_graph(g_cold, R, args.steps, args.warmup)
+    log("[bench] decode step (adamas_append_decode_step), cold: %.2f us" % (ms_step * 1e3))
+
+    # ---- kernel-by-kernel durations (dispatch-recorded HIP events), cold rotation
+    names = ["scan", "select_attend"]
+    evs = [hip.event() for _ in range(2 * len(names))]
+    ev_enc = [hip.event() for _ in range(2)]
+    sums = [0.0] * len(names)
+    enc_sum = 0.0
+    n_prof = max(2 * R, 64)
+    for i in range(n_prof + 8):
+        q, k, v, codes = copies[i % R]
+        A.profile_events(ev_enc)
+        A.encode_keys(k, kv_len, codes, start=start)
+        A.profile_events(evs)
+        A.decode_step(q, k, v, codes, kv_len, budget, wl.scale, out, ws, append=True)
+        A.profile_events(None)
+        torch.cuda.synchronize()
+        if i >= 8:
+            for j in range(len(names)):
+                sums[j] += hip.elapsed_ms(evs[2 * j], evs[2 * j + 1])
+            enc_sum += hip.elapsed_ms(ev_enc[0], ev_enc[1])
+    kern_us = {names[j]: sums[j] / n_prof * 1e3 for j in range(len(names))}
+    kern_us["append_encode"] = enc_sum / n_prof * 1e3
+    log("[bench] kernel means (us): %s" % kern_us)
+
+    # algorithmic bytes (what the method must move), per launch
+    lens = wl.kv_len.astype(np.int64)
+    code_bytes = int(Hkv * lens.sum() * 32)
+    q_bytes = B * Hq * 128 * 2
+    out_bytes = B * Hq * 128 * 4
+    # unique gathered rows per (b, kv head): union of the group's selections
+    sel = torch.empty((B, Hq, budget), dtype=torch.int32, device=dev)
+    A.decode_step(q0, k0, v0, codes0, kv_len, budget, wl.scale, out, ws, sel_idx=sel)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    grp = Hq // Hkv
+    uniq = sum(len(np.unique(sel_np[b, g * grp:(g + 1) * grp][sel_np[b, g * grp:(g + 1) * grp] >= 0]))
+               for b in range(B) for g in range(Hkv))
+    nodedup = int((sel_np >= 0).sum())
+    gather_bytes = uniq * 512
+    algo = {"scan": code_bytes + q_bytes, "select_attend": gather_bytes + q_bytes + out_bytes,
+            "append_encode": B * Hkv * (256 + 32)}
+    dominant = max(kern_us, key=kern_us.get)
+    achieved = algo[dominant] / (kern_us[dominant] * 1e-6) / 1e9 if algo[dominant] else 0.0
+    step_bytes = code_bytes + gather_bytes + q_bytes + out_bytes + B * Hkv * (256 + 32)
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(dominant, algo[dominant]),
+                "kernel": dominant + "_kernel", "kernel_us": round(kern_us[dominant], 3),
+                "algorithmic_bytes_per_launch": algo[dominant]}
+
+    extra = {"kernel_us": {k: round(v, 3) for k, v in kern_us.items()},
+             "step_algorithmic_bytes": step_bytes,
+             "step_achieved_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+             "gathered_rows_unique": uniq, "gathered_rows_no_dedup": nodedup,
+             "cache_copies": R}
+
+    if not args.no_extra:
+        # the same step as two library calls: adamas_encode_keys + adamas_decode_step
+        g_unf = graph_of(step_unfused, copies)
+        ms_unf, _ = time_graph(g_unf, R, args.steps, args.warmup)
+        extra["step_us_unfused_encode_then_decode"] = round(ms_unf * 1e3, 3)
+        log("[bench] encode_keys + decode_step (two calls): %.2f us" % (ms_unf * 1e3))
+        del g_unf
+        # warm: one copy
+        g_warm = graph_of(step, [copies[0]] * 8)
+        ms_warm, _ = time_graph(g_warm, 8, args.steps, args.warmup)
+        extra["step_us_warm"] = round(ms_warm * 1e3, 3)
+        # dense baseline, cold rotation
+        g_dense = graph_of(dense_step, copies)
+        ms_dense, _ = time_graph(g_dense, R, max(R, args.steps // 4), R)
+        dense_bytes = int(Hkv * lens.sum() * 512 + q_bytes + out_bytes)
+        extra["dense_us"] = round(ms_dense * 1e3, 3)
+        extra["dense_GBps"] = round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1)
+        extra["speedup_vs_dense"] = round(ms_dense / ms_step, 3)
+        log("[bench] dense decode baseline: %.2f us (%.0f GB/s); speedup %.2fx"
+            % (ms_dense * 1e3, extra["dense_GBps"], extra["speedup_vs_dense"]))
+        # budget 1024 on the same data
+        if budget != 1024:
+            ws1k = A.alloc_workspace(A.decode_workspace_size(B, Hq, Hkv, cap, 1024), dev)
+            g_1k = graph_of(lambda c: step(c, 1024, ws1k), copies)
+            ms_1k, _ = time_graph(g_1k, R, args.steps, args.warmup)
+            extra["step_us_budget1024"] = round(ms_1k * 1e3, 3)
+            log("[bench] budget 1024: %.2f us" % (ms_1k * 1e3))
+            del g_1k
+        # full-cache key encode (prefill) pass, cold rotation
+        g_enc = graph_of(lambda c: A.encode_keys(c[1], kv_len, c[3]), copies[:16])
+        ms_enc, _ = time_graph(g_enc, 16, 64, 16)
+        enc_bytes = int(Hkv * lens.sum() * (256 + 32))
+        extra["prefill_encode_us"] = round(ms_enc * 1e3, 3)
+        extra["prefill_encode_GBps"] = round(enc_bytes / (ms_enc * 1e-3) / 1e9, 1)
+        log("[bench] prefill key encode: %.2f us (%.0f GB/s)" % (ms_enc * 1e3, extra["prefill_encode_GBps"]))
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, budget, args.cpu_seconds, log)
+
+    res = {"metric": METRIC, "value": round(ms_step * 1e3, 3), "unit": "us", "n_gpus": 1, "steps": steps_done,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": "u8+fp32", "data": "synthetic",
+           "config": {"workload": "llama3.1-8b-shaped decode layer: batch 1, 32 q / 8 kv heads, head_dim 128, "
+                                  "%d cached positions, budget %d; append-encode + decode per step; cold cache"
+                                  % (cap, budget),
+                      "batch": B, "seq_len": cap, "budget": budget, "q_heads": Hq, "kv_heads": Hkv,
+                      "head_dim": 128, "parallelism": "single GPU"},
+           "roofline": roofline, "cpu_baseline": cpu, "extra": extra}
+    print(json.dumps(res), flush=True)
+
+
+def read_traffic(kernel, algo_bytes):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; otherwise None."""
+    import hashlib
+    path = os.path.join(PROFILE_DIR, "%s_kernel_llama32k_counters.txt" % kernel)
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(ROOT, "sparse_attention_long_fwht_amd", "csrc", "kernels.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernels.hip sha256[:16]") != h or "hbm_bytes_per_launch" not in fields:
+        return None
+    return int(float(fields["hbm_bytes_per_launch"]))
+
+
+def cpu_baseline(wl, budget, seconds, log):
+    """The oracle as it stands, timed on this host's cores for a bounded number
+    of full decode steps of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(16, ncpu))
+    codes = oracle.encode_keys(wl.k, wl.kv_len)
+    t0 = time.time()
+    oracle.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, budget, wl.scale, threads=threads, want_dist=False)
+    one = time.time() - t0
+    n = max(1, int(seconds / max(one, 1e-3)))
+    t0 = time.time()
+    for _ in range(n):
+        oracle.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, budget, wl.scale, threads=threads, want_dist=False)
+    dt = (time.time() - t0) / n
+    log("[bench] cpu oracle: %.1f us/step over %d steps with %d threads" % (dt * 1e6, n, threads))
+    return {"value": round(dt * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+            "sample": "%d full decode steps (query encode, distances, top-%d, fp64 attention) of the same "
+                      "32K-context layer, codes precomputed" % (n, budget)}
+
+
+if __name__ == "__main__":
+    main()

@@ -40,8 +40,9 @@
  *     the call returns a status and enqueues nothing.  Values that live in
  *     device memory (kv_len, start, end) are preconditions and are not checked.
  *   - A failed launch returns ADAMAS_ERR_HIP.  The library keeps no mutable
- *     global state; calls on different streams with different workspaces may
- *     run concurrently.  Two calls that share a workspace must be ordered.
+ *     global state (the opt-in profiling setting below is per thread); calls on
+ *     different streams with different workspaces may run concurrently.  Two
+ *     calls that share a workspace must be ordered.
  */
 #ifndef ADAMAS_H
 #define ADAMAS_H
@@ -129,6 +130,22 @@ adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void
                                  uint8_t* q_codes, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/*
+ * The decode step with the key append folded in: encodes the key at position
+ * kv_len[b]-1 of every (b, kv head) into `codes` -- exactly what
+ * adamas_encode_keys(start = kv_len-1, end = kv_len) writes -- and then computes
+ * what adamas_decode_step computes, with the new key competing like any other.
+ * (The first kernel of the step encodes the key in the block that scans its
+ * position, so the append costs no separate launch.)  Same arguments, layouts,
+ * workspace size and errors as adamas_decode_step; `codes` is written at
+ * positions kv_len[b]-1 only.  Precondition: K[b][g][kv_len[b]-1] holds the new key.
+ */
+adamas_status adamas_append_decode_step(const adamas_dims* d, const void* q, const void* k,
+                                        const void* v, uint8_t* codes, const int32_t* kv_len,
+                                        int32_t budget, float scale, float* out, int32_t* sel_idx,
+                                        uint16_t* dist, uint8_t* q_codes, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace dense_decode_attention needs (0 if the dims are invalid). */
 size_t dense_decode_workspace_size(const adamas_dims* d);
 
@@ -141,6 +158,23 @@ size_t dense_decode_workspace_size(const adamas_dims* d);
 adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const void* k, const void* v,
                                      const int32_t* kv_len, float scale, float* out, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling aid, not needed for correct use.  Enables (n_events > 0) or disables
+ * (events == NULL or n_events == 0) per-kernel timing for calls made later on the
+ * CALLING THREAD: launch i of a call (counting from 0) is bracketed by the HIP
+ * events events[2*i] (start) and events[2*i+1] (stop), recorded on the call's
+ * stream by the kernel dispatch itself, for every i with 2*i+1 < n_events.
+ * Launch order: adamas_encode_keys -> 0 encode; adamas_decode_step and
+ * adamas_append_decode_step -> 0 scan, 1 select+attend; dense_decode_attention ->
+ * 0 attend, 1 combine.
+ *   events    array of hipEvent_t handles (as void*) created by the caller with
+ *             timing enabled; the array is copied, the events stay the caller's
+ *   n_events  at most 16
+ * Errors: INVALID_ARGUMENT if n_events < 0 or > 16, or events is NULL with
+ * n_events > 0.  The setting is thread-local; it changes no result.
+ */
+adamas_status adamas_profile_events(void* const* events, int32_t n_events);
 
 /* Static, NUL-terminated description of a status code. */
 const char* adamas_status_string(adamas_status s);

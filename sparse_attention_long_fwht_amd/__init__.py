@@ -45,6 +45,8 @@ _lib.adamas_decode_workspace_size.restype = ctypes.c_size_t
 _lib.adamas_decode_step.argtypes = [_dims_p, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp, _vp,
                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.adamas_decode_step.restype = ctypes.c_int
+_lib.adamas_append_decode_step.argtypes = _lib.adamas_decode_step.argtypes
+_lib.adamas_append_decode_step.restype = ctypes.c_int
 _lib.dense_decode_workspace_size.argtypes = [_dims_p]
 _lib.dense_decode_workspace_size.restype = ctypes.c_size_t
 _lib.dense_decode_attention.argtypes = [_dims_p, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
@@ -52,12 +54,14 @@ _lib.dense_decode_attention.argtypes = [_dims_p, _vp, _vp, _vp, _vp, ctypes.c_fl
 _lib.dense_decode_attention.restype = ctypes.c_int
 _lib.adamas_status_string.argtypes = [ctypes.c_int]
 _lib.adamas_status_string.restype = ctypes.c_char_p
+_lib.adamas_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+_lib.adamas_profile_events.restype = ctypes.c_int
 _lib.adamas_abi_version.argtypes = []
 _lib.adamas_abi_version.restype = ctypes.c_int32
 
 EXPORTED_SYMBOLS = ("adamas_encode_keys", "adamas_decode_workspace_size", "adamas_decode_step",
-                    "dense_decode_workspace_size", "dense_decode_attention", "adamas_status_string",
-                    "adamas_abi_version")
+                    "adamas_append_decode_step", "dense_decode_workspace_size", "dense_decode_attention", "adamas_profile_events",
+                    "adamas_status_string", "adamas_abi_version")
 
 
 class AdamasError(RuntimeError):
@@ -128,18 +132,22 @@ def alloc_workspace(nbytes, device=None):
 
 
 def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=None, dist=None, q_codes=None,
-                stream=None):
-    """One Adamas decode step; writes out [B][Hq][128] fp32 (and the optional outputs)."""
+                stream=None, append=False):
+    """One Adamas decode step; writes out [B][Hq][128] fp32 (and the optional outputs).
+
+    append=True calls adamas_append_decode_step: the key at kv_len[b]-1 is
+    encoded into `codes` first (no separate encode launch)."""
     B, Hq, hd = q.shape
     _, Hkv, cap, _ = k.shape
     d = dims(B, Hq, Hkv, cap, hd)
-    st = _lib.adamas_decode_step(ctypes.byref(d), _ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2),
+    fn = _lib.adamas_append_decode_step if append else _lib.adamas_decode_step
+    st = fn(ctypes.byref(d), _ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2),
                                  _ptr(codes, "codes", 1), _ptr(kv_len, "kv_len", 4), int(budget), float(scale),
                                  _ptr(out, "out", 4), _ptr(sel_idx, "sel_idx", 4, optional=True),
                                  _ptr(dist, "dist", 2, optional=True), _ptr(q_codes, "q_codes", 1, optional=True),
                                  _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                  _stream(stream))
-    _check(st, "adamas_decode_step")
+    _check(st, "adamas_append_decode_step" if append else "adamas_decode_step")
 
 
 def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None):
@@ -152,6 +160,15 @@ def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None):
                                      _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                      _stream(stream))
     _check(st, "dense_decode_attention")
+
+
+def profile_events(events):
+    """Time later calls on this thread kernel by kernel: `events` is a list of raw
+    hipEvent_t handles (ints); launch i is bracketed by events[2i], events[2i+1].
+    Pass None or [] to switch timing off."""
+    n = len(events) if events else 0
+    arr = (ctypes.c_void_p * max(n, 1))(*(events or [None]))
+    _check(_lib.adamas_profile_events(arr if n else None, n), "adamas_profile_events")
 
 
 def raw_library():

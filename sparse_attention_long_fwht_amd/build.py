@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libadamas.so")
-SOURCES = [os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "kernels.hip")]
+SOURCES = [os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "decode.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

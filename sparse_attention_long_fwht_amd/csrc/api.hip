@@ -9,6 +9,11 @@
 
 using adamas::Plan;
 
+namespace adamas {
+static thread_local ProfileEvents t_profile{};
+ProfileEvents& profile_events() { return t_profile; }
+}  // namespace adamas
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -49,6 +54,15 @@ const char* adamas_status_string(adamas_status s) {
 
 int32_t adamas_abi_version(void) { return ADAMAS_ABI_VERSION; }
 
+adamas_status adamas_profile_events(void* const* events, int32_t n_events) {
+  if (n_events < 0 || n_events > adamas::kMaxProfileEvents || (!events && n_events > 0))
+    return ADAMAS_ERR_INVALID_ARGUMENT;
+  adamas::ProfileEvents& pe = adamas::profile_events();
+  pe.n = events ? n_events : 0;
+  for (int i = 0; i < pe.n; ++i) pe.ev[i] = static_cast<hipEvent_t>(events[i]);
+  return ADAMAS_OK;
+}
+
 adamas_status adamas_encode_keys(const adamas_dims* d, const void* k, const int32_t* start, const int32_t* end,
                                  uint8_t* codes, void* stream) {
   adamas_status st = check_dims(d, false);
@@ -67,10 +81,14 @@ size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget) {
   return adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false).total;
 }
 
-adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void* k, const void* v,
-                                 const uint8_t* codes, const int32_t* kv_len, int32_t budget, float scale,
-                                 float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+adamas_status decode_common(const adamas_dims* d, const void* q, const void* k, const void* v, uint8_t* codes,
+                            bool append, const int32_t* kv_len, int32_t budget, float scale, float* out,
+                            int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   adamas_status st = check_dims(d, true);
   if (st != ADAMAS_OK) return st;
   if (!q || !k || !v || !codes || !kv_len || !out || budget < 1) return ADAMAS_ERR_INVALID_ARGUMENT;
@@ -81,9 +99,30 @@ adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void
   const Plan p = adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false);
   if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return ADAMAS_ERR_WORKSPACE;
   hipError_t e = adamas::launch_decode(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                       static_cast<const uint16_t*>(v), codes, kv_len, scale, out, sel_idx, dist,
-                                       q_codes, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+                                       static_cast<const uint16_t*>(v), codes, append, kv_len, scale, out, sel_idx,
+                                       dist, q_codes, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                 const uint8_t* codes, const int32_t* kv_len, int32_t budget, float scale,
+                                 float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  // codes are only read on this path
+  return decode_common(d, q, k, v, const_cast<uint8_t*>(codes), false, kv_len, budget, scale, out, sel_idx, dist,
+                       q_codes, workspace, workspace_bytes, stream);
+}
+
+adamas_status adamas_append_decode_step(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                        uint8_t* codes, const int32_t* kv_len, int32_t budget, float scale,
+                                        float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(d, q, k, v, codes, true, kv_len, budget, scale, out, sel_idx, dist, q_codes, workspace,
+                       workspace_bytes, stream);
 }
 
 size_t dense_decode_workspace_size(const adamas_dims* d) {

@@ -106,11 +106,96 @@ __device__ __forceinline__ void encode_quad(float (&x)[32], int quarter, uint32_
   hi_word = ~nhi;
 }
 
-// Wave-wide (64-lane) sum, result in every lane.
+// ---- wave-wide reductions (64 lanes) with DPP inside each 16-lane row and
+// readlane across the four rows; the result is wave-uniform.
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  v += dpp_f<kQuadXor1>(v);
+  v += dpp_f<kQuadXor2>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  v += dpp_f<kDppRowMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp_u<kQuadXor1>(v);
+  v += dpp_u<kQuadXor2>(v);
+  v += dpp_u<kDppRowHalfMirror>(v);
+  v += dpp_u<kDppRowMirror>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within each
+// 16-lane row, then row broadcasts of lanes 15 and 31).
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr1, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr2, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr4, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr8, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false);
   return v;
+}
+
+// ---- coherent global accesses between blocks of one kernel.  A store at agent
+// scope writes through the XCD's L2 and an agent-scope load bypasses it, so a
+// block can publish results to a later block on another XCD without flushing
+// the whole L2 (which a device-scope fence does on this chip).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this thread issued has completed (for the
+// write-through stores above: reached the point of coherence).  The signal
+// fence keeps the compiler from moving the stores past the wait.
+__device__ __forceinline__ void wait_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ---- MFMA 16x16x32 bf16 (gfx950).  Operand layout, lane l = 0..63:
+//   A (16 x 32): lane holds A[l % 16][8 * (l / 16) .. +8]
+//   B (32 x 16): lane holds B[8 * (l / 16) .. +8][l % 16]
+//   C (16 x 16): lane holds C[4 * (l / 16) + i][l % 16], i = 0..3
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }

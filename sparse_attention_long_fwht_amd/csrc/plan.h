@@ -19,9 +19,12 @@ constexpr int64_t kMaxCapacity = (int64_t)kMaxChunks * kMaxChunk;  // 1,048,576 
 
 struct Plan {
   int B, Hq, Hkv, R, cap, budget;
-  int chunk;  // positions per chunk (power of two)
-  int nch;    // chunks covering cap
-  size_t off_dist, off_hist, off_cinfo, off_hinfo, off_part, off_count, total;
+  int chunk;           // positions per chunk (power of two)
+  int nch;             // chunks covering cap
+  int dstride;         // distance row stride (positions), multiple of 64
+  int splits;          // blocks per query head in the select/attend kernel
+  int rows_per_split;  // selected rows each of those blocks attends over
+  size_t off_dist, off_hist, off_part, off_count, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -34,6 +37,14 @@ inline int choose_chunk(int cap) {
   return c;
 }
 
+// Rows per select/attend block: at least 256, and few enough blocks per head
+// (<= 64) that merging their partials stays cheap.
+inline int choose_rows_per_split(int budget) {
+  int r = (budget + 63) / 64;
+  r = (r + 127) / 128 * 128;
+  return r < 256 ? 256 : r;
+}
+
 inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   Plan p{};
   p.B = B;
@@ -44,33 +55,47 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   p.budget = budget;
   p.chunk = choose_chunk(cap);
   p.nch = (cap + p.chunk - 1) / p.chunk;
+  p.dstride = (cap + 63) / 64 * 64;
+  p.rows_per_split = choose_rows_per_split(budget);
+  p.splits = dense ? 1 : (budget + p.rows_per_split - 1) / p.rows_per_split;
   size_t off = 0;
   const size_t bhq = (size_t)B * Hq;
+  size_t nparts;
   if (!dense) {
     p.off_dist = off;
-    off = align256(off + bhq * (size_t)cap * sizeof(uint16_t));
+    off = align256(off + bhq * (size_t)p.dstride * sizeof(uint16_t));
     p.off_hist = off;
     off = align256(off + bhq * p.nch * kHistStride * sizeof(uint16_t));
-    p.off_cinfo = off;
-    off = align256(off + bhq * p.nch * 2 * sizeof(int32_t));
-    p.off_hinfo = off;
-    off = align256(off + bhq * 2 * sizeof(int32_t));
+    nparts = bhq * p.splits;
+  } else {
+    nparts = bhq * p.nch;
   }
   p.off_part = off;
-  off = align256(off + bhq * p.nch * kPartFloats * sizeof(float));
+  off = align256(off + nparts * kPartFloats * sizeof(float));
   p.off_count = off;
-  off = align256(off + (size_t)B * Hkv * sizeof(uint32_t));
+  off = align256(off + bhq * sizeof(uint32_t));
   p.total = off;
   return p;
 }
+
+// Per-thread kernel-timing events (adamas_profile_events).
+constexpr int kMaxProfileEvents = 16;
+struct ProfileEvents {
+  hipEvent_t ev[kMaxProfileEvents];
+  int n;
+};
+ProfileEvents& profile_events();  // this thread's setting
 
 // ---- launchers (kernels.hip) ----
 hipError_t launch_encode_keys(int B, int Hkv, int cap, const uint16_t* k, const int32_t* start,
                               const int32_t* end, uint8_t* codes, hipStream_t s);
 
-hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const uint8_t* codes, const int32_t* kv_len, float scale, float* out,
-                         int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s);
+// `append`: first encode the key at position kv_len[b]-1 of every (b, kv head)
+// into `codes` (the scan block holding that position does it); otherwise codes
+// are only read.
+hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* codes,
+                         bool append, const int32_t* kv_len, float scale, float* out, int32_t* sel_idx,
+                         uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s);
 
 hipError_t launch_dense(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const int32_t* kv_len, float scale, float* out, char* ws, hipStream_t s);

@@ -58,6 +58,7 @@ class DeviceCase:
         dist = torch.zeros((wl.B, wl.Hq, wl.cap), dtype=torch.int16, device="cuda") if want_debug else None
         qc = torch.zeros((wl.B, wl.Hq, 32), dtype=torch.uint8, device="cuda") if want_debug else None
         ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, budget))
+        ws.fill_(0xFF)  # poison: any read of scratch not written by this call shows up
         A.decode_step(self.q, self.k, self.v, self.codes, self.kv_len, budget, wl.scale, out, ws, sel_idx=sel,
                       dist=dist, q_codes=qc)
         torch.cuda.synchronize()
@@ -68,6 +69,7 @@ class DeviceCase:
         A, torch, wl = self.A, self.torch, self.wl
         out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device="cuda")
         ws = A.alloc_workspace(A.dense_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap))
+        ws.fill_(0xFF)
         A.dense_decode_attention(self.q, self.k, self.v, self.kv_len, wl.scale, out, ws)
         torch.cuda.synchronize()
         return from_dev(out)

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("adamas_encode_keys", "adamas_decode_step", "dense_decode_attention", "adamas_decode_workspace_size",
+    for n in ("adamas_encode_keys", "adamas_decode_step", "adamas_append_decode_step", "dense_decode_attention",
+              "adamas_decode_workspace_size",
               "dense_decode_workspace_size", "adamas_status_string", "adamas_abi_version"):
         assert n in names
 

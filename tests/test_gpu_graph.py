@@ -1,0 +1,56 @@
+"""HIP-graph replay of the decode step (the benchmark times graph replays).
+
+The step's launches are captured once and replayed several times, with eager
+work and synchronisations between replays; every replay must reproduce the
+eager result bit for bit (same kernels, same inputs, deterministic).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from helpers import DeviceCase, from_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_matches_eager():
+    import torch
+    import sparse_attention_long_fwht_amd as A
+
+    wl = W.llama(40, cap=20000, budget=200, B=2, kv_len=np.array([20000, 11111], np.int32))
+    case = DeviceCase(wl, A, torch)
+    start = case.kv_len - 1
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((wl.B, wl.Hq, wl.budget), dtype=torch.int32, device="cuda")
+    ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, wl.budget))
+
+    def step():
+        A.encode_keys(case.k, case.kv_len, case.codes, start=start)
+        A.decode_step(case.q, case.k, case.v, case.codes, case.kv_len, wl.budget, wl.scale, out, ws, sel_idx=sel)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_sel = from_dev(out).copy(), from_dev(sel).copy()
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-5)
+        # eager work between replays (a dense call on the same stream)
+        dout = torch.empty_like(out)
+        A.dense_decode_attention(case.q, case.k, case.v, case.kv_len, wl.scale, dout,
+                                 A.alloc_workspace(A.dense_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(out), ref_out), "replay %d: out differs" % i
+        assert np.array_equal(from_dev(sel), ref_sel), "replay %d: sel_idx differs" % i

@@ -164,6 +164,69 @@ def test_decode_is_deterministic(env):
         assert np.array_equal(x, y)
 
 
+def test_decode_reused_workspace_new_inputs(env):
+    """One workspace, three calls with different inputs (A, B, A): each result
+    must match the oracle for its own inputs, so nothing is carried over."""
+    A, torch, oracle = env
+    wa = W.llama(38, cap=6000, budget=150, B=2, Hq=8, Hkv=2, kv_len=np.array([6000, 3001], np.int32))
+    wb = W.llama(39, cap=6000, budget=150, B=2, Hq=8, Hkv=2, kv_len=np.array([4500, 6000], np.int32))
+    ca, cb = DeviceCase(wa, A, torch), DeviceCase(wb, A, torch)
+    ws = A.alloc_workspace(A.decode_workspace_size(2, 8, 2, 6000, 150))
+    ws.fill_(0xFF)
+    refs = {}
+    for name, wl in (("a", wa), ("b", wb)):
+        codes = oracle.encode_keys(wl.k, wl.kv_len)
+        refs[name] = oracle.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, 150, wl.scale)
+    for name, case in (("a", ca), ("b", cb), ("a", ca)):
+        out = torch.empty((2, 8, 128), dtype=torch.float32, device="cuda")
+        sel = torch.empty((2, 8, 150), dtype=torch.int32, device="cuda")
+        A.decode_step(case.q, case.k, case.v, case.codes, case.kv_len, 150, case.wl.scale, out, ws, sel_idx=sel)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(sel), refs[name][1]), name
+        assert_out_close(from_dev(out), refs[name][0], what="out(%s)" % name)
+
+
+def check_append_decode(A, torch, oracle, wl, budget=None):
+    """Codes hold every key but the last; adamas_append_decode_step must encode
+    key kv_len-1 and then match the oracle step on the complete codes."""
+    budget = wl.budget if budget is None else budget
+    case = DeviceCase(wl, A, torch, encode=False)
+    end_prev = to_dev(wl.kv_len - 1, torch)
+    A.encode_keys(case.k, end_prev, case.codes)  # positions [0, len-1)
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((wl.B, wl.Hq, budget), dtype=torch.int32, device="cuda")
+    qc = torch.empty((wl.B, wl.Hq, 32), dtype=torch.uint8, device="cuda")
+    ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, budget))
+    ws.fill_(0xFF)
+    A.decode_step(case.q, case.k, case.v, case.codes, case.kv_len, budget, wl.scale, out, ws, sel_idx=sel,
+                  q_codes=qc, append=True)
+    torch.cuda.synchronize()
+    codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
+    codes = from_dev(case.codes)
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        assert np.array_equal(codes[b, :, :L], codes_ref[b, :, :L]), "codes after append (b=%d)" % b
+        assert not codes[b, :, L:].any(), "append wrote past kv_len (b=%d)" % b
+    out_r, sel_r, _, qc_r = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, budget, wl.scale, threads=16,
+                                               want_dist=False)
+    assert np.array_equal(from_dev(qc), qc_r)
+    assert np.array_equal(from_dev(sel), sel_r)
+    return assert_out_close(from_dev(out), out_r)
+
+
+def test_append_decode_ragged(env):
+    A, torch, oracle = env
+    wl = W.llama(41, cap=3000, budget=100, B=3, Hq=8, Hkv=2, kv_len=np.array([3000, 1537, 1], np.int32))
+    check_append_decode(A, torch, oracle, wl)
+    wl = W.llama(42, cap=5000, budget=64, B=2, Hq=8, Hkv=1, kv_len=np.array([4097, 512], np.int32))
+    check_append_decode(A, torch, oracle, wl)
+
+
+def test_append_decode_llama32k(env):
+    A, torch, oracle = env
+    check_append_decode(A, torch, oracle, W.llama(0, cap=32768, budget=128))
+
+
 @pytest.mark.parametrize("budget", [128, 1024])
 def test_decode_llama32k(env, budget):
     """Llama-3.1-8B-shaped layer: 32 q heads / 8 kv heads, 32K context."""
