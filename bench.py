@@ -49,6 +49,15 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB, three times (the reference "
+                         "kernel that scales the HBM byte counters of a rocprofv3 --pmc run)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: write the counter summary of the dominant kernel under profiles/ from the CSV "
+                         "output of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of PMC_COMMAND")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="no GPU: write the kernel-trace summary under profiles/ from the CSV output of "
+                         "TRACE_COMMAND and the JSON line that run printed")
     return ap.parse_args()
 
 
@@ -76,6 +85,10 @@ class Hip:
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the Adamas decode step is built and timed on a single MI355X; "
@@ -94,6 +107,16 @@ def main():
     dev = torch.device("cuda", 0)
     hip = Hip()
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: %d MiB x 3" % args.calibrate_copy_mib)
+        del src, dst
 
     cap = args.context
     budget = args.budget
@@ -273,23 +296,156 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+# Source files that make up each kernel of the step; a counter summary counts
+# only while the sha256 of these files is the one it was taken on.
+CSRC = os.path.join(ROOT, "sparse_attention_long_fwht_amd", "csrc")
+KERNEL_SOURCES = {
+    "scan": ["decode.hip", "device_common.h", "plan.h"],
+    "select_attend": ["decode.hip", "device_common.h", "plan.h"],
+    "append_encode": ["kernels.hip", "device_common.h", "plan.h"],
+}
+WORKLOAD_TAG = "llama32k_b128"
+PMC_ARGS = "--steps 8 --warmup 2 --copies 4 --no-extra --no-cpu --calibrate-copy-mib 64"
+PMC_COMMAND = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc {counter} "
+               "--output-format csv -d gpurun_out/pmc_{tag} -o pmc -- python3 bench.py " + PMC_ARGS)
+TRACE_COMMAND = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -k 10 300 rocprofv3 --kernel-trace "
+                 "--stats --output-format csv -d gpurun_out/trace -o trace -- python3 bench.py --no-extra")
+COPY_KIB = 64 * 1024  # the calibration copy: reads and writes 64 MiB
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counters_path(kernel):
+    return os.path.join(PROFILE_DIR, "%s_kernel_%s_counters.txt" % (kernel, WORKLOAD_TAG))
+
+
 def read_traffic(kernel, algo_bytes):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; otherwise None."""
-    import hashlib
-    path = os.path.join(PROFILE_DIR, "%s_kernel_llama32k_counters.txt" % kernel)
+    path = counters_path(kernel)
     if not os.path.exists(path):
         return None
-    src = os.path.join(ROOT, "sparse_attention_long_fwht_amd", "csrc", "kernels.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     fields = {}
     for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernels.hip sha256[:16]") != h or "hbm_bytes_per_launch" not in fields:
+    if fields.get("source sha256[:16]") != source_hash(kernel) or "hbm_bytes_per_launch" not in fields:
         return None
     return int(float(fields["hbm_bytes_per_launch"]))
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, d))
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{kernel name: [value per dispatch]} for one counter (summed over the
+    dimensions rocprofv3 reports it in)."""
+    acc = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in acc.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Counter summary of the step's dominant kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by calibration against a copy of known size."""
+    import statistics
+    fetch = _per_dispatch(_csv_rows(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = _per_dispatch(_csv_rows(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+
+    def pick(table, sub):
+        names = [n for n in table if sub in n]
+        if not names:
+            raise SystemExit("no kernel matching %r in %s" % (sub, sorted(table)))
+        vals = [v for n in names for v in table[n]]
+        return names, vals
+
+    _, cf = pick(fetch, "copyBuffer")
+    _, cw = pick(write, "copyBuffer")
+    # the calibration copies are the largest dispatches of the copy kernel
+    f_scale = COPY_KIB / max(cf)
+    w_scale = COPY_KIB / max(cw)
+    lines = []
+    for kernel in ("select_attend", "scan"):
+        nf, vf = pick(fetch, kernel + "_kernel")
+        _, vw = pick(write, kernel + "_kernel")
+        fk, wk = statistics.mean(vf), statistics.mean(vw)
+        hbm = (fk * f_scale + wk * w_scale) * 1024
+        text = [
+            "rocprofv3 HBM byte counters: %s_kernel, Llama-3.1-8B-shaped decode layer "
+            "(batch 1, 32 q / 8 kv heads, head_dim 128, 32768 cached positions, budget 128)" % kernel,
+            "",
+            "command (FETCH_SIZE): " + PMC_COMMAND.format(counter="FETCH_SIZE", tag="fetch"),
+            "command (WRITE_SIZE): " + PMC_COMMAND.format(counter="WRITE_SIZE", tag="write"),
+            "kernel: " + nf[0],
+            "dispatches: %d (FETCH_SIZE run), %d (WRITE_SIZE run)" % (len(vf), len(vw)),
+            "FETCH_SIZE KiB/dispatch mean: %.1f  (min %.1f, max %.1f)" % (fk, min(vf), max(vf)),
+            "WRITE_SIZE KiB/dispatch mean: %.1f  (min %.1f, max %.1f)" % (wk, min(vw), max(vw)),
+            "calibration copy (%d KiB read + written): FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB" % (
+                COPY_KIB, max(cf), max(cw)),
+            "scale: FETCH_SIZE x %.3f, WRITE_SIZE x %.3f" % (f_scale, w_scale),
+            "hbm_bytes_per_launch: %d" % int(hbm),
+            "source sha256[:16]: %s  (%s)" % (source_hash(kernel), ", ".join(KERNEL_SOURCES[kernel])),
+        ]
+        os.makedirs(PROFILE_DIR, exist_ok=True)
+        with open(counters_path(kernel), "w") as fh:
+            fh.write("\n".join(text) + "\n")
+        lines.append("%s: %.0f bytes/launch" % (kernel, hbm))
+    print("\n".join(lines))
+
+
+def summarize_trace(trace_dir, bench_json):
+    """Kernel-trace statistics of TRACE_COMMAND beside the bench's own
+    event-timed kernel means from the same run."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    res = None
+    for line in open(bench_json):
+        line = line.strip()
+        if line.startswith("{"):
+            res = json.loads(line)
+    if res is None:
+        raise SystemExit("no JSON line in " + bench_json)
+    text = ["rocprofv3 kernel trace: Adamas decode step, Llama-3.1-8B-shaped decode layer "
+            "(batch 1, 32 q / 8 kv heads, head_dim 128, 32768 cached positions, budget 128)", "",
+            "command: " + TRACE_COMMAND, "",
+            "%-60s %7s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        nm = r["Name"].split("(")[0]
+        text.append("%-60s %7s %10.3f %10.3f %10.3f" % (nm[-60:], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                       float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    text += ["", "bench.py in the same run (HIP events recorded by each kernel's dispatch):",
+             "kernel_us: " + json.dumps(res["extra"]["kernel_us"]),
+             "step us (graph replay, cold): %s" % res["value"],
+             "source sha256[:16]: %s  (%s)" % (source_hash("select_attend"),
+                                             ", ".join(KERNEL_SOURCES["select_attend"]))]
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    path = os.path.join(PROFILE_DIR, "decode_step_%s_kernel_trace.txt" % WORKLOAD_TAG)
+    with open(path, "w") as fh:
+        fh.write("\n".join(text) + "\n")
+    print(path)
 
 
 def cpu_baseline(wl, budget, seconds, log):

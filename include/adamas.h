@@ -167,7 +167,9 @@ adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const 
  * stream by the kernel dispatch itself, for every i with 2*i+1 < n_events.
  * Launch order: adamas_encode_keys -> 0 encode; adamas_decode_step and
  * adamas_append_decode_step -> 0 scan, 1 select+attend; dense_decode_attention ->
- * 0 attend, 1 combine.
+ * 0 attend, 1 combine.  While timing is on, a call waits (on the host) for each
+ * of its kernels before launching the next, so that every event pair brackets
+ * one kernel and not the dispatch gap after the previous one.
  *   events    array of hipEvent_t handles (as void*) created by the caller with
  *             timing enabled; the array is copied, the events stay the caller's
  *   n_events  at most 16

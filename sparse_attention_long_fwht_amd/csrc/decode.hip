@@ -97,22 +97,36 @@ __device__ __forceinline__ void encode_wave(uint32_t qlo_bits, uint32_t qhi_bits
 }
 
 // --------------------------------------------------------------------------
-// Scan
+// Scan: distances, then a counting sort of each chunk by distance
 // --------------------------------------------------------------------------
+//
+// Per (query head, chunk) the scan leaves two things in the workspace:
+//   sorted[slot]  chunk-local positions ordered by distance (any order inside a
+//                 distance), kept only for distances <= localk, where localk is
+//                 the smallest distance with at least kk = min(k_eff, n_c)
+//                 positions at or below it (n_c = positions in the chunk);
+//   record        dmin, localk, complete (kk == n_c), n_c, then the cumulative
+//                 count cum(d) for d = dmin .. localk.
+// The k_eff smallest distances overall never go past localk of a chunk that is
+// not complete (that chunk alone has kk = k_eff positions at or below localk),
+// and a complete chunk keeps all of its positions; so the records determine the
+// threshold and the sorted prefixes hold every selected position.
 
 constexpr int kScanThreads = 512;  // one key per thread per pass
+constexpr int kHistBins = 7 * 64;  // bins as scanned by one wave: 7 per lane (385 used)
+constexpr int kScanPasses = kScanMaxChunk / kScanThreads;
 
 struct ScanArgs {
   const uint16_t* q;
   const uint16_t* k;   // read only when `append`
   uint8_t* codes;      // written only when `append` (the appended key's code)
   const int32_t* kv_len;
-  uint16_t* dist;      // [B][Hq][dstride] (workspace)
+  uint16_t* sorted;    // [B][Hq][nch][chunk]
+  uint16_t* rec;       // [B][Hq][nch][kRecStride]
   uint16_t* dist_out;  // optional [B][Hq][cap]
-  uint16_t* hist;      // [B][Hq][nch][kHistStride]
   uint8_t* q_codes;    // optional [B][Hq][32]
   uint32_t* counters;  // [B][Hq], cleared here for select_attend_kernel
-  int Hq, Hkv, cap, dstride, chunk, nch, append;
+  int Hq, Hkv, cap, chunk, nch, budget, append;
 };
 
 template <int R>
@@ -134,9 +148,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   uint4 khi = cbase[(size_t)p * 2 + 1];
   const int len = a.kv_len[b];
 
-  __shared__ uint32_t s_hist[R][kHistStride];
-  __shared__ uint32_t s_code[R + 1][8];  // query codes, then the appended key's
-  for (int i = tid; i < R * kHistStride; i += kScanThreads) (&s_hist[0][0])[i] = 0u;
+  __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins 385.. stay 0)
+  __shared__ uint32_t s_code[R + 1][8];      // query codes, then the appended key's
+  __shared__ uint32_t s_limit[R];
+  for (int i = tid; i < R * kHistBins; i += kScanThreads) (&s_hist[0][0])[i] = 0u;
   // Vectors to encode: the group's R queries, plus -- in the block holding
   // position len-1 when appending -- that key.  Wave w takes vectors w, w+8.
   const bool app_here = a.append && (len - 1) >= p0 && (len - 1) < p0 + a.chunk;
@@ -176,53 +191,119 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       qt[r][8 + w] = lo & hi;
     }
 
-  uint16_t* drow = a.dist + ((size_t)b * a.Hq + (size_t)g * R) * (size_t)a.dstride;
-#pragma unroll 1
-  for (int base = p0; base < p1; base += kScanThreads) {
-    if (base != p0) {
-      p = min(base + tid, p1 - 1);
-      klo = cbase[(size_t)p * 2];
-      khi = cbase[(size_t)p * 2 + 1];
-    }
-    p = base + tid;
-    if (p < p1) {
-      if (app_here && p == len - 1) {  // the code this block just produced
-        klo = make_uint4(s_code[R][0], s_code[R][1], s_code[R][2], s_code[R][3]);
-        khi = make_uint4(s_code[R][4], s_code[R][5], s_code[R][6], s_code[R][7]);
-      }
-      // |a - b| summed over coordinates = popcount of the three thermometer
-      // XORs (t1 = lo|hi, t2 = hi, t3 = lo&hi) over the 128 coordinates
-      const uint32_t lo[4] = {klo.x, klo.y, klo.z, klo.w};
-      const uint32_t hi[4] = {khi.x, khi.y, khi.z, khi.w};
-      uint32_t t1[4], t3[4];
+  // distances; each (key, head) takes the next rank in its distance's bin
+  uint32_t dr[kScanPasses][R];  // (distance << 16) | rank inside the bin
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        t1[w] = lo[w] | hi[w];
-        t3[w] = lo[w] & hi[w];
+  for (int pass = 0; pass < kScanPasses; ++pass) {
+    const int base = p0 + pass * kScanThreads;
+    if (base < p1) {
+      if (pass > 0) {
+        p = min(base + tid, p1 - 1);
+        klo = cbase[(size_t)p * 2];
+        khi = cbase[(size_t)p * 2 + 1];
       }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        uint32_t d = 0;
+      p = base + tid;
+      if (p < p1) {
+        if (app_here && p == len - 1) {  // the code this block just produced
+          klo = make_uint4(s_code[R][0], s_code[R][1], s_code[R][2], s_code[R][3]);
+          khi = make_uint4(s_code[R][4], s_code[R][5], s_code[R][6], s_code[R][7]);
+        }
+        // |a - b| summed over coordinates = popcount of the three thermometer
+        // XORs (t1 = lo|hi, t2 = hi, t3 = lo&hi) over the 128 coordinates
+        const uint32_t lo[4] = {klo.x, klo.y, klo.z, klo.w};
+        const uint32_t hi[4] = {khi.x, khi.y, khi.z, khi.w};
+        uint32_t t1[4], t3[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          d += __builtin_popcount(t1[w] ^ qt[r][w]);
-          d += __builtin_popcount(hi[w] ^ qt[r][4 + w]);
-          d += __builtin_popcount(t3[w] ^ qt[r][8 + w]);
+          t1[w] = lo[w] | hi[w];
+          t3[w] = lo[w] & hi[w];
         }
-        atomicAdd(&s_hist[r][d], 1u);
-        drow[(size_t)r * a.dstride + p] = (uint16_t)d;
-        if (a.dist_out) a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + p] = (uint16_t)d;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          uint32_t d = 0;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            d += __builtin_popcount(t1[w] ^ qt[r][w]);
+            d += __builtin_popcount(hi[w] ^ qt[r][4 + w]);
+            d += __builtin_popcount(t3[w] ^ qt[r][8 + w]);
+          }
+          dr[pass][r] = (d << 16) | atomicAdd(&s_hist[r][d], 1u);
+          if (a.dist_out) a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + p] = (uint16_t)d;
+        }
       }
     }
   }
   __syncthreads();
-  // histogram rows as u16 pairs
-  uint32_t* hout = reinterpret_cast<uint32_t*>(a.hist + ((size_t)(b * a.Hq + g * R) * a.nch + c) * kHistStride);
-  constexpr int W = kHistStride / 2;
-  for (int i = tid; i < R * W; i += kScanThreads) {
-    const int r = i / W;
-    const int j = i - r * W;
-    hout[(size_t)r * a.nch * W + j] = s_hist[r][2 * j] | (s_hist[r][2 * j + 1] << 16);
+
+  // per head (wave r): bin offsets, dmin, localk, and the record
+  const int n_c = p1 - p0;
+  const int kk = min(min(a.budget, len), n_c);
+  if (wave < R) {
+    const int r = wave;
+    uint32_t cnt[7], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      cnt[j] = s_hist[r][7 * lane + j];  // bins past 384 are zero
+      loc += cnt[j];
+    }
+    const uint32_t inc = wave_inclusive_scan_u32(loc);
+    const int lmin = __builtin_ffsll((long long)__ballot(loc > 0)) - 1;            // n_c >= 1
+    const int lk = __builtin_ffsll((long long)__ballot(inc >= (uint32_t)kk)) - 1;  // total n_c >= kk
+    uint32_t run = inc - loc;
+    int dmin_l = 0, localk_l = 0;
+    uint32_t limit_l = 0;
+    bool fmin = false, fk = false;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const int d = 7 * lane + j;
+      s_hist[r][d] = run;  // exclusive offset of bin d
+      run += cnt[j];
+      if (!fmin && cnt[j] > 0) {
+        fmin = true;
+        dmin_l = d;
+      }
+      if (!fk && run >= (uint32_t)kk) {
+        fk = true;
+        localk_l = d;
+        limit_l = run;
+      }
+    }
+    // (cross-lane reads stay outside lane-divergent code: a value read from
+    // lane lk must have been computed with lane lk active)
+    const int dmin = __builtin_amdgcn_readlane(dmin_l, lmin);
+    const int localk = __builtin_amdgcn_readlane(localk_l, lk);
+    const uint32_t limit = (uint32_t)__builtin_amdgcn_readlane((int)limit_l, lk);
+    uint16_t* rec = a.rec + ((size_t)(b * a.Hq + g * R + r) * a.nch + c) * kRecStride;
+    if (lane == 0) {
+      rec[0] = (uint16_t)dmin;
+      rec[1] = (uint16_t)localk;
+      rec[2] = (uint16_t)(kk == n_c ? 1 : 0);
+      rec[3] = (uint16_t)n_c;
+      s_limit[r] = limit;
+    }
+    run = inc - loc;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const int d = 7 * lane + j;
+      run += cnt[j];
+      if (d >= dmin && d <= localk) rec[4 + d - dmin] = (uint16_t)run;  // cum(d)
+    }
+  }
+  __syncthreads();
+
+  // scatter the chunk-local positions of distances <= localk, ordered by distance
+#pragma unroll
+  for (int pass = 0; pass < kScanPasses; ++pass) {
+    const int pp = p0 + pass * kScanThreads + tid;
+    if (pp < p1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t d = dr[pass][r] >> 16;
+        const uint32_t slot = s_hist[r][d] + (dr[pass][r] & 0xFFFFu);
+        if (slot < s_limit[r])
+          a.sorted[((size_t)(b * a.Hq + g * R + r) * a.nch + c) * a.chunk + slot] = (uint16_t)(pp - p0);
+      }
+    }
   }
 }
 
@@ -235,21 +316,19 @@ struct SelAttArgs {
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* kv_len;
-  const uint16_t* dist;  // [B][Hq][dstride]
-  const uint16_t* hist;  // [B][Hq][nch][kHistStride]
-  float* part;           // [B][Hq][splits][kPartFloats]
-  uint32_t* counters;    // [B][Hq]
-  int32_t* sel_idx;      // optional [B][Hq][budget]
-  float* out;            // [B][Hq][128]
-  float qscale;          // softmax scale * log2(e)
-  int Hq, Hkv, R, cap, dstride, budget, chunk, nch, splits, rows_per_split;
+  const uint16_t* sorted;  // [B][Hq][nch][chunk]
+  const uint16_t* rec;     // [B][Hq][nch][kRecStride]
+  float* part;             // [B][Hq][splits][kPartFloats]
+  uint32_t* counters;      // [B][Hq]
+  int32_t* sel_idx;        // optional [B][Hq][budget]
+  float* out;              // [B][Hq][128]
+  float qscale;            // softmax scale * log2(e)
+  int Hq, Hkv, R, cap, budget, chunk, nch, rec_win, splits, rows_per_split, bitmap_words;
 };
 
 constexpr int kSAThreads = 512;
 constexpr int kSAWaves = kSAThreads / 64;
-constexpr int kSAPPT = 64;                       // positions per thread per pass
-constexpr int kSAPass = kSAThreads * kSAPPT;     // 32768 positions per pass
-constexpr int kSATile = kSAWaves * 16;           // 128 rows per attention tile
+constexpr int kSATile = kSAWaves * 16;  // 128 rows per attention tile
 
 // Exclusive prefix sum over the block; `total` = block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wsum, uint32_t& total) {
@@ -269,29 +348,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + inc - v;
 }
 
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-
-// Number of the two 16-bit distances in w that are >= the threshold whose
-// bias (0x8000 - thr in both halves) is given: d + 0x8000 - thr has its top
-// bit set exactly when d >= thr (all values < 0x8000, so nothing wraps).
-__device__ __forceinline__ uint32_t count_ge2(uint32_t w, uint32_t bias) {
-  const u16x2_t s = __builtin_bit_cast(u16x2_t, w) + __builtin_bit_cast(u16x2_t, bias);
-  return __builtin_popcount(__builtin_bit_cast(uint32_t, s) & 0x80008000u);
-}
-
-// Distances of the 16-byte word `i` of the 64 positions a thread owns, with
-// positions at or past `len` replaced by 0x7FFF (never selected).
-__device__ __forceinline__ uint4 masked_dists(uint4 w, int pos, int len) {
-  uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = pos + 2 * j;
-    if (p >= len) x[j] = 0x7FFF7FFFu;
-    else if (p + 1 >= len) x[j] = (x[j] & 0xFFFFu) | 0x7FFF0000u;
-  }
-  return make_uint4(x[0], x[1], x[2], x[3]);
-}
-
 __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a) {
   const int bh = blockIdx.x;
   const int split = blockIdx.y;
@@ -302,28 +358,26 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   const int lane = lane_id();
   const int wave = wave_id();
 
-  extern __shared__ int s_list[];  // this split's selected positions, in order
-  __shared__ uint32_t s_tot[2][kHistStride];
-  __shared__ uint32_t s_wsum[kSAWaves];
-  __shared__ int s_T;
-  __shared__ uint32_t s_quota;
+  // dynamic LDS: [list: rows_per_split ints][keep bitmap][records | tie bitmap]
+  extern __shared__ uint32_t s_dyn[];
+  int* s_list = reinterpret_cast<int*>(s_dyn);
+  uint32_t* s_keep = s_dyn + a.rows_per_split;
+  uint32_t* s_aux = s_keep + a.bitmap_words;
+  uint16_t* s_rec = reinterpret_cast<uint16_t*>(s_aux);  // [nch][rec_win]
+  uint32_t* s_tie = s_aux;
+
+  __shared__ uint2 s_hdr[kScanMaxChunks];  // per chunk: dmin | localk << 16, complete | n << 16
+  __shared__ uint32_t s_lt[kScanMaxChunks], s_m[kScanMaxChunks + 1];
+  __shared__ uint32_t s_G[kBins];
+  __shared__ uint32_t s_wsum[kSAWaves], s_wneed[kSAWaves];
   __shared__ float s_S[kSATile];
-  __shared__ float s_m, s_l, s_corr;
+  __shared__ float s_mx, s_l, s_corr;
   __shared__ float s_red[kSAWaves][kHeadDim];
   __shared__ int s_last;
 
-  // ---- 1. loads: the first pass of distances, the chunk histograms (two
-  // threads per bin pair: even / odd chunks), kv_len and the query fragment.
-  const uint4* drow = reinterpret_cast<const uint4*>(a.dist + (size_t)bh * a.dstride);
-  const int dmax16 = a.dstride / 8 - 1;  // last 16-byte word of the row
-  uint4 dw[kSAPPT / 8];
-#pragma unroll
-  for (int i = 0; i < kSAPPT / 8; ++i) dw[i] = drow[min(tid * (kSAPPT / 8) + i, dmax16)];
+  // ---- A. loads: kv_len, the query fragment, the first rec_win words of every
+  // chunk record; the headers also go to s_hdr.
   const int len = a.kv_len[b];
-  const uint32_t* hbase = reinterpret_cast<const uint32_t*>(a.hist + (size_t)bh * a.nch * kHistStride);
-  constexpr int W = kHistStride / 2;  // bin pairs per row
-  const int hj = tid % W;
-  const int hs = tid / W;  // 0, 1 for tid < 2W; larger values are idle
   const int col = lane & 15;
   const int kg = lane >> 4;
   uint4 qf[4];
@@ -333,130 +387,213 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     for (int s = 0; s < 4; ++s)
       qf[s] = col == 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * kg) : make_uint4(0, 0, 0, 0);
   }
-  if (hs < 2) {
-    const int nch_b = (len + a.chunk - 1) / a.chunk;
-    uint32_t acc_lo = 0, acc_hi = 0;
-#pragma unroll 1
-    for (int c0 = hs; c0 < a.nch; c0 += 32) {
-      uint32_t w[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) w[u] = hbase[(size_t)min(c0 + 2 * u, a.nch - 1) * W + hj];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const bool ok = c0 + 2 * u < nch_b;
-        acc_lo += ok ? (w[u] & 0xFFFFu) : 0u;
-        acc_hi += ok ? (w[u] >> 16) : 0u;
-      }
-    }
-    s_tot[hs][2 * hj] = acc_lo;
-    s_tot[hs][2 * hj + 1] = acc_hi;
-  }
+  const uint16_t* grec = a.rec + (size_t)bh * a.nch * kRecStride;
   const int k_eff = min(a.budget, len);
+  const int nch_b = (len + a.chunk - 1) / a.chunk;
+  {
+    const int per = a.rec_win / 8;  // 16-byte words per chunk record window
+    const int n16 = a.nch * per;
+#pragma unroll 1
+    for (int i0 = 0; i0 < n16; i0 += 4 * kSAThreads) {
+      uint4 t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
+        const int cc = i / per, j = i - cc * per;
+        t[u] = *reinterpret_cast<const uint4*>(grec + (size_t)cc * kRecStride + 8 * j);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
+        reinterpret_cast<uint4*>(s_rec)[i] = t[u];
+        const int cc = i / per;
+        if (i - cc * per == 0 && cc < nch_b) s_hdr[cc] = make_uint2(t[u].x, t[u].y);
+      }
+    }
+  }
+  for (int i = tid; i < a.bitmap_words; i += kSAThreads) s_keep[i] = 0u;
   __syncthreads();
 
-  // ---- 2. threshold T = smallest distance whose cumulative count reaches
-  // k_eff; quota = how many of the ties at T are kept.
-  if (wave == 0) {
-    uint32_t loc = 0;
-#pragma unroll
-    for (int j = 0; j < 7; ++j) {
-      const int d = 7 * lane + j;
-      if (d < kBins) loc += s_tot[0][d] + s_tot[1][d];
+  // cum'(cc, d): the number of chunk cc's positions at distance <= d, where
+  // d > localk of a chunk that is not complete counts k_eff (that chunk alone
+  // then reaches k_eff; its exact count is not recorded and not needed).
+  auto cum_from = [&](const uint2 hd, uint32_t v, int d) -> uint32_t {
+    const int dm = (int)(hd.x & 0xFFFFu), lk = (int)(hd.x >> 16);
+    const uint32_t over = (hd.y & 0xFFFFu) ? (hd.y >> 16) : (uint32_t)k_eff;
+    return d < dm ? 0u : (d > lk ? over : v);
+  };
+  auto rec_index = [&](const uint2 hd, int d) -> int {
+    const int dm = (int)(hd.x & 0xFFFFu), lk = (int)(hd.x >> 16);
+    return 4 + min(max(d - dm, 0), lk - dm);
+  };
+
+  // ---- B. G'(d) = sum over chunks of cum'(cc, d), one thread per distance d.
+  // G' equals the exact count G below D* (the least localk of the chunks that
+  // are not complete) and is >= k_eff from D* on, so T, the smallest d with
+  // G(d) >= k_eff, is the number of d with G'(d) < k_eff.  The counts come
+  // from the LDS windows; if some chunk's counts run past its window (a wide
+  // spread of distances below localk), the block redoes the sums from the
+  // global records.
+  const int d_me = tid;
+  auto publish_G = [&](uint32_t gsum) {
+    if (d_me < kBins) s_G[d_me] = gsum;
+    const uint64_t below = __ballot(d_me < kBins && gsum < (uint32_t)k_eff);  // whole wave, outside the branch
+    if (lane == 0) s_wsum[wave] = (uint32_t)__builtin_popcountll(below);
+  };
+  {
+    uint32_t gsum = 0;
+    bool need = false;
+#pragma unroll 8
+    for (int cc = 0; cc < nch_b; ++cc) {
+      const uint2 hd = s_hdr[cc];
+      const int idx = rec_index(hd, d_me);
+      need |= idx >= a.rec_win;
+      gsum += cum_from(hd, s_rec[(size_t)cc * a.rec_win + min(idx, a.rec_win - 1)], d_me);
     }
-    const uint32_t inc = wave_inclusive_scan_u32(loc);
-    const uint64_t ball = __ballot(inc >= (uint32_t)k_eff);
-    const int first = __builtin_ffsll((long long)ball) - 1;  // exists: the total is len >= k_eff
-    if (lane == first) {
-      uint32_t cum = inc - loc;
-      int T = 7 * lane;
-      for (int j = 0; j < 7; ++j) {
-        const int d = 7 * lane + j;
-        const uint32_t nc = cum + s_tot[0][d] + s_tot[1][d];
-        if (nc >= (uint32_t)k_eff) {
-          T = d;
-          break;
-        }
-        cum = nc;
+    publish_G(gsum);
+    const uint64_t nb = __ballot(need);
+    if (lane == 0) s_wneed[wave] = nb != 0 ? 1u : 0u;
+  }
+  __syncthreads();
+  bool ovf = false;  // block-uniform
+#pragma unroll
+  for (int w = 0; w < kSAWaves; ++w) ovf |= s_wneed[w] != 0;
+  if (ovf) {
+    uint32_t gsum = 0;
+#pragma unroll 8
+    for (int cc = 0; cc < nch_b; ++cc) {
+      const uint2 hd = s_hdr[cc];
+      gsum += cum_from(hd, grec[(size_t)cc * kRecStride + rec_index(hd, d_me)], d_me);
+    }
+    __syncthreads();
+    publish_G(gsum);
+    __syncthreads();
+  }
+  int T = 0;
+#pragma unroll
+  for (int w = 0; w < kSAWaves; ++w) T += (int)s_wsum[w];
+  const uint32_t quota = (uint32_t)k_eff - (T > 0 ? s_G[T - 1] : 0u);
+
+  // ---- E. per chunk: positions below T (slots [0, lt) of its sorted prefix)
+  // and at T (the next eq slots); m = lt + eq entries to read.
+  uint32_t total_m;
+  {
+    uint32_t m = 0;
+    if (tid < nch_b) {
+      const uint2 hd = s_hdr[tid];
+      const int i0 = rec_index(hd, T - 1), i1 = rec_index(hd, T);
+      uint32_t v0 = s_rec[(size_t)tid * a.rec_win + min(i0, a.rec_win - 1)];
+      uint32_t v1 = s_rec[(size_t)tid * a.rec_win + min(i1, a.rec_win - 1)];
+      if (ovf) {  // (volatile: kept apart from the LDS reads above, never merged into a generic load)
+        v0 = reinterpret_cast<const volatile uint16_t*>(grec)[(size_t)tid * kRecStride + i0];
+        v1 = reinterpret_cast<const volatile uint16_t*>(grec)[(size_t)tid * kRecStride + i1];
       }
-      s_T = T;
-      s_quota = (uint32_t)k_eff - cum;
+      const uint32_t lt = cum_from(hd, v0, T - 1);
+      m = cum_from(hd, v1, T);
+      s_lt[tid] = lt;
+    }
+    const uint32_t before = block_exclusive_scan(m, s_wsum, total_m);
+    if (tid < nch_b) s_m[tid] = before;
+    if (tid == 0) s_m[nch_b] = total_m;
+  }
+  // (the scan's barriers order the record reads above before the tie bitmap
+  // overwrites the record area)
+  for (int i = tid; i < a.bitmap_words; i += kSAThreads) s_tie[i] = 0u;
+  __syncthreads();
+
+  // ---- F. mark the selected positions: below T -> keep bitmap, at T -> tie
+  // bitmap.  Flat index f over all chunks' entries; chunk by binary search.
+  {
+    const uint16_t* gsorted = a.sorted + (size_t)bh * a.nch * a.chunk;
+#pragma unroll 1
+    for (int f0 = 0; f0 < (int)total_m; f0 += 4 * kSAThreads) {
+      int pos[4];
+      bool is_lt[4];
+      uint16_t lp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = min(f0 + u * kSAThreads + tid, (int)total_m - 1);
+        int lo = 0, hi = nch_b - 1;  // last chunk cc with s_m[cc] <= f
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if ((int)s_m[mid] <= f) lo = mid;
+          else hi = mid - 1;
+        }
+        const int slot = f - (int)s_m[lo];
+        lp[u] = gsorted[(size_t)lo * a.chunk + slot];
+        pos[u] = lo * a.chunk;
+        is_lt[u] = (uint32_t)slot < s_lt[lo];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (f0 + u * kSAThreads + tid < (int)total_m) {
+          const int pp = pos[u] + lp[u];
+          atomicOr((is_lt[u] ? s_keep : s_tie) + (pp >> 5), 1u << (pp & 31));
+        }
+      }
     }
   }
   __syncthreads();
-  const uint32_t T = (uint32_t)s_T;
-  const uint32_t quota = s_quota;
-  const uint32_t biasT = (0x8000u - T) * 0x10001u;        // d >= T
-  const uint32_t biasT1 = (0x8000u - T - 1u) * 0x10001u;  // d >= T + 1
 
-  // ---- 3. ordered compaction.  Thread t owns positions [base + 64t, +64) of
-  // a pass; every distance < T is kept, ties at T while the running tie count
-  // (in position order) is below quota.  This split keeps global ranks
-  // [lo_rank, hi_rank) of the selection.
+  // ---- G. ties: keep the `quota` lowest positions at T.  H. emit the kept
+  // positions in ascending order; ranks [lo_rank, hi_rank) belong to this split.
+  const int wpt = (a.bitmap_words + kSAThreads - 1) / kSAThreads;  // words per thread
+  const int w0 = tid * wpt;
+  const int w1 = min(w0 + wpt, a.bitmap_words);
+  {
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __builtin_popcount(s_tie[w]);
+    uint32_t tot;
+    uint32_t r = block_exclusive_scan(cnt, s_wsum, tot);
+    if (tot > quota) {
+      for (int w = w0; w < w1 && r < quota; ++w) {
+        uint32_t bits = s_tie[w];
+        while (bits && r < quota) {
+          const uint32_t bit = bits & (0u - bits);
+          bits ^= bit;
+          s_keep[w] |= bit;
+          ++r;
+        }
+      }
+    } else {
+      for (int w = w0; w < w1; ++w) s_keep[w] |= s_tie[w];
+    }
+  }
+  __syncthreads();
   const int lo_rank = split * a.rows_per_split;
   const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
-  uint32_t carry_eq = 0, carry_sel = 0;
-#pragma unroll 1
-  for (int base = 0; base < len && lo_rank < hi_rank && (int)carry_sel < hi_rank; base += kSAPass) {
-    const int pos0 = base + tid * kSAPPT;
-    if (base != 0) {
-#pragma unroll
-      for (int i = 0; i < kSAPPT / 8; ++i) dw[i] = drow[min((base >> 3) + tid * (kSAPPT / 8) + i, dmax16)];
-    }
-    if (pos0 + kSAPPT > len) {
-#pragma unroll
-      for (int i = 0; i < kSAPPT / 8; ++i) dw[i] = masked_dists(dw[i], pos0 + 8 * i, len);
-    }
-    uint32_t ge = 0, ge1 = 0;
-#pragma unroll
-    for (int i = 0; i < kSAPPT / 8; ++i) {
-      ge += count_ge2(dw[i].x, biasT) + count_ge2(dw[i].y, biasT) + count_ge2(dw[i].z, biasT) +
-            count_ge2(dw[i].w, biasT);
-      ge1 += count_ge2(dw[i].x, biasT1) + count_ge2(dw[i].y, biasT1) + count_ge2(dw[i].z, biasT1) +
-             count_ge2(dw[i].w, biasT1);
-    }
-    const uint32_t lt = kSAPPT - ge;  // masked positions count as >= T
-    const uint32_t eq = ge - ge1;
-    uint32_t tot_eq, tot_sel;
-    const uint32_t e_before = carry_eq + block_exclusive_scan(eq, s_wsum, tot_eq);
-    const uint32_t take = quota > e_before ? min(quota - e_before, eq) : 0u;
-    const uint32_t s_before = carry_sel + block_exclusive_scan(lt + take, s_wsum, tot_sel);
-    if (lt + take > 0 && (int)s_before < hi_rank && (int)(s_before + lt + take) > lo_rank) {
-      uint32_t r = s_before, ties = 0;
-#pragma unroll 1
-      for (int i = 0; i < kSAPPT / 8; ++i) {
-        uint4 w = drow[min((pos0 >> 3) + i, dmax16)];
-        w = masked_dists(w, pos0 + 8 * i, len);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t d = (ww[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-          bool keep = d < T;
-          if (d == T) keep = ties++ < take;
-          if (keep) {
-            if ((int)r >= lo_rank && (int)r < hi_rank) {
-              const int pp = pos0 + 8 * i + j;
-              s_list[r - lo_rank] = pp;
-              if (a.sel_idx) a.sel_idx[(size_t)bh * a.budget + r] = pp;
-            }
-            ++r;
+  {
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __builtin_popcount(s_keep[w]);
+    uint32_t tot;
+    uint32_t r = block_exclusive_scan(cnt, s_wsum, tot);
+    if (cnt > 0 && (int)r < hi_rank && (int)(r + cnt) > lo_rank) {
+      for (int w = w0; w < w1; ++w) {
+        uint32_t bits = s_keep[w];
+        while (bits) {
+          const int bit = __builtin_ctz(bits);
+          bits &= bits - 1;
+          if ((int)r >= lo_rank && (int)r < hi_rank) {
+            const int pp = 32 * w + bit;
+            s_list[r - lo_rank] = pp;
+            if (a.sel_idx) a.sel_idx[(size_t)bh * a.budget + r] = pp;
           }
+          ++r;
         }
       }
     }
-    carry_eq += tot_eq;
-    carry_sel += tot_sel;
   }
   if (a.sel_idx && split == 0) {
     for (int i = k_eff + tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
   }
   const int nrows = max(0, hi_rank - lo_rank);
   if (tid == 0) {
-    s_m = -INFINITY;
+    s_mx = -INFINITY;
     s_l = 0.f;
   }
   __syncthreads();
 
-  // ---- 4. attention over the split's rows: tiles of 128 rows (16 per wave).
+  // ---- I. attention over the split's rows: tiles of 128 rows (16 per wave).
   float o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.f;
@@ -491,7 +628,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     __syncthreads();
     if (wave == 0) {
       const float x0 = s_S[lane], x1 = s_S[lane + 64];
-      const float mo = s_m;
+      const float mo = s_mx;
       const float mn = fmaxf(mo, wave_max(fmaxf(x0, x1)));  // finite: the tile has >= 1 row
       const float cr = exp2f(mo - mn);
       const float p0 = x0 == -INFINITY ? 0.f : exp2f(x0 - mn);
@@ -501,7 +638,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
       const float ts = wave_sum(p0 + p1);
       if (lane == 0) {
         s_corr = cr;
-        s_m = mn;
+        s_mx = mn;
         s_l = __builtin_fmaf(s_l, cr, ts);
       }
     }
@@ -545,7 +682,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     return;
   }
 
-  // ---- 5. several splits: publish (m, l, o) write-through, count, and let the
+  // ---- J. several splits: publish (m, l, o) write-through, count, and let the
   // last split of this head merge them.
   float* pc = a.part + ((size_t)bh * a.splits + split) * kPartFloats;
   if (tid < kHeadDim) {
@@ -554,7 +691,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     for (int w = 0; w < kSAWaves; ++w) O += s_red[w][tid];
     store_coherent(pc + 4 + tid, O);
     if (tid == 0) {
-      store_coherent(pc, s_m);
+      store_coherent(pc, s_mx);
       store_coherent(pc + 1, s_l);
     }
   }
@@ -622,13 +759,13 @@ static void launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
 hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* codes,
                          bool append, const int32_t* kv_len, float scale, float* out, int32_t* sel_idx,
                          uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s) {
-  uint16_t* ws_dist = reinterpret_cast<uint16_t*>(ws + p.off_dist);
-  uint16_t* ws_hist = reinterpret_cast<uint16_t*>(ws + p.off_hist);
+  uint16_t* ws_sorted = reinterpret_cast<uint16_t*>(ws + p.off_sorted);
+  uint16_t* ws_rec = reinterpret_cast<uint16_t*>(ws + p.off_rec);
   float* ws_part = reinterpret_cast<float*>(ws + p.off_part);
   uint32_t* counters = reinterpret_cast<uint32_t*>(ws + p.off_count);
 
-  ScanArgs sa{q,        k,       codes,   kv_len, ws_dist, dist,    ws_hist, q_codes,
-              counters, p.Hq,    p.Hkv,   p.cap,  p.dstride, p.chunk, p.nch, append ? 1 : 0};
+  ScanArgs sa{q,       k,     codes,   kv_len, ws_sorted, ws_rec,   dist,          q_codes,
+              counters, p.Hq, p.Hkv, p.cap, p.chunk,   p.nch,    p.budget, append ? 1 : 0};
   switch (p.R) {
     case 1: launch_scan<1>(p, sa, s); break;
     case 2: launch_scan<2>(p, sa, s); break;
@@ -636,16 +773,22 @@ hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, co
     case 8: launch_scan<8>(p, sa, s); break;
     default: return hipErrorInvalidValue;
   }
-  SelAttArgs aa{q,      k,        v,       kv_len, ws_dist, ws_hist, ws_part, counters, sel_idx, out,
-                scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.dstride, p.budget, p.chunk, p.nch,
-                p.splits, p.rows_per_split};
-  const size_t lds = (size_t)p.rows_per_split * sizeof(int);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_attend_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // In timing mode the select/attend kernel waits for the scan on the host, so
+  // that its events bracket that kernel alone (not the dispatch gap after the scan).
+  const ProfileEvents& pe = profile_events();
+  if (pe.n >= 4) {
+    hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess) return e;
   }
-  launch_k(1, select_attend_kernel, dim3(p.B * p.Hq, p.splits), dim3(kSAThreads), (uint32_t)lds, s, aa);
+  SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
+                scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch, p.rec_win,
+                p.splits, p.rows_per_split, p.bitmap_words};
+  if (p.lds_select > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_attend_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_select);
+    if (e != hipSuccess) return e;
+  }
+  launch_k(1, select_attend_kernel, dim3(p.B * p.Hq, p.splits), dim3(kSAThreads), (uint32_t)p.lds_select, s, aa);
   return hipGetLastError();
 }
 

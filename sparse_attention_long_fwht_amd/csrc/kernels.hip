@@ -334,6 +334,10 @@ static hipError_t launch_dense_r(const Plan& p, const uint16_t* q, const uint16_
   float* ws_part = reinterpret_cast<float*>(ws + p.off_part);
   AttendArgs aa{q, k, v, kv_len, ws_part, scale * 1.4426950408889634f, p.Hq, p.Hkv, p.cap, p.chunk, p.nch};
   launch_k(0, dense_attend_kernel<R>, dim3(p.nch, p.B * p.Hkv), dim3(256), 0, s, aa);
+  if (profile_events().n >= 4) {  // timing mode: see adamas_profile_events
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+  }
   launch_k(1, combine_kernel<R>, dim3(p.B * p.Hkv), dim3(256), 0, s, (const float*)ws_part, kv_len, out, p.Hq,
            p.Hkv, p.chunk, p.nch);
   return hipGetLastError();

@@ -10,39 +10,43 @@ namespace adamas {
 constexpr int kHeadDim = 128;
 constexpr int kCodeBytes = 32;
 constexpr int kBins = 385;        // distances 0..384 (128 coordinates x largest code gap 3)
-constexpr int kHistStride = 392;  // u16 entries per stored histogram row (784 B, 16 B aligned)
-constexpr int kMaxChunks = 128;           // chunks per (batch, kv head)
-constexpr int kMinChunk = 512;            // positions per chunk, lower bound
-constexpr int kMaxChunk = 8192;           // upper bound (LDS list of one chunk)
-constexpr int kPartFloats = 132;          // m, l, 2 pad, o[128]
-constexpr int64_t kMaxCapacity = (int64_t)kMaxChunks * kMaxChunk;  // 1,048,576 positions
+// Sparse path: chunks of the scan (one block per (b, kv head, chunk)).
+constexpr int kScanMinChunk = 512;   // = threads of the scan block: one key per thread per pass
+constexpr int kScanMaxChunk = 2048;  // at most four passes per block
+constexpr int kScanMaxChunks = 256;  // chunks per (b, kv head)
+constexpr int64_t kMaxCapacity = (int64_t)kScanMaxChunks * kScanMaxChunk;  // 524,288 positions
+constexpr int kRecStride = 392;      // u16 per (head, chunk) record: 4 header words + up to 385 bins
+// Dense baseline: chunks of the split-K attention.
+constexpr int kMaxChunks = 128;      // dense chunks per (b, kv head)
+constexpr int kPartFloats = 132;     // m, l, 2 pad, o[128]
 
 struct Plan {
   int B, Hq, Hkv, R, cap, budget;
   int chunk;           // positions per chunk (power of two)
   int nch;             // chunks covering cap
-  int dstride;         // distance row stride (positions), multiple of 64
+  int rec_win;         // record words per chunk read in one go by the select/attend kernel
   int splits;          // blocks per query head in the select/attend kernel
   int rows_per_split;  // selected rows each of those blocks attends over
-  size_t off_dist, off_hist, off_part, off_count, total;
+  int bitmap_words;    // ceil(cap / 32)
+  size_t lds_select;   // dynamic LDS of the select/attend kernel
+  size_t off_sorted, off_rec, off_part, off_count, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Chunk size: the smallest power of two >= kMinChunk that keeps cap within
-// kMaxChunks chunks.
-inline int choose_chunk(int cap) {
-  int c = kMinChunk;
-  while ((int64_t)c * kMaxChunks < cap) c <<= 1;
+inline int choose_chunk(int cap, int min_chunk, int max_chunks) {
+  int c = min_chunk;
+  while ((int64_t)c * max_chunks < cap) c <<= 1;
   return c;
 }
 
-// Rows per select/attend block: at least 256, and few enough blocks per head
-// (<= 64) that merging their partials stays cheap.
+// Rows per select/attend block: one 128-row attention tile for budgets up to
+// 2048 (so a head's selection is spread over up to 16 blocks), growing beyond
+// that so that at most 64 blocks share a head.
 inline int choose_rows_per_split(int budget) {
   int r = (budget + 63) / 64;
   r = (r + 127) / 128 * 128;
-  return r < 256 ? 256 : r;
+  return r < 128 ? 128 : r;
 }
 
 inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
@@ -53,25 +57,35 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   p.R = Hq / Hkv;
   p.cap = cap;
   p.budget = budget;
-  p.chunk = choose_chunk(cap);
-  p.nch = (cap + p.chunk - 1) / p.chunk;
-  p.dstride = (cap + 63) / 64 * 64;
-  p.rows_per_split = choose_rows_per_split(budget);
-  p.splits = dense ? 1 : (budget + p.rows_per_split - 1) / p.rows_per_split;
-  size_t off = 0;
   const size_t bhq = (size_t)B * Hq;
-  size_t nparts;
-  if (!dense) {
-    p.off_dist = off;
-    off = align256(off + bhq * (size_t)p.dstride * sizeof(uint16_t));
-    p.off_hist = off;
-    off = align256(off + bhq * p.nch * kHistStride * sizeof(uint16_t));
-    nparts = bhq * p.splits;
-  } else {
-    nparts = bhq * p.nch;
+  size_t off = 0;
+  if (dense) {
+    p.chunk = choose_chunk(cap, 512, kMaxChunks);
+    p.nch = (cap + p.chunk - 1) / p.chunk;
+    p.splits = 1;
+    p.off_part = off;
+    off = align256(off + bhq * p.nch * kPartFloats * sizeof(float));
+    p.off_count = off;
+    off = align256(off + bhq * sizeof(uint32_t));
+    p.total = off;
+    return p;
   }
+  p.chunk = choose_chunk(cap, kScanMinChunk, kScanMaxChunks);
+  p.nch = (cap + p.chunk - 1) / p.chunk;
+  p.rec_win = p.nch <= 64 ? 256 : 64;
+  p.rows_per_split = choose_rows_per_split(budget);
+  p.splits = (budget + p.rows_per_split - 1) / p.rows_per_split;
+  p.bitmap_words = ((cap + 31) / 32 + 3) / 4 * 4;  // keeps the record area 16-byte aligned
+  const size_t rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);
+  const size_t tie_bytes = (size_t)p.bitmap_words * sizeof(uint32_t);
+  p.lds_select = (size_t)p.rows_per_split * sizeof(int) + (size_t)p.bitmap_words * sizeof(uint32_t) +
+                 (rec_bytes > tie_bytes ? rec_bytes : tie_bytes);
+  p.off_sorted = off;
+  off = align256(off + bhq * (size_t)p.nch * p.chunk * sizeof(uint16_t));
+  p.off_rec = off;
+  off = align256(off + bhq * (size_t)p.nch * kRecStride * sizeof(uint16_t));
   p.off_part = off;
-  off = align256(off + nparts * kPartFloats * sizeof(float));
+  off = align256(off + bhq * p.splits * kPartFloats * sizeof(float));
   p.off_count = off;
   off = align256(off + bhq * sizeof(uint32_t));
   p.total = off;

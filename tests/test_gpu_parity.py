@@ -141,6 +141,55 @@ def test_decode_heavy_ties(env):
     check_decode(DeviceCase(wl, A, torch), oracle)
 
 
+def widest_record(wl, dist, budget):
+    """Largest per-chunk record (4 header words + one count per distance from
+    the chunk's smallest distance up to its localk) over all heads, with the
+    library's chunking: 512-position chunks while a head has at most 256 of
+    them; the select kernel keeps the first 256 record words of each chunk in
+    LDS when a head has at most 64 chunks, else the first 64."""
+    chunk = 512
+    while chunk * 256 < wl.cap:
+        chunk *= 2
+    nch = -(-wl.cap // chunk)
+    window = 256 if nch <= 64 else 64
+    worst = 0
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        k_eff = min(budget, L)
+        for h in range(wl.Hq):
+            d = dist[b, h, :L].astype(np.int64)
+            for c0 in range(0, L, chunk):
+                dc = np.sort(d[c0:c0 + chunk])
+                kk = min(k_eff, len(dc))
+                worst = max(worst, 4 + int(dc[kk - 1] - dc[0]))
+    return worst, window
+
+
+def test_decode_record_window_overflow(env):
+    """Chunk records longer than the select kernel's LDS window: the threshold
+    counts then come from the global records.  (a) 79 chunks, so 64-word
+    windows, budget 1024; (b) 4 chunks with 256-word windows, where one query's
+    transform is exactly a +-1 vector (codes 0 and 3 only) and chunk 0 holds
+    keys equal to that query (distance 0) and to its negation (distance 384)."""
+    A, torch, oracle = env
+    wa = W.llama(50, cap=40000, budget=1024, B=1, Hq=8, Hkv=2)
+    wb = W.llama(51, cap=2048, budget=520, B=1, Hq=2, Hkv=1)
+    H = np.array([[1.0]], np.float32)
+    while H.shape[0] < 128:
+        H = np.block([[H, H], [H, -H]])
+    s = np.where(np.random.default_rng(7).random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+    qv = (H @ s) / 128.0  # multiples of 1/64 in [-1, 1]: exact in bf16, and H @ qv == s exactly
+    wb.q[0, 0] = W.f32_to_bf16(qv.astype(np.float32))
+    wb.k[0, 0, 0:100] = W.f32_to_bf16(-qv.astype(np.float32))
+    wb.k[0, 0, 100:110] = wb.q[0, 0]
+    for wl in (wa, wb):
+        codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
+        _, _, dist_r, _ = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, wl.budget, wl.scale, threads=8)
+        worst, window = widest_record(wl, dist_r, wl.budget)
+        assert worst > window, "case does not reach the overflow path (%d <= %d)" % (worst, window)
+        check_decode(DeviceCase(wl, A, torch), oracle)
+
+
 def test_decode_full_budget_equals_dense(env):
     A, torch, oracle = env
     wl = W.llama(35, cap=1500, budget=2000, B=2, Hq=8, Hkv=2, kv_len=np.array([1500, 733], np.int32))
