@@ -94,7 +94,8 @@ adamas_status adamas_encode_keys(const adamas_dims* d, const void* k, const int3
                                  const int32_t* end, uint8_t* codes, void* stream);
 
 /* Bytes of workspace adamas_decode_step needs for these dims and budget (0 if
- * the arguments are invalid).  Any alignment of 256 bytes is sufficient. */
+ * the arguments are invalid or the combination is unsupported).  Any alignment
+ * of 256 bytes is sufficient. */
 size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget);
 
 /*
@@ -122,7 +123,10 @@ size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget);
  *              bytes, 256-byte aligned; its contents need no initialisation and
  *              are meaningless after the call.
  * Codes, distances and sel_idx are deterministic integers; out is deterministic
- * for fixed inputs.  Errors: INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE, HIP.
+ * for fixed inputs.  Errors: INVALID_ARGUMENT, UNSUPPORTED (also: a budget so
+ * large at a large capacity that the per-head selection state exceeds one
+ * block's on-chip memory -- the budget is supported whenever
+ * adamas_decode_workspace_size returns nonzero), WORKSPACE, HIP.
  */
 adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void* k, const void* v,
                                  const uint8_t* codes, const int32_t* kv_len, int32_t budget,

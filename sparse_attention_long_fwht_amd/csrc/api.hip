@@ -78,7 +78,8 @@ adamas_status adamas_encode_keys(const adamas_dims* d, const void* k, const int3
 
 size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget) {
   if (check_dims(d, true) != ADAMAS_OK || budget < 1) return 0;
-  return adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false).total;
+  const Plan p = adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false);
+  return p.supported ? p.total : 0;
 }
 
 }  // extern "C"
@@ -97,6 +98,7 @@ adamas_status decode_common(const adamas_dims* d, const void* q, const void* k, 
       (q_codes && !aligned(q_codes, 4)))
     return ADAMAS_ERR_INVALID_ARGUMENT;
   const Plan p = adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false);
+  if (!p.supported) return ADAMAS_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return ADAMAS_ERR_WORKSPACE;
   hipError_t e = adamas::launch_decode(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                        static_cast<const uint16_t*>(v), codes, append, kv_len, scale, out, sel_idx,

@@ -129,17 +129,34 @@ struct ScanArgs {
   int Hq, Hkv, cap, chunk, nch, budget, append;
 };
 
+// Blocks are dealt to the eight XCDs round-robin by linear block index.  When
+// the number of groups allows it, all chunks of one (b, kv head) group go to the
+// same XCD, so the group's query rows are fetched into one L2 only.
+constexpr int kXcds = 8;
+
 template <int R>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
-  const int bg = blockIdx.y;
+  const int G = (int)gridDim.x / a.nch;  // (b, kv head) groups
+  int bg, c;
+  if (G % kXcds == 0) {
+    const int xcd = (int)blockIdx.x % kXcds, s = (int)blockIdx.x / kXcds;
+    bg = xcd + kXcds * (s / a.nch);
+    c = s % a.nch;
+  } else {
+    bg = (int)blockIdx.x / a.nch;
+    c = (int)blockIdx.x % a.nch;
+  }
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
-  const int c = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
   const int p0 = c * a.chunk;
 
+  // the query rows first (wave w < R encodes query w), so that the encode does
+  // not wait behind the key-code loads
+  const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)(g * R + min(wave, R - 1))) * kHeadDim;
+  const uint16_t q_lo = qrow[lane], q_hi = qrow[lane + 64];
   // first pass of key codes, addresses clamped to the capacity so that they
   // do not wait for kv_len
   const uint4* cbase = reinterpret_cast<const uint4*>(a.codes + (size_t)bg * (size_t)a.cap * kCodeBytes);
@@ -158,10 +175,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int nvec = R + (app_here ? 1 : 0);
 #pragma unroll 1
   for (int vi = wave; vi < nvec; vi += kScanThreads / 64) {
-    const uint16_t* row = vi < R ? a.q + ((size_t)b * a.Hq + (size_t)(g * R + vi)) * kHeadDim
-                                 : a.k + ((size_t)bg * a.cap + (size_t)(len - 1)) * kHeadDim;
+    uint32_t xlo = q_lo, xhi = q_hi;  // vi < R: vi == wave, the row loaded above
+    if (vi >= R) {
+      const uint16_t* row = a.k + ((size_t)bg * a.cap + (size_t)(len - 1)) * kHeadDim;
+      xlo = row[lane];
+      xhi = row[lane + 64];
+    }
     uint32_t lo[4], hi[4];
-    encode_wave(row[lane], row[lane + 64], lo, hi);
+    encode_wave(xlo, xhi, lo, hi);
     if (lane < 8) {
       const uint32_t w = lane < 4 ? lo[lane & 3] : hi[lane & 3];
       s_code[vi][lane] = w;
@@ -323,29 +344,101 @@ struct SelAttArgs {
   int32_t* sel_idx;        // optional [B][Hq][budget]
   float* out;              // [B][Hq][128]
   float qscale;            // softmax scale * log2(e)
-  int Hq, Hkv, R, cap, budget, chunk, nch, rec_win, splits, rows_per_split, bitmap_words;
+  int Hq, Hkv, R, cap, budget, chunk, nch, rec_win, pre_slots, splits, rows_per_split, bitmap_words;
 };
 
 constexpr int kSAThreads = 512;
 constexpr int kSAWaves = kSAThreads / 64;
 constexpr int kSATile = kSAWaves * 16;  // 128 rows per attention tile
 
-// Exclusive prefix sum over the block; `total` = block sum.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wsum, uint32_t& total) {
+// Inclusive prefix sum over the block of one value per thread (every thread
+// calls it).  `before` = exclusive prefix, `total` = block sum.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* s_wsum, uint32_t& before, uint32_t& total) {
   const int lane = lane_id(), wave = wave_id();
   const uint32_t inc = wave_inclusive_scan_u32(v);
   if (lane == 63) s_wsum[wave] = inc;
   __syncthreads();
-  uint32_t before = 0, tot = 0;
+  uint32_t b = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kSAWaves; ++w) {
     const uint32_t x = s_wsum[w];
-    before += w < wave ? x : 0u;
+    b += w < wave ? x : 0u;
     tot += x;
   }
   __syncthreads();
   total = tot;
-  return before + inc - v;
+  before = b + inc - v;
+  return b + inc;
+}
+
+// The same for two values at once (each block sum below 2^32).
+__device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t* s_wsum2, uint32_t& before0,
+                                            uint32_t& before1, uint32_t& total0, uint32_t& total1) {
+  const int lane = lane_id(), wave = wave_id();
+  const uint32_t inc0 = wave_inclusive_scan_u32(v0);
+  const uint32_t inc1 = wave_inclusive_scan_u32(v1);
+  if (lane == 63) {
+    s_wsum2[2 * wave] = inc0;
+    s_wsum2[2 * wave + 1] = inc1;
+  }
+  __syncthreads();
+  uint32_t b0 = 0, b1 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+  for (int w = 0; w < kSAWaves; ++w) {
+    const uint32_t x0 = s_wsum2[2 * w], x1 = s_wsum2[2 * w + 1];
+    b0 += w < wave ? x0 : 0u;
+    b1 += w < wave ? x1 : 0u;
+    t0 += x0;
+    t1 += x1;
+  }
+  __syncthreads();
+  before0 = b0 + inc0 - v0;
+  before1 = b1 + inc1 - v1;
+  total0 = t0;
+  total1 = t1;
+}
+
+// Selection with every chunk's entries in one group of S >= m lanes (see
+// select_attend_kernel, step F).
+struct SortedEmit {
+  const uint4* cinfo;      // per chunk: m, lt, first kept rank, ties before it
+  const uint16_t* pre;     // LDS sorted prefixes [nch][pre_slots]
+  const uint16_t* gsorted; // the head's sorted slots in the workspace
+  int pre_slots, chunk, nch_b;
+  uint32_t quota;
+  int lo_rank, hi_rank;
+  int* list;               // LDS rows of this split
+  int32_t* sel;            // optional sel_idx row of the head
+};
+
+template <int S>
+__device__ __forceinline__ void emit_sorted(const SortedEmit& e) {
+  const int lane = lane_id(), wave = wave_id();
+  constexpr int cpi = 64 / S;  // chunks per wave per iteration
+  const int j = lane & (S - 1);
+  const uint64_t gmask = S == 64 ? ~0ull : (((1ull << S) - 1ull) << (lane & ~(S - 1)));
+#pragma unroll 1
+  for (int c0 = wave * cpi; c0 < e.nch_b; c0 += kSAWaves * cpi) {
+    const int cc = c0 + lane / S;
+    const uint4 ci = cc < e.nch_b ? e.cinfo[cc] : make_uint4(0u, 0u, 0u, 0u);
+    uint32_t key = 0xFFFFFFFFu;
+    if (j < (int)ci.x) {
+      uint32_t lp = e.pre[(size_t)cc * e.pre_slots + min(j, e.pre_slots - 1)];
+      if (j >= e.pre_slots) lp = reinterpret_cast<const volatile uint16_t*>(e.gsorted)[(size_t)cc * e.chunk + j];
+      key = ((uint32_t)(cc * e.chunk + (int)lp) << 1) | (j >= (int)ci.y ? 1u : 0u);
+    }
+    key = group_sort_u32<S>(key);
+    const bool valid = key != 0xFFFFFFFFu;
+    const bool tie = valid && (key & 1u);
+    const uint32_t tie_rank = lanes_below(__ballot(tie) & gmask);
+    const bool kept = valid && (!tie || ci.w + tie_rank < e.quota);
+    const uint32_t r = ci.z + lanes_below(__ballot(kept) & gmask);
+    if (kept && (int)r >= e.lo_rank && (int)r < e.hi_rank) {
+      const int pp = (int)(key >> 1);
+      e.list[r - e.lo_rank] = pp;
+      if (e.sel) e.sel[r] = pp;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a) {
@@ -353,30 +446,35 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   const int split = blockIdx.y;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
-  const int g = h / a.R;
+  const int g = h >> __builtin_ctz(a.R);  // R is a power of two
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
 
-  // dynamic LDS: [list: rows_per_split ints][keep bitmap][records | tie bitmap]
-  extern __shared__ uint32_t s_dyn[];
+  // dynamic LDS: [list: rows_per_split ints][keep bitmap][sorted prefixes: nch x
+  // pre_slots u16][records: nch x rec_win u16 | tie bitmap]
+  extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // 16-byte aligned: uint4 accesses
   int* s_list = reinterpret_cast<int*>(s_dyn);
   uint32_t* s_keep = s_dyn + a.rows_per_split;
-  uint32_t* s_aux = s_keep + a.bitmap_words;
-  uint16_t* s_rec = reinterpret_cast<uint16_t*>(s_aux);  // [nch][rec_win]
+  uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_keep + a.bitmap_words);
+  uint32_t* s_aux = s_keep + a.bitmap_words + a.nch * a.pre_slots / 2;
+  uint16_t* s_rec = reinterpret_cast<uint16_t*>(s_aux);
   uint32_t* s_tie = s_aux;
 
   __shared__ uint2 s_hdr[kScanMaxChunks];  // per chunk: dmin | localk << 16, complete | n << 16
-  __shared__ uint32_t s_lt[kScanMaxChunks], s_m[kScanMaxChunks + 1];
-  __shared__ uint32_t s_G[kBins];
-  __shared__ uint32_t s_wsum[kSAWaves], s_wneed[kSAWaves];
+  __shared__ uint4 s_cinfo[kScanMaxChunks];  // per chunk: m, lt, first kept rank, ties before it
+  __shared__ uint32_t s_H[kBins];  // per distance: positions at that distance, over chunks (up to localk)
+  __shared__ uint32_t s_wsum[2 * kSAWaves], s_wmax[kSAWaves];
+  __shared__ int s_T;
+  __shared__ uint32_t s_quota;
   __shared__ float s_S[kSATile];
   __shared__ float s_mx, s_l, s_corr;
   __shared__ float s_red[kSAWaves][kHeadDim];
   __shared__ int s_last;
 
   // ---- A. loads: kv_len, the query fragment, the first rec_win words of every
-  // chunk record; the headers also go to s_hdr.
+  // chunk record (headers also to s_hdr) and the first pre_slots sorted slots
+  // of every chunk.
   const int len = a.kv_len[b];
   const int col = lane & 15;
   const int kg = lane >> 4;
@@ -388,188 +486,227 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
       qf[s] = col == 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * kg) : make_uint4(0, 0, 0, 0);
   }
   const uint16_t* grec = a.rec + (size_t)bh * a.nch * kRecStride;
+  const uint16_t* gsorted = a.sorted + (size_t)bh * a.nch * a.chunk;
   const int k_eff = min(a.budget, len);
-  const int nch_b = (len + a.chunk - 1) / a.chunk;
+  const int nch_b = (len + a.chunk - 1) >> __builtin_ctz(a.chunk);  // chunk is a power of two
   {
-    const int per = a.rec_win / 8;  // 16-byte words per chunk record window
-    const int n16 = a.nch * per;
+    // 16-byte words per chunk: record window and sorted prefix (powers of two)
+    const int per_log2 = __builtin_ctz(a.rec_win) - 3, pper_log2 = __builtin_ctz(a.pre_slots) - 3;
+    const int per = 1 << per_log2, pper = 1 << pper_log2;
+    const int n16 = a.nch << per_log2;
+    const int p16 = a.nch << pper_log2;
+    auto pre_src = [&](int i) {
+      const int cc = i >> pper_log2, j = i & (pper - 1);
+      return reinterpret_cast<const uint4*>(gsorted + (size_t)cc * a.chunk + 8 * j);
+    };
+    const uint4 tp = *pre_src(min(tid, p16 - 1));  // first pass of the prefixes, issued with the records
 #pragma unroll 1
     for (int i0 = 0; i0 < n16; i0 += 4 * kSAThreads) {
       uint4 t[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
-        const int cc = i / per, j = i - cc * per;
+        const int cc = i >> per_log2, j = i & (per - 1);
         t[u] = *reinterpret_cast<const uint4*>(grec + (size_t)cc * kRecStride + 8 * j);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
         reinterpret_cast<uint4*>(s_rec)[i] = t[u];
-        const int cc = i / per;
-        if (i - cc * per == 0 && cc < nch_b) s_hdr[cc] = make_uint2(t[u].x, t[u].y);
+        const int cc = i >> per_log2;
+        if ((i & (per - 1)) == 0 && cc < nch_b) s_hdr[cc] = make_uint2(t[u].x, t[u].y);
       }
     }
-  }
-  for (int i = tid; i < a.bitmap_words; i += kSAThreads) s_keep[i] = 0u;
-  __syncthreads();
-
-  // cum'(cc, d): the number of chunk cc's positions at distance <= d, where
-  // d > localk of a chunk that is not complete counts k_eff (that chunk alone
-  // then reaches k_eff; its exact count is not recorded and not needed).
-  auto cum_from = [&](const uint2 hd, uint32_t v, int d) -> uint32_t {
-    const int dm = (int)(hd.x & 0xFFFFu), lk = (int)(hd.x >> 16);
-    const uint32_t over = (hd.y & 0xFFFFu) ? (hd.y >> 16) : (uint32_t)k_eff;
-    return d < dm ? 0u : (d > lk ? over : v);
-  };
-  auto rec_index = [&](const uint2 hd, int d) -> int {
-    const int dm = (int)(hd.x & 0xFFFFu), lk = (int)(hd.x >> 16);
-    return 4 + min(max(d - dm, 0), lk - dm);
-  };
-
-  // ---- B. G'(d) = sum over chunks of cum'(cc, d), one thread per distance d.
-  // G' equals the exact count G below D* (the least localk of the chunks that
-  // are not complete) and is >= k_eff from D* on, so T, the smallest d with
-  // G(d) >= k_eff, is the number of d with G'(d) < k_eff.  The counts come
-  // from the LDS windows; if some chunk's counts run past its window (a wide
-  // spread of distances below localk), the block redoes the sums from the
-  // global records.
-  const int d_me = tid;
-  auto publish_G = [&](uint32_t gsum) {
-    if (d_me < kBins) s_G[d_me] = gsum;
-    const uint64_t below = __ballot(d_me < kBins && gsum < (uint32_t)k_eff);  // whole wave, outside the branch
-    if (lane == 0) s_wsum[wave] = (uint32_t)__builtin_popcountll(below);
-  };
-  {
-    uint32_t gsum = 0;
-    bool need = false;
-#pragma unroll 8
-    for (int cc = 0; cc < nch_b; ++cc) {
-      const uint2 hd = s_hdr[cc];
-      const int idx = rec_index(hd, d_me);
-      need |= idx >= a.rec_win;
-      gsum += cum_from(hd, s_rec[(size_t)cc * a.rec_win + min(idx, a.rec_win - 1)], d_me);
-    }
-    publish_G(gsum);
-    const uint64_t nb = __ballot(need);
-    if (lane == 0) s_wneed[wave] = nb != 0 ? 1u : 0u;
-  }
-  __syncthreads();
-  bool ovf = false;  // block-uniform
-#pragma unroll
-  for (int w = 0; w < kSAWaves; ++w) ovf |= s_wneed[w] != 0;
-  if (ovf) {
-    uint32_t gsum = 0;
-#pragma unroll 8
-    for (int cc = 0; cc < nch_b; ++cc) {
-      const uint2 hd = s_hdr[cc];
-      gsum += cum_from(hd, grec[(size_t)cc * kRecStride + rec_index(hd, d_me)], d_me);
-    }
-    __syncthreads();
-    publish_G(gsum);
-    __syncthreads();
-  }
-  int T = 0;
-#pragma unroll
-  for (int w = 0; w < kSAWaves; ++w) T += (int)s_wsum[w];
-  const uint32_t quota = (uint32_t)k_eff - (T > 0 ? s_G[T - 1] : 0u);
-
-  // ---- E. per chunk: positions below T (slots [0, lt) of its sorted prefix)
-  // and at T (the next eq slots); m = lt + eq entries to read.
-  uint32_t total_m;
-  {
-    uint32_t m = 0;
-    if (tid < nch_b) {
-      const uint2 hd = s_hdr[tid];
-      const int i0 = rec_index(hd, T - 1), i1 = rec_index(hd, T);
-      uint32_t v0 = s_rec[(size_t)tid * a.rec_win + min(i0, a.rec_win - 1)];
-      uint32_t v1 = s_rec[(size_t)tid * a.rec_win + min(i1, a.rec_win - 1)];
-      if (ovf) {  // (volatile: kept apart from the LDS reads above, never merged into a generic load)
-        v0 = reinterpret_cast<const volatile uint16_t*>(grec)[(size_t)tid * kRecStride + i0];
-        v1 = reinterpret_cast<const volatile uint16_t*>(grec)[(size_t)tid * kRecStride + i1];
-      }
-      const uint32_t lt = cum_from(hd, v0, T - 1);
-      m = cum_from(hd, v1, T);
-      s_lt[tid] = lt;
-    }
-    const uint32_t before = block_exclusive_scan(m, s_wsum, total_m);
-    if (tid < nch_b) s_m[tid] = before;
-    if (tid == 0) s_m[nch_b] = total_m;
-  }
-  // (the scan's barriers order the record reads above before the tie bitmap
-  // overwrites the record area)
-  for (int i = tid; i < a.bitmap_words; i += kSAThreads) s_tie[i] = 0u;
-  __syncthreads();
-
-  // ---- F. mark the selected positions: below T -> keep bitmap, at T -> tie
-  // bitmap.  Flat index f over all chunks' entries; chunk by binary search.
-  {
-    const uint16_t* gsorted = a.sorted + (size_t)bh * a.nch * a.chunk;
+    reinterpret_cast<uint4*>(s_pre)[min(tid, p16 - 1)] = tp;
 #pragma unroll 1
-    for (int f0 = 0; f0 < (int)total_m; f0 += 4 * kSAThreads) {
-      int pos[4];
-      bool is_lt[4];
-      uint16_t lp[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int f = min(f0 + u * kSAThreads + tid, (int)total_m - 1);
-        int lo = 0, hi = nch_b - 1;  // last chunk cc with s_m[cc] <= f
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if ((int)s_m[mid] <= f) lo = mid;
-          else hi = mid - 1;
-        }
-        const int slot = f - (int)s_m[lo];
-        lp[u] = gsorted[(size_t)lo * a.chunk + slot];
-        pos[u] = lo * a.chunk;
-        is_lt[u] = (uint32_t)slot < s_lt[lo];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (f0 + u * kSAThreads + tid < (int)total_m) {
-          const int pp = pos[u] + lp[u];
-          atomicOr((is_lt[u] ? s_keep : s_tie) + (pp >> 5), 1u << (pp & 31));
-        }
-      }
-    }
+    for (int i = tid + kSAThreads; i < p16; i += kSAThreads) reinterpret_cast<uint4*>(s_pre)[i] = *pre_src(i);
   }
+  if (tid < kBins) s_H[tid] = 0u;
   __syncthreads();
 
-  // ---- G. ties: keep the `quota` lowest positions at T.  H. emit the kept
-  // positions in ascending order; ranks [lo_rank, hi_rank) belong to this split.
-  const int wpt = (a.bitmap_words + kSAThreads - 1) / kSAThreads;  // words per thread
-  const int w0 = tid * wpt;
-  const int w1 = min(w0 + wpt, a.bitmap_words);
-  {
-    uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __builtin_popcount(s_tie[w]);
-    uint32_t tot;
-    uint32_t r = block_exclusive_scan(cnt, s_wsum, tot);
-    if (tot > quota) {
-      for (int w = w0; w < w1 && r < quota; ++w) {
-        uint32_t bits = s_tie[w];
-        while (bits && r < quota) {
-          const uint32_t bit = bits & (0u - bits);
-          bits ^= bit;
-          s_keep[w] |= bit;
-          ++r;
-        }
+  // Record word idx of chunk cc: from the LDS window, else from the global
+  // record (volatile: never merged with the LDS read into one generic load).
+  auto rec_word = [&](int cc, int idx) -> uint32_t {
+    uint32_t v = s_rec[(size_t)cc * a.rec_win + min(idx, a.rec_win - 1)];
+    if (idx >= a.rec_win) v = reinterpret_cast<const volatile uint16_t*>(grec)[(size_t)cc * kRecStride + idx];
+    return v;
+  };
+  // cum(cc, d): positions of chunk cc at distance <= d, for d <= localk of a
+  // chunk that is not complete (complete chunks: any d).
+  auto cum = [&](int cc, int d) -> uint32_t {
+    const uint2 hd = s_hdr[cc];
+    const int dm = (int)(hd.x & 0xFFFFu), lk = (int)(hd.x >> 16);
+    const uint32_t v = rec_word(cc, 4 + min(max(d - dm, 0), lk - dm));
+    return d < dm ? 0u : (d > lk ? (hd.y >> 16) : v);
+  };
+
+  // ---- B. threshold.  H[d] = sum over chunks of the chunk's count at d, for
+  // d <= its localk; G'(d) = H[0] + ... + H[d] is the sum over chunks of
+  // cum(cc, min(d, localk)).  Below D* (the least localk of the chunks that are
+  // not complete) G' is the exact count G; from D* on it is >= k_eff (that
+  // chunk alone has k_eff positions at or below D*).  G' is non-decreasing, so
+  // the threshold T (the smallest d with G(d) >= k_eff) is where G' first
+  // reaches k_eff, and quota = k_eff - G(T-1) ties at T are kept.
+  // Wave w takes chunks w, w+8, ...; lane i of the wave holds the header of
+  // its i-th chunk.  A chunk's distances dmin..localk go one per lane: first
+  // the offsets below 64 for four chunks at a time, then the rest.
+  const int per_wave = (nch_b - wave + kSAWaves - 1) / kSAWaves;  // chunks of this wave (<= 32)
+  const int my_cc = wave + kSAWaves * lane;
+  const uint2 my_hdr = my_cc < nch_b ? s_hdr[my_cc] : make_uint2(0u, 0u);
+  const int my_width = (int)(my_hdr.x >> 16) - (int)(my_hdr.x & 0xFFFFu) + 1;  // localk - dmin + 1
+#pragma unroll 1
+  for (int i0 = 0; i0 < per_wave; i0 += 4) {
+    uint32_t c1[4], c0[4];
+    int dmv[4], wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = min(i0 + u, per_wave - 1);
+      const int cc = wave + kSAWaves * i;
+      const uint32_t hx = (uint32_t)__builtin_amdgcn_readlane((int)my_hdr.x, i);
+      dmv[u] = (int)(hx & 0xFFFFu);
+      wv[u] = i0 + u < per_wave ? (int)(hx >> 16) - dmv[u] + 1 : 0;
+      c1[u] = s_rec[(size_t)cc * a.rec_win + min(4 + lane, a.rec_win - 1)];
+      c0[u] = s_rec[(size_t)cc * a.rec_win + min(3 + lane, a.rec_win - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (lane < wv[u] && 4 + lane < a.rec_win) {
+        const uint32_t d1 = c1[u] - (lane > 0 ? c0[u] : 0u);
+        if (d1) atomicAdd(&s_H[dmv[u] + lane], d1);
       }
-    } else {
-      for (int w = w0; w < w1; ++w) s_keep[w] |= s_tie[w];
+    }
+  }
+  {
+    // offsets the pass above did not cover: 64 and up, or past the LDS window
+    const int cover = min(64, a.rec_win - 4);
+    uint64_t rest = __ballot(my_cc < nch_b && my_width > cover);
+    while (rest) {
+      const int i = __builtin_ctzll(rest);
+      rest &= rest - 1;
+      const int cc = wave + kSAWaves * i;
+      const uint32_t hx = (uint32_t)__builtin_amdgcn_readlane((int)my_hdr.x, i);
+      const int dm = (int)(hx & 0xFFFFu), w = (int)(hx >> 16) - dm + 1;
+#pragma unroll 1
+      for (int j = cover + lane; j < w; j += 64) {
+        const uint32_t c1 = rec_word(cc, 4 + j), c0 = rec_word(cc, 3 + j);
+        if (c1 != c0) atomicAdd(&s_H[dm + j], c1 - c0);
+      }
     }
   }
   __syncthreads();
+  {
+    const uint32_t hv = tid < kBins ? s_H[tid] : 0u;
+    uint32_t before, total;
+    const uint32_t inc = block_scan(hv, s_wsum, before, total);
+    if (tid < kBins && before < (uint32_t)k_eff && inc >= (uint32_t)k_eff) {
+      s_T = tid;
+      s_quota = (uint32_t)k_eff - before;
+    }
+  }
+  __syncthreads();
+  const int T = s_T;
+  const uint32_t quota = s_quota;
+
+  // ---- E. per chunk: lt = positions below T (slots [0, lt) of its sorted
+  // prefix), m = lt + its positions at T (the next slots).  Ties are kept in
+  // position order, so the chunk's first kept rank is (positions below T in
+  // earlier chunks) + min(ties in earlier chunks, quota).
   const int lo_rank = split * a.rows_per_split;
   const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
+  uint32_t max_m;
   {
-    uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __builtin_popcount(s_keep[w]);
-    uint32_t tot;
-    uint32_t r = block_exclusive_scan(cnt, s_wsum, tot);
-    if (cnt > 0 && (int)r < hi_rank && (int)(r + cnt) > lo_rank) {
+    uint32_t lt = 0, m = 0;
+    if (tid < nch_b) {
+      lt = cum(tid, T - 1);
+      m = cum(tid, T);
+    }
+    const uint32_t wm = (uint32_t)wave_max((float)m);  // exact: m <= 2048
+    if (lane == 0) s_wmax[wave] = wm;
+    uint32_t ltb, tb, lt_tot, tie_tot;
+    block_scan2(lt, m - lt, s_wsum, ltb, tb, lt_tot, tie_tot);  // (its barriers also publish s_wmax)
+    if (tid < nch_b) s_cinfo[tid] = make_uint4(m, lt, ltb + min(tb, quota), tb);
+    max_m = 0;
+#pragma unroll
+    for (int w = 0; w < kSAWaves; ++w) max_m = max(max_m, s_wmax[w]);
+  }
+
+  if (max_m <= 64) {
+    // ---- F. every chunk's m entries in one group of S >= m lanes, sorted by
+    // position (key = 2 * position + [at T]); a tie is kept while its rank
+    // among all ties stays below the quota; ranks by ballot.
+    __syncthreads();
+    const SortedEmit e{s_cinfo, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, quota, lo_rank, hi_rank, s_list,
+                       a.sel_idx ? a.sel_idx + (size_t)bh * a.budget : nullptr};
+    if (max_m <= 1) emit_sorted<1>(e);
+    else if (max_m <= 2) emit_sorted<2>(e);
+    else if (max_m <= 4) emit_sorted<4>(e);
+    else if (max_m <= 8) emit_sorted<8>(e);
+    else if (max_m <= 16) emit_sorted<16>(e);
+    else if (max_m <= 32) emit_sorted<32>(e);
+    else emit_sorted<64>(e);
+  } else {
+    // ---- F (wide chunks). Mark the selected positions in bitmaps with one
+    // bit per position: below T -> keep, at T -> tie.  Wave w takes chunks w,
+    // w+8, ...; a chunk's m entries go one per lane.
+    // (the scan's barriers above ordered the record reads before the tie
+    // bitmap overwrites the record area)
+    for (int i = tid; i < a.bitmap_words; i += kSAThreads) {
+      s_keep[i] = 0u;
+      s_tie[i] = 0u;
+    }
+    __syncthreads();
+    {
+      int my_m = 0, my_lt = 0;
+      if (my_cc < nch_b) {
+        const uint4 ci = s_cinfo[my_cc];
+        my_m = (int)ci.x;
+        my_lt = (int)ci.y;
+      }
+      const uint64_t todo = __ballot(my_cc < nch_b && my_m > 0);
+      uint64_t rest = todo;
+      while (rest) {
+        const int i = __builtin_ctzll(rest);
+        rest &= rest - 1;
+        const int cc = wave + kSAWaves * i;
+        const int m = __builtin_amdgcn_readlane(my_m, i), lt = __builtin_amdgcn_readlane(my_lt, i);
+#pragma unroll 1
+        for (int jj = lane; jj < m; jj += 64) {
+          uint32_t lp = s_pre[(size_t)cc * a.pre_slots + min(jj, a.pre_slots - 1)];
+          if (jj >= a.pre_slots) lp = reinterpret_cast<const volatile uint16_t*>(gsorted)[(size_t)cc * a.chunk + jj];
+          const int pp = cc * a.chunk + (int)lp;
+          atomicOr((jj < lt ? s_keep : s_tie) + (pp >> 5), 1u << (pp & 31));
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- G/H. keep every position below T and the `quota` lowest positions
+    // at T, and emit the kept positions in ascending order: each thread owns
+    // contiguous bitmap words; one scan of (kept-below, ties) counts gives each
+    // thread its first rank and its share of the quota.
+    const int wpt = (a.bitmap_words + kSAThreads - 1) / kSAThreads;  // words per thread
+    const int w0 = tid * wpt;
+    const int w1 = min(w0 + wpt, a.bitmap_words);
+    uint32_t nk = 0, nt = 0;
+    for (int w = w0; w < w1; ++w) {
+      nk += __builtin_popcount(s_keep[w]);
+      nt += __builtin_popcount(s_tie[w]);
+    }
+    uint32_t kb, tb, ktot, ttot;
+    block_scan2(nk, nt, s_wsum, kb, tb, ktot, ttot);
+    uint32_t tie_left = tb >= quota ? 0u : min(nt, quota - tb);  // this thread's kept ties
+    uint32_t r = kb + min(tb, quota);
+    if ((int)r < hi_rank && (int)(r + nk + tie_left) > lo_rank) {
       for (int w = w0; w < w1; ++w) {
-        uint32_t bits = s_keep[w];
+        uint32_t tw = s_tie[w];
+        uint32_t ties_kept = 0;
+        while (tw && tie_left) {  // the lowest tie_left ties of this word
+          const uint32_t bit = tw & (0u - tw);
+          tw ^= bit;
+          ties_kept |= bit;
+          --tie_left;
+        }
+        uint32_t bits = s_keep[w] | ties_kept;
         while (bits) {
           const int bit = __builtin_ctz(bits);
           bits &= bits - 1;
@@ -753,7 +890,7 @@ static void launch_k(int i, Kernel kernel, dim3 grid, dim3 block, uint32_t shmem
 
 template <int R>
 static void launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
-  launch_k(0, scan_kernel<R>, dim3(p.nch, p.B * p.Hkv), dim3(kScanThreads), 0, s, sa);
+  launch_k(0, scan_kernel<R>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), 0, s, sa);
 }
 
 hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* codes,
@@ -782,7 +919,7 @@ hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, co
   }
   SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
                 scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch, p.rec_win,
-                p.splits, p.rows_per_split, p.bitmap_words};
+                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words};
   if (p.lds_select > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_attend_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_select);

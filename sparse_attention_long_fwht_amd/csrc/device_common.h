@@ -167,6 +167,55 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v) {
   return v;
 }
 
+// The value held by lane (lane ^ X), X = 1, 2, 3, 4, 7, 8, 15, 16, 31 or 63:
+// DPP where a row permute does it, else a swizzle or a permute through LDS.
+constexpr int kQuadMirror = 0x1B;   // quad_perm [3,2,1,0] = xor 3
+constexpr int kDppRowRor8 = 0x128;  // rotate by 8 inside a 16-lane row = xor 8
+template <int X>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+  if constexpr (X == 1) return dpp_u<kQuadXor1>(v);
+  else if constexpr (X == 2) return dpp_u<kQuadXor2>(v);
+  else if constexpr (X == 3) return dpp_u<kQuadMirror>(v);
+  else if constexpr (X == 7) return dpp_u<kDppRowHalfMirror>(v);
+  else if constexpr (X == 8) return dpp_u<kDppRowRor8>(v);
+  else if constexpr (X == 15) return dpp_u<kDppRowMirror>(v);
+  else if constexpr (X < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (X << 10));
+  else return (uint32_t)__shfl_xor((int)v, X, 64);
+}
+
+// One compare-exchange step: the lower lane of each pair keeps the minimum.
+template <int X>
+__device__ __forceinline__ uint32_t cmp_xchg(uint32_t key, int lane, int low_bit) {
+  const uint32_t other = lane_xor_u32<X>(key);
+  return (lane & low_bit) == 0 ? min(key, other) : max(key, other);
+}
+
+// Ascending sort of one key per lane inside every aligned group of S lanes (S a
+// power of two, 1..64): bitonic sort in the form where stage k first compares
+// lane i with its mirror i ^ (k-1) inside the k-block, then half-cleans with
+// i ^ j for j = k/4, ..., 1, every comparison ascending.  All lanes active.
+template <int K>
+__device__ __forceinline__ uint32_t sort_stage(uint32_t key, int lane) {
+  key = cmp_xchg<K - 1>(key, lane, K >> 1);
+  if constexpr (K >= 64) key = cmp_xchg<16>(key, lane, 16);
+  if constexpr (K >= 32) key = cmp_xchg<8>(key, lane, 8);
+  if constexpr (K >= 16) key = cmp_xchg<4>(key, lane, 4);
+  if constexpr (K >= 8) key = cmp_xchg<2>(key, lane, 2);
+  if constexpr (K >= 4) key = cmp_xchg<1>(key, lane, 1);
+  return key;
+}
+template <int S>
+__device__ __forceinline__ uint32_t group_sort_u32(uint32_t key) {
+  const int lane = (int)(threadIdx.x & 63);
+  if constexpr (S >= 2) key = sort_stage<2>(key, lane);
+  if constexpr (S >= 4) key = sort_stage<4>(key, lane);
+  if constexpr (S >= 8) key = sort_stage<8>(key, lane);
+  if constexpr (S >= 16) key = sort_stage<16>(key, lane);
+  if constexpr (S >= 32) key = sort_stage<32>(key, lane);
+  if constexpr (S >= 64) key = sort_stage<64>(key, lane);
+  return key;
+}
+
 // ---- coherent global accesses between blocks of one kernel.  A store at agent
 // scope writes through the XCD's L2 and an agent-scope load bypasses it, so a
 // block can publish results to a later block on another XCD without flushing
@@ -198,7 +247,9 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(uint4 a, uint4 b, f32x4_t 
                                                  c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// (readfirstlane: tells the compiler the value is the same in every lane of
+// the wave, so loops and branches on it stay scalar)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Number of set bits of `mask` in lanes below this lane.

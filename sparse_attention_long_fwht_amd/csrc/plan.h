@@ -19,16 +19,21 @@ constexpr int kRecStride = 392;      // u16 per (head, chunk) record: 4 header w
 // Dense baseline: chunks of the split-K attention.
 constexpr int kMaxChunks = 128;      // dense chunks per (b, kv head)
 constexpr int kPartFloats = 132;     // m, l, 2 pad, o[128]
+// Dynamic LDS the select/attend kernel may take (160 KB per block, less what
+// its static arrays need).
+constexpr size_t kSelectDynLdsMax = 144 * 1024;
 
 struct Plan {
   int B, Hq, Hkv, R, cap, budget;
   int chunk;           // positions per chunk (power of two)
   int nch;             // chunks covering cap
   int rec_win;         // record words per chunk read in one go by the select/attend kernel
+  int pre_slots;       // leading sorted slots per chunk the select/attend kernel keeps in LDS
   int splits;          // blocks per query head in the select/attend kernel
   int rows_per_split;  // selected rows each of those blocks attends over
   int bitmap_words;    // ceil(cap / 32)
   size_t lds_select;   // dynamic LDS of the select/attend kernel
+  bool supported;      // false: the select/attend kernel's LDS would not fit this shape and budget
   size_t off_sorted, off_rec, off_part, off_count, total;
 };
 
@@ -51,6 +56,7 @@ inline int choose_rows_per_split(int budget) {
 
 inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   Plan p{};
+  p.supported = true;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
@@ -73,13 +79,22 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   p.chunk = choose_chunk(cap, kScanMinChunk, kScanMaxChunks);
   p.nch = (cap + p.chunk - 1) / p.chunk;
   p.rec_win = p.nch <= 64 ? 256 : 64;
+  // about twice the mean number of selected positions per chunk: a power of
+  // two, 16..64 (halved below, down to 8, when LDS is short)
+  p.pre_slots = 16;
+  while (p.pre_slots < 64 && p.pre_slots < 2 * budget / p.nch) p.pre_slots <<= 1;
   p.rows_per_split = choose_rows_per_split(budget);
   p.splits = (budget + p.rows_per_split - 1) / p.rows_per_split;
   p.bitmap_words = ((cap + 31) / 32 + 3) / 4 * 4;  // keeps the record area 16-byte aligned
   const size_t rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);
   const size_t tie_bytes = (size_t)p.bitmap_words * sizeof(uint32_t);
-  p.lds_select = (size_t)p.rows_per_split * sizeof(int) + (size_t)p.bitmap_words * sizeof(uint32_t) +
-                 (rec_bytes > tie_bytes ? rec_bytes : tie_bytes);
+  auto lds_for = [&](int pre) {
+    return (size_t)p.rows_per_split * sizeof(int) + (size_t)p.bitmap_words * sizeof(uint32_t) +
+           (size_t)p.nch * pre * sizeof(uint16_t) + (rec_bytes > tie_bytes ? rec_bytes : tie_bytes);
+  };
+  while (p.pre_slots > 8 && lds_for(p.pre_slots) > kSelectDynLdsMax) p.pre_slots >>= 1;
+  p.lds_select = lds_for(p.pre_slots);
+  if (p.lds_select > kSelectDynLdsMax) p.supported = false;
   p.off_sorted = off;
   off = align256(off + bhq * (size_t)p.nch * p.chunk * sizeof(uint16_t));
   p.off_rec = off;

@@ -60,6 +60,10 @@ def test_workspace_sizes(A):
     assert A.decode_workspace_size(1, 32, 8, 32768, 8, head_dim=64) == 0
     assert A.decode_workspace_size(1, 48, 8, 32768, 8) == 0  # group of 6 is not supported
     assert A.decode_workspace_size(1, 32, 8, (1 << 20) + 1, 8) == 0
+    # the largest capacity takes budgets up to what one block's on-chip selection state holds
+    assert A.decode_workspace_size(1, 32, 8, 1 << 19, 1024) > 0
+    assert A.decode_workspace_size(1, 32, 8, 1 << 19, 65536) > 0
+    assert A.decode_workspace_size(1, 32, 8, 1 << 19, 1 << 19) == 0
 
 
 FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
@@ -89,6 +93,7 @@ def test_decode_rejects_invalid_arguments(A):
     assert call_decode(A, A.dims(1, 32, 8, 32768, head_dim=64)) == A.ERR_UNSUPPORTED
     assert call_decode(A, A.dims(1, 24, 2, 32768)) == A.ERR_UNSUPPORTED  # group of 12
     assert call_decode(A, A.dims(1, 32, 8, (1 << 20) + 1)) == A.ERR_UNSUPPORTED
+    assert call_decode(A, A.dims(1, 32, 8, 1 << 19), budget=1 << 19) == A.ERR_UNSUPPORTED
     need = A.decode_workspace_size(1, 32, 8, 32768, 8)
     assert call_decode(A, good, ws_bytes=need - 1) == A.ERR_WORKSPACE
     assert call_decode(A, good, ws=None) == A.ERR_WORKSPACE
