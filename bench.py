@@ -57,7 +57,7 @@ def parse():
                          "output of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of PMC_COMMAND")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="no GPU: write the kernel-trace summary under profiles/ from the CSV output of "
-                         "TRACE_COMMAND and the JSON line that run printed")
+                         "TRACE_COMMAND and the JSON line of a plain bench.py run on the same box and sources")
     return ap.parse_args()
 
 
@@ -436,7 +436,8 @@ def summarize_trace(trace_dir, bench_json):
         nm = r["Name"].split("(")[0]
         text.append("%-60s %7s %10.3f %10.3f %10.3f" % (nm[-60:], r["Calls"], float(r["AverageNs"]) / 1e3,
                                                        float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
-    text += ["", "bench.py in the same run (HIP events recorded by each kernel's dispatch):",
+    text += ["", "python3 bench.py without the profiler, same box and sources, just before (HIP events recorded by",
+             "each kernel's own dispatch; under the profiler those events read high, so they are not used):",
              "kernel_us: " + json.dumps(res["extra"]["kernel_us"]),
              "step us (graph replay, cold): %s" % res["value"],
              "source sha256[:16]: %s  (%s)" % (source_hash("select_attend"),
