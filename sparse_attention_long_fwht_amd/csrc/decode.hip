@@ -167,7 +167,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 
   __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins 385.. stay 0)
   __shared__ uint32_t s_code[R + 1][8];      // query codes, then the appended key's
-  __shared__ uint32_t s_limit[R];
+  __shared__ uint32_t s_limit[R];                    // sorted slots kept per head
+  __shared__ uint32_t s_recw[R];                     // 16-byte words of each head's record
+  __shared__ __attribute__((aligned(16))) uint16_t s_rec[R][kRecStride];  // records, staged
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_sorted[];       // [R][chunk] sorted slots, staged
   for (int i = tid; i < R * kHistBins; i += kScanThreads) (&s_hist[0][0])[i] = 0u;
   // Vectors to encode: the group's R queries, plus -- in the block holding
   // position len-1 when appending -- that key.  Wave w takes vectors w, w+8.
@@ -212,16 +215,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       qt[r][8 + w] = lo & hi;
     }
 
-  // distances; each (key, head) takes the next rank in its distance's bin
+  // distances; each (key, head) takes the next rank in its distance's bin.
+  // The next pass's codes are loaded while this pass computes.
   uint32_t dr[kScanPasses][R];  // (distance << 16) | rank inside the bin
 #pragma unroll
   for (int pass = 0; pass < kScanPasses; ++pass) {
     const int base = p0 + pass * kScanThreads;
     if (base < p1) {
-      if (pass > 0) {
-        p = min(base + tid, p1 - 1);
-        klo = cbase[(size_t)p * 2];
-        khi = cbase[(size_t)p * 2 + 1];
+      uint4 nlo = klo, nhi = khi;
+      if (pass + 1 < kScanPasses && base + kScanThreads < p1) {
+        const int pn = min(base + kScanThreads + tid, p1 - 1);
+        nlo = cbase[(size_t)pn * 2];
+        nhi = cbase[(size_t)pn * 2 + 1];
       }
       p = base + tid;
       if (p < p1) {
@@ -252,6 +257,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
           if (a.dist_out) a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + p] = (uint16_t)d;
         }
       }
+      klo = nlo;
+      khi = nhi;
     }
   }
   __syncthreads();
@@ -294,13 +301,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     const int dmin = __builtin_amdgcn_readlane(dmin_l, lmin);
     const int localk = __builtin_amdgcn_readlane(localk_l, lk);
     const uint32_t limit = (uint32_t)__builtin_amdgcn_readlane((int)limit_l, lk);
-    uint16_t* rec = a.rec + ((size_t)(b * a.Hq + g * R + r) * a.nch + c) * kRecStride;
+    uint16_t* rec = s_rec[r];
     if (lane == 0) {
       rec[0] = (uint16_t)dmin;
       rec[1] = (uint16_t)localk;
       rec[2] = (uint16_t)(kk == n_c ? 1 : 0);
       rec[3] = (uint16_t)n_c;
       s_limit[r] = limit;
+      s_recw[r] = (uint32_t)(4 + localk - dmin + 1 + 7) / 8;
     }
     run = inc - loc;
 #pragma unroll
@@ -312,7 +320,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   }
   __syncthreads();
 
-  // scatter the chunk-local positions of distances <= localk, ordered by distance
+  // scatter the chunk-local positions of distances <= localk, ordered by
+  // distance, into LDS
 #pragma unroll
   for (int pass = 0; pass < kScanPasses; ++pass) {
     const int pp = p0 + pass * kScanThreads + tid;
@@ -321,10 +330,27 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       for (int r = 0; r < R; ++r) {
         const uint32_t d = dr[pass][r] >> 16;
         const uint32_t slot = s_hist[r][d] + (dr[pass][r] & 0xFFFFu);
-        if (slot < s_limit[r])
-          a.sorted[((size_t)(b * a.Hq + g * R + r) * a.nch + c) * a.chunk + slot] = (uint16_t)(pp - p0);
+        if (slot < s_limit[r]) s_sorted[r * a.chunk + slot] = (uint16_t)(pp - p0);
       }
     }
+  }
+  __syncthreads();
+
+  // copy records and sorted prefixes out in 16-byte words (the words past
+  // a head's kept slots carry stale LDS values, which nothing reads)
+  const size_t hc0 = (size_t)(b * a.Hq + g * R) * a.nch + c;  // (head g*R, chunk c)
+  if (wave < R && lane < (int)s_recw[wave]) {
+    const int r = wave;
+    reinterpret_cast<uint4*>(a.rec + (hc0 + (size_t)r * a.nch) * kRecStride)[lane] =
+        reinterpret_cast<const uint4*>(s_rec[r])[lane];
+  }
+  const int wlog = __builtin_ctz(a.chunk) - 3;  // log2(16-byte words per chunk)
+#pragma unroll 1
+  for (int i = tid; i < (R << wlog); i += kScanThreads) {
+    const int r = i >> wlog, w = i & ((1 << wlog) - 1);
+    if (8 * w < (int)s_limit[r])
+      reinterpret_cast<uint4*>(a.sorted + (hc0 + (size_t)r * a.nch) * a.chunk)[w] =
+          reinterpret_cast<const uint4*>(s_sorted + r * a.chunk)[w];
   }
 }
 
@@ -351,27 +377,8 @@ constexpr int kSAThreads = 512;
 constexpr int kSAWaves = kSAThreads / 64;
 constexpr int kSATile = kSAWaves * 16;  // 128 rows per attention tile
 
-// Inclusive prefix sum over the block of one value per thread (every thread
-// calls it).  `before` = exclusive prefix, `total` = block sum.
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* s_wsum, uint32_t& before, uint32_t& total) {
-  const int lane = lane_id(), wave = wave_id();
-  const uint32_t inc = wave_inclusive_scan_u32(v);
-  if (lane == 63) s_wsum[wave] = inc;
-  __syncthreads();
-  uint32_t b = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSAWaves; ++w) {
-    const uint32_t x = s_wsum[w];
-    b += w < wave ? x : 0u;
-    tot += x;
-  }
-  __syncthreads();
-  total = tot;
-  before = b + inc - v;
-  return b + inc;
-}
-
-// The same for two values at once (each block sum below 2^32).
+// Exclusive prefix sums over the block of two values per thread (every thread
+// calls it; each block sum below 2^32), and the block sums.
 __device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t* s_wsum2, uint32_t& before0,
                                             uint32_t& before1, uint32_t& total0, uint32_t& total1) {
   const int lane = lane_id(), wave = wave_id();
@@ -464,11 +471,10 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   __shared__ uint2 s_hdr[kScanMaxChunks];  // per chunk: dmin | localk << 16, complete | n << 16
   __shared__ uint4 s_cinfo[kScanMaxChunks];  // per chunk: m, lt, first kept rank, ties before it
   __shared__ uint32_t s_H[kBins];  // per distance: positions at that distance, over chunks (up to localk)
-  __shared__ uint32_t s_wsum[2 * kSAWaves], s_wmax[kSAWaves];
-  __shared__ int s_T;
-  __shared__ uint32_t s_quota;
-  __shared__ float s_S[kSATile];
-  __shared__ float s_mx, s_l, s_corr;
+  __shared__ uint32_t s_wsum[2 * kSAWaves];
+  __shared__ uint32_t s_quota, s_maxm;
+  __shared__ int s_ok, s_wlim[kSAWaves];
+  __shared__ float s_wm[kSAWaves], s_wl[kSAWaves];  // per wave: running max and sum
   __shared__ float s_red[kSAWaves][kHeadDim];
   __shared__ int s_last;
 
@@ -548,8 +554,10 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // the threshold T (the smallest d with G(d) >= k_eff) is where G' first
   // reaches k_eff, and quota = k_eff - G(T-1) ties at T are kept.
   // Wave w takes chunks w, w+8, ...; lane i of the wave holds the header of
-  // its i-th chunk.  A chunk's distances dmin..localk go one per lane: first
-  // the offsets below 64 for four chunks at a time, then the rest.
+  // its i-th chunk.  A chunk's distances dmin..localk go one per lane, from
+  // the LDS window: offsets below 64 (and inside the window), four chunks at a
+  // time.  The offsets past that are added only if the threshold needs them
+  // (see E): T is usually far below a wide chunk's localk.
   const int per_wave = (nch_b - wave + kSAWaves - 1) / kSAWaves;  // chunks of this wave (<= 32)
   const int my_cc = wave + kSAWaves * lane;
   const uint2 my_hdr = my_cc < nch_b ? s_hdr[my_cc] : make_uint2(0u, 0u);
@@ -576,9 +584,84 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
       }
     }
   }
+  // Counts exact so far: every chunk whose record the pass covered, and the
+  // others up to dmin + cover - 1.
+  const int cover = min(64, a.rec_win - 4);
   {
-    // offsets the pass above did not cover: 64 and up, or past the LDS window
-    const int cover = min(64, a.rec_win - 4);
+    const float lim = (my_cc < nch_b && my_width > cover) ? (float)((int)(my_hdr.x & 0xFFFFu) + cover - 1) : 1e9f;
+    const float wl = -wave_max(-lim);  // (exact small integers)
+    if (lane == 0) s_wlim[wave] = (int)fminf(wl, 1e6f);
+  }
+  __syncthreads();
+
+  // ---- E. one wave: T and the quota from the histogram (7 bins per lane),
+  // then per chunk lt = positions below T (slots [0, lt) of its sorted
+  // prefix) and m = lt + its positions at T (the next slots).  Ties are kept in
+  // position order, so a chunk's first kept rank is (positions below T in
+  // earlier chunks) + min(ties in earlier chunks, quota).  With `check`, the
+  // result stands only if T is within the distances whose counts are exact
+  // (s_ok = 0 otherwise: the block then adds the remaining counts and redoes it).
+  const int lo_rank = split * a.rows_per_split;
+  const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
+  auto threshold_and_chunks = [&](bool check) {
+    uint32_t hb[7], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const int d = 7 * lane + j;
+      hb[j] = d < kBins ? s_H[d] : 0u;
+      loc += hb[j];
+    }
+    const uint32_t inc = wave_inclusive_scan_u32(loc);  // G'(7 lane + 6)
+    const uint64_t reach = __ballot(inc >= (uint32_t)k_eff);
+    const int tl = __builtin_ffsll((long long)reach) - 1;
+    uint32_t run = inc - loc;
+    int T_l = 0;
+    uint32_t before_l = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      if (!found && run + hb[j] >= (uint32_t)k_eff) {
+        found = true;
+        T_l = 7 * lane + j;
+        before_l = run;
+      }
+      run += hb[j];
+    }
+    const int T = __builtin_amdgcn_readlane(T_l, max(tl, 0));
+    const uint32_t quota = (uint32_t)k_eff - (uint32_t)__builtin_amdgcn_readlane((int)before_l, max(tl, 0));
+    int exact_to = 384;
+    if (check) {
+#pragma unroll
+      for (int w = 0; w < kSAWaves; ++w) exact_to = min(exact_to, s_wlim[w]);
+    }
+    const bool ok = reach != 0 && T <= exact_to;
+    if (ok) {
+      uint32_t lt_carry = 0, tie_carry = 0, mmax = 0;
+#pragma unroll 1
+      for (int c0 = 0; c0 < nch_b; c0 += 64) {
+        const int cc = c0 + lane;
+        uint32_t lt = 0, m = 0;
+        if (cc < nch_b) {
+          lt = cum(cc, T - 1);
+          m = cum(cc, T);
+        }
+        const uint32_t lt_inc = wave_inclusive_scan_u32(lt), tie_inc = wave_inclusive_scan_u32(m - lt);
+        const uint32_t ltb = lt_carry + lt_inc - lt, tb = tie_carry + tie_inc - (m - lt);
+        if (cc < nch_b) s_cinfo[cc] = make_uint4(m, lt, ltb + min(tb, quota), tb);
+        lt_carry += (uint32_t)__builtin_amdgcn_readlane((int)lt_inc, 63);
+        tie_carry += (uint32_t)__builtin_amdgcn_readlane((int)tie_inc, 63);
+        mmax = max(mmax, (uint32_t)wave_max((float)m));  // exact: m <= 2048
+      }
+      if (lane == 0) {
+        s_quota = quota;
+        s_maxm = mmax;
+      }
+    }
+    if (lane == 0) s_ok = ok ? 1 : 0;
+  };
+  if (wave == 0) threshold_and_chunks(true);
+  __syncthreads();
+  if (!s_ok) {  // (block-uniform) T lies past some chunk's window: all counts from the global records
     uint64_t rest = __ballot(my_cc < nch_b && my_width > cover);
     while (rest) {
       const int i = __builtin_ctzll(rest);
@@ -592,49 +675,17 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         if (c1 != c0) atomicAdd(&s_H[dm + j], c1 - c0);
       }
     }
+    __syncthreads();
+    if (wave == 0) threshold_and_chunks(false);
+    __syncthreads();
   }
-  __syncthreads();
-  {
-    const uint32_t hv = tid < kBins ? s_H[tid] : 0u;
-    uint32_t before, total;
-    const uint32_t inc = block_scan(hv, s_wsum, before, total);
-    if (tid < kBins && before < (uint32_t)k_eff && inc >= (uint32_t)k_eff) {
-      s_T = tid;
-      s_quota = (uint32_t)k_eff - before;
-    }
-  }
-  __syncthreads();
-  const int T = s_T;
   const uint32_t quota = s_quota;
-
-  // ---- E. per chunk: lt = positions below T (slots [0, lt) of its sorted
-  // prefix), m = lt + its positions at T (the next slots).  Ties are kept in
-  // position order, so the chunk's first kept rank is (positions below T in
-  // earlier chunks) + min(ties in earlier chunks, quota).
-  const int lo_rank = split * a.rows_per_split;
-  const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
-  uint32_t max_m;
-  {
-    uint32_t lt = 0, m = 0;
-    if (tid < nch_b) {
-      lt = cum(tid, T - 1);
-      m = cum(tid, T);
-    }
-    const uint32_t wm = (uint32_t)wave_max((float)m);  // exact: m <= 2048
-    if (lane == 0) s_wmax[wave] = wm;
-    uint32_t ltb, tb, lt_tot, tie_tot;
-    block_scan2(lt, m - lt, s_wsum, ltb, tb, lt_tot, tie_tot);  // (its barriers also publish s_wmax)
-    if (tid < nch_b) s_cinfo[tid] = make_uint4(m, lt, ltb + min(tb, quota), tb);
-    max_m = 0;
-#pragma unroll
-    for (int w = 0; w < kSAWaves; ++w) max_m = max(max_m, s_wmax[w]);
-  }
+  const uint32_t max_m = s_maxm;
 
   if (max_m <= 64) {
     // ---- F. every chunk's m entries in one group of S >= m lanes, sorted by
     // position (key = 2 * position + [at T]); a tie is kept while its rank
     // among all ties stays below the quota; ranks by ballot.
-    __syncthreads();
     const SortedEmit e{s_cinfo, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, quota, lo_rank, hi_rank, s_list,
                        a.sel_idx ? a.sel_idx + (size_t)bh * a.budget : nullptr};
     if (max_m <= 1) emit_sorted<1>(e);
@@ -724,16 +775,16 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     for (int i = k_eff + tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
   }
   const int nrows = max(0, hi_rank - lo_rank);
-  if (tid == 0) {
-    s_mx = -INFINITY;
-    s_l = 0.f;
-  }
   __syncthreads();
 
-  // ---- I. attention over the split's rows: tiles of 128 rows (16 per wave).
+  // ---- I. attention over the split's rows: tiles of 128 rows, 16 per wave.
+  // Each wave keeps its own running max, sum and output over its rows.
+  // Scores: q (A operand, row 0) times the rows (B operand) puts row j's score
+  // in lane j.
   float o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.f;
+  float m_w = -INFINITY, l_w = 0.f;
   const uint16_t* Kg = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
   const uint16_t* Vg = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
 #pragma unroll 1
@@ -754,48 +805,30 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_16x16x32_bf16(ka[s], qf[s], acc);
-    if (col == 0) {
+    for (int s = 0; s < 4; ++s) acc = mfma_16x16x32_bf16(qf[s], ka[s], acc);
+    const float sj = (lane < 16 && t0 + 16 * wave + lane < nrows) ? acc[0] * a.qscale : -INFINITY;
+    const float m_new = fmaxf(m_w, wave_max(sj));
+    if (m_new != -INFINITY) {  // (wave-uniform) the wave has rows
+      const float corr = exp2f(m_w - m_new);  // 0 while m_w is -inf
+      const float pj = sj == -INFINITY ? 0.f : exp2f(sj - m_new);
+      l_w = __builtin_fmaf(l_w, corr, wave_sum(pj));
+      m_w = m_new;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] *= corr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * wave + 4 * kg + i;
-        s_S[rr] = t0 + rr < nrows ? acc[i] * a.qscale : -INFINITY;
+        const float pr = __shfl(pj, 4 * i + kg, 64);  // row 4i + kg of the wave's 16
+        const uint32_t vw[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = __builtin_fmaf(pr, bf16_lo(vw[j]), o[2 * j]);
+          o[2 * j + 1] = __builtin_fmaf(pr, bf16_hi(vw[j]), o[2 * j + 1]);
+        }
       }
     }
-    __syncthreads();
-    if (wave == 0) {
-      const float x0 = s_S[lane], x1 = s_S[lane + 64];
-      const float mo = s_mx;
-      const float mn = fmaxf(mo, wave_max(fmaxf(x0, x1)));  // finite: the tile has >= 1 row
-      const float cr = exp2f(mo - mn);
-      const float p0 = x0 == -INFINITY ? 0.f : exp2f(x0 - mn);
-      const float p1 = x1 == -INFINITY ? 0.f : exp2f(x1 - mn);
-      s_S[lane] = p0;
-      s_S[lane + 64] = p1;
-      const float ts = wave_sum(p0 + p1);
-      if (lane == 0) {
-        s_corr = cr;
-        s_mx = mn;
-        s_l = __builtin_fmaf(s_l, cr, ts);
-      }
-    }
-    __syncthreads();
-    const float cr = s_corr;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] *= cr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pr = s_S[16 * wave + 4 * i + kg];
-      const uint32_t vw[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[2 * j] = __builtin_fmaf(pr, bf16_lo(vw[j]), o[2 * j]);
-        o[2 * j + 1] = __builtin_fmaf(pr, bf16_hi(vw[j]), o[2 * j + 1]);
-      }
-    }
-    __syncthreads();
   }
-  // reduce o over the four k-groups of each wave, then over the waves
+  // ---- J. merge: o over the four k-groups of each wave, then the waves'
+  // (max, sum, output) partials.
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float v = o[j];
@@ -807,31 +840,37 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll
     for (int j = 0; j < 8; ++j) s_red[wave][8 * col + j] = o[j];
   }
-  __syncthreads();
-
-  if (a.splits == 1) {
-    if (tid < kHeadDim) {
-      float O = 0.f;
-#pragma unroll
-      for (int w = 0; w < kSAWaves; ++w) O += s_red[w][tid];
-      a.out[(size_t)bh * kHeadDim + tid] = O / s_l;
-    }
-    return;
+  if (lane == 0) {
+    s_wm[wave] = m_w;
+    s_wl[wave] = l_w;
   }
-
-  // ---- J. several splits: publish (m, l, o) write-through, count, and let the
-  // last split of this head merge them.
+  __syncthreads();
   float* pc = a.part + ((size_t)bh * a.splits + split) * kPartFloats;
   if (tid < kHeadDim) {
-    float O = 0.f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSAWaves; ++w) O += s_red[w][tid];
-    store_coherent(pc + 4 + tid, O);
-    if (tid == 0) {
-      store_coherent(pc, s_mx);
-      store_coherent(pc + 1, s_l);
+    for (int w = 0; w < kSAWaves; ++w) M = fmaxf(M, s_wm[w]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSAWaves; ++w) {
+      const float mw = s_wm[w];
+      const float wgt = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      L = __builtin_fmaf(s_wl[w], wgt, L);
+      O = __builtin_fmaf(s_red[w][tid], wgt, O);
+    }
+    if (a.splits == 1) {
+      a.out[(size_t)bh * kHeadDim + tid] = O / L;
+    } else {
+      // several splits: publish (m, l, o) write-through; the last split of
+      // this head merges them
+      store_coherent(pc + 4 + tid, O);
+      if (tid == 0) {
+        store_coherent(pc, M);
+        store_coherent(pc + 1, L);
+      }
     }
   }
+  if (a.splits == 1) return;
   wait_memory();
   __syncthreads();
   if (tid == 0) {
@@ -889,8 +928,15 @@ static void launch_k(int i, Kernel kernel, dim3 grid, dim3 block, uint32_t shmem
 }
 
 template <int R>
-static void launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
-  launch_k(0, scan_kernel<R>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), 0, s, sa);
+static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
+  const uint32_t shmem = (uint32_t)(R * p.chunk * sizeof(uint16_t));  // sorted slots, staged
+  if (shmem > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<R>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  launch_k(0, scan_kernel<R>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), shmem, s, sa);
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* codes,
@@ -903,13 +949,14 @@ hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, co
 
   ScanArgs sa{q,       k,     codes,   kv_len, ws_sorted, ws_rec,   dist,          q_codes,
               counters, p.Hq, p.Hkv, p.cap, p.chunk,   p.nch,    p.budget, append ? 1 : 0};
+  hipError_t es = hipErrorInvalidValue;
   switch (p.R) {
-    case 1: launch_scan<1>(p, sa, s); break;
-    case 2: launch_scan<2>(p, sa, s); break;
-    case 4: launch_scan<4>(p, sa, s); break;
-    case 8: launch_scan<8>(p, sa, s); break;
-    default: return hipErrorInvalidValue;
+    case 1: es = launch_scan<1>(p, sa, s); break;
+    case 2: es = launch_scan<2>(p, sa, s); break;
+    case 4: es = launch_scan<4>(p, sa, s); break;
+    case 8: es = launch_scan<8>(p, sa, s); break;
   }
+  if (es != hipSuccess) return es;
   // In timing mode the select/attend kernel waits for the scan on the host, so
   // that its events bracket that kernel alone (not the dispatch gap after the scan).
   const ProfileEvents& pe = profile_events();

@@ -12,9 +12,10 @@ constexpr int kCodeBytes = 32;
 constexpr int kBins = 385;        // distances 0..384 (128 coordinates x largest code gap 3)
 // Sparse path: chunks of the scan (one block per (b, kv head, chunk)).
 constexpr int kScanMinChunk = 512;   // = threads of the scan block: one key per thread per pass
-constexpr int kScanMaxChunk = 2048;  // at most four passes per block
+constexpr int kScanMaxChunk = 4096;  // at most eight passes per block
 constexpr int kScanMaxChunks = 256;  // chunks per (b, kv head)
-constexpr int64_t kMaxCapacity = (int64_t)kScanMaxChunks * kScanMaxChunk;  // 524,288 positions
+constexpr int kScanTargetChunks = 64;  // chunks grow (up to kScanMaxChunk) until a head has at most this many
+constexpr int64_t kMaxCapacity = 524288;  // positions per (b, kv head)
 constexpr int kRecStride = 392;      // u16 per (head, chunk) record: 4 header words + up to 385 bins
 // Dense baseline: chunks of the split-K attention.
 constexpr int kMaxChunks = 128;      // dense chunks per (b, kv head)
@@ -76,9 +77,10 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
     p.total = off;
     return p;
   }
-  p.chunk = choose_chunk(cap, kScanMinChunk, kScanMaxChunks);
+  p.chunk = kScanMinChunk;
+  while (p.chunk < kScanMaxChunk && (int64_t)p.chunk * kScanTargetChunks < cap) p.chunk <<= 1;
   p.nch = (cap + p.chunk - 1) / p.chunk;
-  p.rec_win = p.nch <= 64 ? 256 : 64;
+  p.rec_win = 256;
   // about twice the mean number of selected positions per chunk: a power of
   // two, 16..64 (halved below, down to 8, when LDS is short)
   p.pre_slots = 16;
@@ -86,12 +88,17 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   p.rows_per_split = choose_rows_per_split(budget);
   p.splits = (budget + p.rows_per_split - 1) / p.rows_per_split;
   p.bitmap_words = ((cap + 31) / 32 + 3) / 4 * 4;  // keeps the record area 16-byte aligned
-  const size_t rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);
+  size_t rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);
   const size_t tie_bytes = (size_t)p.bitmap_words * sizeof(uint32_t);
   auto lds_for = [&](int pre) {
     return (size_t)p.rows_per_split * sizeof(int) + (size_t)p.bitmap_words * sizeof(uint32_t) +
            (size_t)p.nch * pre * sizeof(uint16_t) + (rec_bytes > tie_bytes ? rec_bytes : tie_bytes);
   };
+  // record window, then prefix slots, shrink while the LDS is short
+  while (p.rec_win > 64 && lds_for(8) > kSelectDynLdsMax) {
+    p.rec_win >>= 1;
+    rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);
+  }
   while (p.pre_slots > 8 && lds_for(p.pre_slots) > kSelectDynLdsMax) p.pre_slots >>= 1;
   p.lds_select = lds_for(p.pre_slots);
   if (p.lds_select > kSelectDynLdsMax) p.supported = false;

@@ -141,17 +141,21 @@ def test_decode_heavy_ties(env):
     check_decode(DeviceCase(wl, A, torch), oracle)
 
 
+def chunking(cap):
+    """The library's chunk size (512 positions, doubled up to 4096 until a head
+    has at most 64 chunks) and the select kernel's per-chunk LDS record window
+    (256 words at these sizes)."""
+    chunk = 512
+    while chunk < 4096 and chunk * 64 < cap:
+        chunk *= 2
+    return chunk, 256
+
+
 def widest_record(wl, dist, budget):
     """Largest per-chunk record (4 header words + one count per distance from
-    the chunk's smallest distance up to its localk) over all heads, with the
-    library's chunking: 512-position chunks while a head has at most 256 of
-    them; the select kernel keeps the first 256 record words of each chunk in
-    LDS when a head has at most 64 chunks, else the first 64."""
-    chunk = 512
-    while chunk * 256 < wl.cap:
-        chunk *= 2
-    nch = -(-wl.cap // chunk)
-    window = 256 if nch <= 64 else 64
+    the chunk's smallest distance up to its localk) over all heads, and the LDS
+    window it is compared with."""
+    chunk, window = chunking(wl.cap)
     worst = 0
     for b in range(wl.B):
         L = int(wl.kv_len[b])
@@ -165,14 +169,37 @@ def widest_record(wl, dist, budget):
     return worst, window
 
 
+def threshold_past_window(wl, dist, budget):
+    """True if some head's threshold distance T lies past the part of a chunk
+    record the select kernel's first pass covers (its first 64 counts), so
+    that the remaining counts must be added."""
+    chunk, window = chunking(wl.cap)
+    cover = min(64, window - 4)
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        k_eff = min(budget, L)
+        for h in range(wl.Hq):
+            d = dist[b, h, :L].astype(np.int64)
+            T = int(np.sort(d)[k_eff - 1])
+            for c0 in range(0, L, chunk):
+                dc = np.sort(d[c0:c0 + chunk])
+                kk = min(k_eff, len(dc))
+                if dc[kk - 1] - dc[0] + 1 > cover and T > dc[0] + cover - 1:
+                    return True
+    return False
+
+
 def test_decode_record_window_overflow(env):
-    """Chunk records longer than the select kernel's LDS window: the threshold
-    counts then come from the global records.  (a) 79 chunks, so 64-word
-    windows, budget 1024; (b) 4 chunks with 256-word windows, where one query's
-    transform is exactly a +-1 vector (codes 0 and 3 only) and chunk 0 holds
-    keys equal to that query (distance 0) and to its negation (distance 384)."""
+    """Wide chunk records.  (a) 40 chunks of 1024, budget 1024; one key equals
+    query head 0, so its chunk's smallest distance is 0 and the threshold lies
+    past the counts the select kernel's first pass covers: the rest are added.
+    (b) 4 chunks, where one query's transform is exactly a +-1 vector (codes 0
+    and 3 only) and chunk 0 holds keys equal to that query (distance 0) and to
+    its negation (distance 384): that record is longer than the LDS window, so
+    its tail comes from the global record."""
     A, torch, oracle = env
     wa = W.llama(50, cap=40000, budget=1024, B=1, Hq=8, Hkv=2)
+    wa.k[0, 0, 2600] = wa.q[0, 0]
     wb = W.llama(51, cap=2048, budget=520, B=1, Hq=2, Hkv=1)
     H = np.array([[1.0]], np.float32)
     while H.shape[0] < 128:
@@ -185,9 +212,21 @@ def test_decode_record_window_overflow(env):
     for wl in (wa, wb):
         codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
         _, _, dist_r, _ = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, wl.budget, wl.scale, threads=8)
-        worst, window = widest_record(wl, dist_r, wl.budget)
-        assert worst > window, "case does not reach the overflow path (%d <= %d)" % (worst, window)
+        assert threshold_past_window(wl, dist_r, wl.budget), "case does not need the remaining counts"
+        if wl is wb:
+            worst, window = widest_record(wl, dist_r, wl.budget)
+            assert worst > window, "case (b) record fits the LDS window (%d <= %d)" % (worst, window)
         check_decode(DeviceCase(wl, A, torch), oracle)
+
+
+@pytest.mark.parametrize("budget", [300, 2500])
+def test_decode_multipass_chunks_ragged(env, budget):
+    """Chunks of 2048 positions (four passes of the scan block, each loading the
+    next pass's codes while it computes), kv_len ending inside a pass."""
+    A, torch, oracle = env
+    wl = W.llama(52, cap=100000, budget=budget, B=2, Hq=8, Hkv=2, kv_len=np.array([99999, 61234], np.int32))
+    assert chunking(wl.cap)[0] == 2048
+    check_decode(DeviceCase(wl, A, torch), oracle)
 
 
 def test_decode_full_budget_equals_dense(env):
