@@ -14,7 +14,8 @@ constexpr int kBins = 385;        // distances 0..384 (128 coordinates x largest
 constexpr int kScanMinChunk = 512;   // = threads of the scan block: one key per thread per pass
 constexpr int kScanMaxChunk = 4096;  // at most eight passes per block
 constexpr int kScanMaxChunks = 256;  // chunks per (b, kv head)
-constexpr int kScanTargetChunks = 64;  // chunks grow (up to kScanMaxChunk) until a head has at most this many
+constexpr int kScanTargetChunks = 64;  // chunks per head wanted at most (see make_plan)
+constexpr int64_t kScanBlocks = 512;   // scan blocks wanted at most: two per compute unit
 constexpr int64_t kMaxCapacity = 524288;  // positions per (b, kv head)
 constexpr int kRecStride = 392;      // u16 per (head, chunk) record: 4 header words + up to 385 bins
 // Dense baseline: chunks of the split-K attention.
@@ -46,13 +47,19 @@ inline int choose_chunk(int cap, int min_chunk, int max_chunks) {
   return c;
 }
 
-// Rows per select/attend block: one 128-row attention tile for budgets up to
-// 2048 (so a head's selection is spread over up to 16 blocks), growing beyond
-// that so that at most 64 blocks share a head.
-inline int choose_rows_per_split(int budget) {
-  int r = (budget + 63) / 64;
-  r = (r + 127) / 128 * 128;
-  return r < 128 ? 128 : r;
+// Rows per select/attend block (a multiple of the 128-row attention tile).
+// Several blocks share a head while the heads alone leave the GPU's compute
+// units idle (about kSelectBlocks blocks wanted) or a block would attend more
+// than 16 tiles; at most 64 blocks share a head.
+constexpr int kSelectBlocks = 256;
+inline int choose_rows_per_split(int budget, int heads) {
+  int splits = (kSelectBlocks + heads - 1) / heads;
+  const int tiles = (budget + 127) / 128;
+  splits = splits < 1 ? 1 : (splits > tiles ? tiles : splits);
+  splits = splits < (tiles + 15) / 16 ? (tiles + 15) / 16 : splits;
+  splits = splits > 64 ? 64 : splits;
+  int r = (budget + splits - 1) / splits;
+  return (r + 127) / 128 * 128;
 }
 
 inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
@@ -77,15 +84,21 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
     p.total = off;
     return p;
   }
+  // chunks grow (up to kScanMaxChunk) until a head has at most
+  // kScanTargetChunks of them and the scan grid is about kScanBlocks blocks:
+  // larger chunks amortize each block's query encode and record pass
   p.chunk = kScanMinChunk;
-  while (p.chunk < kScanMaxChunk && (int64_t)p.chunk * kScanTargetChunks < cap) p.chunk <<= 1;
+  auto scan_blocks = [&](int ch) { return (int64_t)B * Hkv * ((cap + ch - 1) / ch); };
+  while (p.chunk < kScanMaxChunk &&
+         ((int64_t)p.chunk * kScanTargetChunks < cap || scan_blocks(p.chunk) > kScanBlocks))
+    p.chunk <<= 1;
   p.nch = (cap + p.chunk - 1) / p.chunk;
   p.rec_win = 256;
   // about twice the mean number of selected positions per chunk: a power of
   // two, 16..64 (halved below, down to 8, when LDS is short)
   p.pre_slots = 16;
   while (p.pre_slots < 64 && p.pre_slots < 2 * budget / p.nch) p.pre_slots <<= 1;
-  p.rows_per_split = choose_rows_per_split(budget);
+  p.rows_per_split = choose_rows_per_split(budget, B * Hq);
   p.splits = (budget + p.rows_per_split - 1) / p.rows_per_split;
   p.bitmap_words = ((cap + 31) / 32 + 3) / 4 * 4;  // keeps the record area 16-byte aligned
   size_t rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);

@@ -141,12 +141,13 @@ def test_decode_heavy_ties(env):
     check_decode(DeviceCase(wl, A, torch), oracle)
 
 
-def chunking(cap):
+def chunking(cap, groups=1):
     """The library's chunk size (512 positions, doubled up to 4096 until a head
-    has at most 64 chunks) and the select kernel's per-chunk LDS record window
-    (256 words at these sizes)."""
+    has at most 64 chunks and the scan has at most 512 blocks, one per (b, kv
+    head, chunk)) and the select kernel's per-chunk LDS record window (256 words
+    at these sizes)."""
     chunk = 512
-    while chunk < 4096 and chunk * 64 < cap:
+    while chunk < 4096 and (chunk * 64 < cap or groups * -(-cap // chunk) > 512):
         chunk *= 2
     return chunk, 256
 
@@ -155,7 +156,7 @@ def widest_record(wl, dist, budget):
     """Largest per-chunk record (4 header words + one count per distance from
     the chunk's smallest distance up to its localk) over all heads, and the LDS
     window it is compared with."""
-    chunk, window = chunking(wl.cap)
+    chunk, window = chunking(wl.cap, wl.B * wl.Hkv)
     worst = 0
     for b in range(wl.B):
         L = int(wl.kv_len[b])
@@ -173,7 +174,7 @@ def threshold_past_window(wl, dist, budget):
     """True if some head's threshold distance T lies past the part of a chunk
     record the select kernel's first pass covers (its first 64 counts), so
     that the remaining counts must be added."""
-    chunk, window = chunking(wl.cap)
+    chunk, window = chunking(wl.cap, wl.B * wl.Hkv)
     cover = min(64, window - 4)
     for b in range(wl.B):
         L = int(wl.kv_len[b])
@@ -225,7 +226,7 @@ def test_decode_multipass_chunks_ragged(env, budget):
     next pass's codes while it computes), kv_len ending inside a pass."""
     A, torch, oracle = env
     wl = W.llama(52, cap=100000, budget=budget, B=2, Hq=8, Hkv=2, kv_len=np.array([99999, 61234], np.int32))
-    assert chunking(wl.cap)[0] == 2048
+    assert chunking(wl.cap, wl.B * wl.Hkv)[0] == 2048
     check_decode(DeviceCase(wl, A, torch), oracle)
 
 
@@ -325,7 +326,8 @@ def test_decode_llama32k(env, budget):
 
 
 def test_decode_batched16(env):
-    """16 sequences with ragged lengths in [16K, 32K], budget 256."""
+    """16 sequences with ragged lengths in [16K, 32K], budget 256 (chunks of
+    4096 positions: eight passes per scan block; one 256-row block per head)."""
     A, torch, oracle = env
     wl = W.batched(0)
     err = check_decode(DeviceCase(wl, A, torch), oracle, threads=16)
