@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline: step latency over contexts 4K..128K x budgets 64..1024 on the "
+                         "32/8-head layer (one JSON line per context), with the dense baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB, three times (the reference "
                          "kernel that scales the HBM byte counters of a rocprofv3 --pmc run)")
@@ -107,6 +110,8 @@ def main():
     dev = torch.device("cuda", 0)
     hip = Hip()
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    if args.sweep:
+        return sweep(A, W, np, torch, dev, log)
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
@@ -279,6 +284,14 @@ def main():
         extra["prefill_encode_us"] = round(ms_enc * 1e3, 3)
         extra["prefill_encode_GBps"] = round(enc_bytes / (ms_enc * 1e-3) / 1e9, 1)
         log("[bench] prefill key encode: %.2f us (%.0f GB/s)" % (ms_enc * 1e3, extra["prefill_encode_GBps"]))
+        del copies, g_cold, g_warm, g_dense, g_enc
+        torch.cuda.empty_cache()
+        # the batched and long-context workloads
+        for name, wl_x, ncopy in (("batched16_ragged16k-32k_b256", W.batched(args.seed), 3),
+                                  ("long512k_b1024", W.llama(args.seed, cap=524288, budget=1024, name="long512k"), 2)):
+            extra[name] = other_workload(A, np, torch, dev, wl_x, ncopy)
+            log("[bench] %s: %s" % (name, extra[name]))
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
@@ -447,6 +460,78 @@ def summarize_trace(trace_dir, bench_json):
     with open(path, "w") as fh:
         fh.write("\n".join(text) + "\n")
     print(path)
+
+
+def timed_graph_steps(torch, fn, cases, reps):
+    """Mean microseconds per call of fn(case), from a HIP graph holding one call
+    per case (rotating copies), replayed `reps` times after one untimed replay."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in cases:
+            fn(c)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for c in cases:
+            fn(c)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(cases))
+
+
+def upload(np, torch, dev, a):
+    return torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+
+
+def other_workload(A, np, torch, dev, wl, ncopy):
+    """Step latency (append-encode + decode, rotating `ncopy` copies of q, K, V
+    and codes) and the dense baseline on one workload."""
+    kv_len = upload(np, torch, dev, wl.kv_len)
+    q, k, v = upload(np, torch, dev, wl.q), upload(np, torch, dev, wl.k), upload(np, torch, dev, wl.v)
+    codes = torch.zeros((wl.B, wl.Hkv, wl.cap, 32), dtype=torch.uint8, device=dev)
+    A.encode_keys(k, kv_len, codes)
+    cases = [(q, k, v, codes)] + [tuple(t.clone() for t in (q, k, v, codes)) for _ in range(ncopy - 1)]
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device=dev)
+    ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, wl.budget), dev)
+    wsd = A.alloc_workspace(A.dense_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap), dev)
+    step_us = timed_graph_steps(torch, lambda c: A.decode_step(c[0], c[1], c[2], c[3], kv_len, wl.budget,
+                                                               wl.scale, out, ws, append=True),
+                                cases * max(1, 16 // ncopy), 5)
+    dense_us = timed_graph_steps(torch, lambda c: A.dense_decode_attention(c[0], c[1], c[2], kv_len, wl.scale,
+                                                                           out, wsd), cases, 5)
+    L = int(wl.kv_len.astype(np.int64).sum())
+    code_bytes = L * wl.Hkv * 32
+    gathered_max = wl.B * wl.Hq * wl.budget * 512  # no-dedup upper bound
+    return {"batch": wl.B, "context": wl.cap, "positions": L, "budget": wl.budget, "cache_copies": ncopy,
+            "step_us": round(step_us, 3), "dense_us": round(dense_us, 3),
+            "speedup_vs_dense": round(dense_us / step_us, 3),
+            "dense_GBps": round(L * wl.Hkv * 512 / (dense_us * 1e3), 1),
+            "step_GBps_codes_plus_gather_upper_bound": round((code_bytes + gathered_max) / (step_us * 1e3), 1)}
+
+
+def sweep(A, W, np, torch, dev, log):
+    """Contexts 4K..128K x budgets 64..1024 on the 32/8-head layer: step latency
+    (4 rotating copies) and the dense baseline, one JSON line per context."""
+    for cap in (4096, 8192, 16384, 32768, 65536, 131072):
+        wl = W.llama(0, cap=cap, budget=64)
+        row = {"context": cap, "step_us": {}}
+        for budget in (64, 128, 256, 512, 1024):
+            wl.budget = budget
+            r = other_workload(A, np, torch, dev, wl, 4)
+            row["step_us"][budget] = r["step_us"]
+            row["dense_us"] = r["dense_us"]
+            log("[sweep] context %d budget %d: %.2f us (dense %.2f us)" % (cap, budget, r["step_us"], r["dense_us"]))
+            torch.cuda.empty_cache()
+        print(json.dumps(row), flush=True)
 
 
 def cpu_baseline(wl, budget, seconds, log):

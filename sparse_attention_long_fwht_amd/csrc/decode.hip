@@ -187,7 +187,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     uint32_t lo[4], hi[4];
     encode_wave(xlo, xhi, lo, hi);
     if (lane < 8) {
-      const uint32_t w = lane < 4 ? lo[lane & 3] : hi[lane & 3];
+      uint32_t w = 0;  // word lane & 3 of the low (lanes 0-3) or high plane; constant indices keep lo/hi in registers
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w = (lane & 3) == j ? (lane < 4 ? lo[j] : hi[j]) : w;
       s_code[vi][lane] = w;
       if (vi < R) {
         if (c == 0 && a.q_codes)
