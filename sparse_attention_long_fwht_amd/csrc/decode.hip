@@ -407,13 +407,23 @@ __device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t* 
   total1 = t1;
 }
 
+// A record header as read, clamped so that no content of the workspace can
+// lead the block out of bounds: dmin <= localk <= 384, complete 0 or 1, n at
+// most the chunk's length.
+__device__ __forceinline__ uint2 sanitize_hdr(uint32_t x, uint32_t y, int n_true) {
+  const uint32_t dm = min(x & 0xFFFFu, 384u);
+  const uint32_t lk = min(max(x >> 16, dm), 384u);
+  const uint32_t n = min(y >> 16, (uint32_t)n_true);
+  return make_uint2(dm | (lk << 16), ((y & 0xFFFFu) ? 1u : 0u) | (n << 16));
+}
+
 // Selection with every chunk's entries in one group of S >= m lanes (see
 // select_attend_kernel, step F).
 struct SortedEmit {
   const uint4* cinfo;      // per chunk: m, lt, first kept rank, ties before it
   const uint16_t* pre;     // LDS sorted prefixes [nch][pre_slots]
   const uint16_t* gsorted; // the head's sorted slots in the workspace
-  int pre_slots, chunk, nch_b;
+  int pre_slots, chunk, nch_b, len;
   uint32_t quota;
   int lo_rank, hi_rank;
   int* list;               // LDS rows of this split
@@ -434,6 +444,7 @@ __device__ __forceinline__ void emit_sorted(const SortedEmit& e) {
     if (j < (int)ci.x) {
       uint32_t lp = e.pre[(size_t)cc * e.pre_slots + min(j, e.pre_slots - 1)];
       if (j >= e.pre_slots) lp = reinterpret_cast<const volatile uint16_t*>(e.gsorted)[(size_t)cc * e.chunk + j];
+      lp = min(lp, (uint32_t)(min(e.chunk, e.len - cc * e.chunk) - 1));  // (a position of the chunk)
       key = ((uint32_t)(cc * e.chunk + (int)lp) << 1) | (j >= (int)ci.y ? 1u : 0u);
     }
     key = group_sort_u32<S>(key);
@@ -522,7 +533,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
         reinterpret_cast<uint4*>(s_rec)[i] = t[u];
         const int cc = i >> per_log2;
-        if ((i & (per - 1)) == 0 && cc < nch_b) s_hdr[cc] = make_uint2(t[u].x, t[u].y);
+        if ((i & (per - 1)) == 0 && cc < nch_b) s_hdr[cc] = sanitize_hdr(t[u].x, t[u].y, min(a.chunk, len - cc * a.chunk));
       }
     }
     reinterpret_cast<uint4*>(s_pre)[min(tid, p16 - 1)] = tp;
@@ -644,8 +655,8 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         const int cc = c0 + lane;
         uint32_t lt = 0, m = 0;
         if (cc < nch_b) {
-          lt = cum(cc, T - 1);
-          m = cum(cc, T);
+          m = min(cum(cc, T), s_hdr[cc].y >> 16);  // (clamps keep garbage in bounds)
+          lt = min(cum(cc, T - 1), m);
         }
         const uint32_t lt_inc = wave_inclusive_scan_u32(lt), tie_inc = wave_inclusive_scan_u32(m - lt);
         const uint32_t ltb = lt_carry + lt_inc - lt, tb = tie_carry + tie_inc - (m - lt);
@@ -688,7 +699,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     // ---- F. every chunk's m entries in one group of S >= m lanes, sorted by
     // position (key = 2 * position + [at T]); a tie is kept while its rank
     // among all ties stays below the quota; ranks by ballot.
-    const SortedEmit e{s_cinfo, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, quota, lo_rank, hi_rank, s_list,
+    const SortedEmit e{s_cinfo, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, len, quota, lo_rank, hi_rank, s_list,
                        a.sel_idx ? a.sel_idx + (size_t)bh * a.budget : nullptr};
     if (max_m <= 1) emit_sorted<1>(e);
     else if (max_m <= 2) emit_sorted<2>(e);
@@ -726,7 +737,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         for (int jj = lane; jj < m; jj += 64) {
           uint32_t lp = s_pre[(size_t)cc * a.pre_slots + min(jj, a.pre_slots - 1)];
           if (jj >= a.pre_slots) lp = reinterpret_cast<const volatile uint16_t*>(gsorted)[(size_t)cc * a.chunk + jj];
-          const int pp = cc * a.chunk + (int)lp;
+          const int pp = cc * a.chunk + min((int)lp, min(a.chunk, len - cc * a.chunk) - 1);
           atomicOr((jj < lt ? s_keep : s_tie) + (pp >> 5), 1u << (pp & 31));
         }
       }
@@ -794,14 +805,14 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     uint4 ka[4], vv[4];
     {
       const int ia = t0 + 16 * wave + col;
-      const int pa = s_list[ia < nrows ? ia : 0];
+      const int pa = min(max(s_list[ia < nrows ? ia : 0], 0), len - 1);  // (clamped: a position of the cache)
       const uint16_t* kr = Kg + (size_t)pa * kHeadDim + 8 * kg;
 #pragma unroll
       for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int iv = t0 + 16 * wave + 4 * i + kg;
-        const int pv = s_list[iv < nrows ? iv : 0];
+        const int pv = min(max(s_list[iv < nrows ? iv : 0], 0), len - 1);
         vv[i] = *reinterpret_cast<const uint4*>(Vg + (size_t)pv * kHeadDim + 8 * col);
       }
     }
