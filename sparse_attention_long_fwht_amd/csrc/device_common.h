@@ -167,6 +167,18 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v) {
   return v;
 }
 
+// Largest value over the 64 lanes (unsigned): maxima inside each 16-lane row,
+// then row broadcasts carry rows 0-2 into row 3; lane 63 holds the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kQuadXor1>(v));
+  v = max(v, dpp_u<kQuadXor2>(v));
+  v = max(v, dpp_u<kDppRowHalfMirror>(v));
+  v = max(v, dpp_u<kDppRowMirror>(v));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // The value held by lane (lane ^ X), X = 1, 2, 3, 4, 7, 8, 15, 16, 31 or 63:
 // DPP where a row permute does it, else a swizzle or a permute through LDS.
 constexpr int kQuadMirror = 0x1B;   // quad_perm [3,2,1,0] = xor 3

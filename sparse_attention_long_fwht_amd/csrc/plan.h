@@ -13,11 +13,12 @@ constexpr int kBins = 385;        // distances 0..384 (128 coordinates x largest
 // Sparse path: chunks of the scan (one block per (b, kv head, chunk)).
 constexpr int kScanMinChunk = 512;   // = threads of the scan block: one key per thread per pass
 constexpr int kScanMaxChunk = 4096;  // at most eight passes per block
-constexpr int kScanMaxChunks = 256;  // chunks per (b, kv head)
 constexpr int kScanTargetChunks = 64;  // chunks per head wanted at most (see make_plan)
-constexpr int64_t kScanBlocks = 512;   // scan blocks wanted at most: two per compute unit
+constexpr int64_t kScanBlocks = 256;   // scan blocks wanted at most: one per compute unit
 constexpr int64_t kMaxCapacity = 524288;  // positions per (b, kv head)
-constexpr int kRecStride = 392;      // u16 per (head, chunk) record: 4 header words + up to 385 bins
+constexpr int kSelMaxChunks = 128;  // chunks per (b, kv head) at most: kMaxCapacity / kScanMaxChunk
+constexpr int kRecHead = 5;          // record words before cum(dmin): dmin, localk, complete, n, zero
+constexpr int kRecStride = 392;      // u16 per (head, chunk) record: kRecHead + up to 385 counts, padded
 // Dense baseline: chunks of the split-K attention.
 constexpr int kMaxChunks = 128;      // dense chunks per (b, kv head)
 constexpr int kPartFloats = 132;     // m, l, 2 pad, o[128]
@@ -93,6 +94,7 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
          ((int64_t)p.chunk * kScanTargetChunks < cap || scan_blocks(p.chunk) > kScanBlocks))
     p.chunk <<= 1;
   p.nch = (cap + p.chunk - 1) / p.chunk;
+  if (p.nch > kSelMaxChunks) p.supported = false;  // (not reached for cap <= kMaxCapacity)
   p.rec_win = 256;
   // about twice the mean number of selected positions per chunk: a power of
   // two, 16..64 (halved below, down to 8, when LDS is short)

@@ -143,63 +143,78 @@ def test_decode_heavy_ties(env):
 
 def chunking(cap, groups=1):
     """The library's chunk size (512 positions, doubled up to 4096 until a head
-    has at most 64 chunks and the scan has at most 512 blocks, one per (b, kv
+    has at most 64 chunks and the scan has at most 256 blocks, one per (b, kv
     head, chunk)) and the select kernel's per-chunk LDS record window (256 words
     at these sizes)."""
     chunk = 512
-    while chunk < 4096 and (chunk * 64 < cap or groups * -(-cap // chunk) > 512):
+    while chunk < 4096 and (chunk * 64 < cap or groups * -(-cap // chunk) > 256):
         chunk *= 2
     return chunk, 256
 
 
+def chunk_records(d, L, chunk, k_eff):
+    """Per chunk of one head: (dmin, localk, complete) as the scan records them."""
+    out = []
+    for c0 in range(0, L, chunk):
+        dc = np.sort(d[c0:c0 + chunk])
+        kk = min(k_eff, len(dc))
+        out.append((int(dc[0]), int(dc[kk - 1]), kk == len(dc)))
+    return out
+
+
 def widest_record(wl, dist, budget):
-    """Largest per-chunk record (4 header words + one count per distance from
-    the chunk's smallest distance up to its localk) over all heads, and the LDS
-    window it is compared with."""
+    """Largest per-chunk record (5 header words -- dmin, localk, complete, n and
+    a zero -- then one count per distance from the chunk's smallest distance up
+    to its localk) over all heads, and the LDS window it is compared with."""
     chunk, window = chunking(wl.cap, wl.B * wl.Hkv)
     worst = 0
     for b in range(wl.B):
         L = int(wl.kv_len[b])
         k_eff = min(budget, L)
         for h in range(wl.Hq):
-            d = dist[b, h, :L].astype(np.int64)
-            for c0 in range(0, L, chunk):
-                dc = np.sort(d[c0:c0 + chunk])
-                kk = min(k_eff, len(dc))
-                worst = max(worst, 4 + int(dc[kk - 1] - dc[0]))
+            for dm, lk, _ in chunk_records(dist[b, h, :L].astype(np.int64), L, chunk, k_eff):
+                worst = max(worst, 5 + lk - dm + 1)
     return worst, window
 
 
-def threshold_past_window(wl, dist, budget):
-    """True if some head's threshold distance T lies past the part of a chunk
-    record the select kernel's first pass covers (its first 64 counts), so
-    that the remaining counts must be added."""
-    chunk, window = chunking(wl.cap, wl.B * wl.Hkv)
-    cover = min(64, window - 4)
+def threshold_search_rounds(wl, dist, budget):
+    """Rounds of the select kernel's threshold search, largest over heads: the
+    candidates start at lo - 1 (lo = the least dmin) and cover 64 distances a
+    round, or 128 while hi = min(least localk of the incomplete chunks, largest
+    localk) lies 64 or more past the round's start."""
+    chunk, _ = chunking(wl.cap, wl.B * wl.Hkv)
+    worst = 0
     for b in range(wl.B):
         L = int(wl.kv_len[b])
         k_eff = min(budget, L)
         for h in range(wl.Hq):
             d = dist[b, h, :L].astype(np.int64)
+            recs = chunk_records(d, L, chunk, k_eff)
+            lo = min(r[0] for r in recs)
+            inc = [r[1] for r in recs if not r[2]]
+            hi = min(min(inc) if inc else 384, max(r[1] for r in recs))
             T = int(np.sort(d)[k_eff - 1])
-            for c0 in range(0, L, chunk):
-                dc = np.sort(d[c0:c0 + chunk])
-                kk = min(k_eff, len(dc))
-                if dc[kk - 1] - dc[0] + 1 > cover and T > dc[0] + cover - 1:
-                    return True
-    return False
+            base, rounds = lo - 1, 0
+            while True:
+                rounds += 1
+                width = 128 if hi - base >= 64 else 64
+                if T < base + width:
+                    break
+                base += width
+            worst = max(worst, rounds)
+    return worst
 
 
 def test_decode_record_window_overflow(env):
-    """Wide chunk records.  (a) 40 chunks of 1024, budget 1024; one key equals
-    query head 0, so its chunk's smallest distance is 0 and the threshold lies
-    past the counts the select kernel's first pass covers: the rest are added.
-    (b) 4 chunks, where one query's transform is exactly a +-1 vector (codes 0
-    and 3 only) and chunk 0 holds keys equal to that query (distance 0) and to
-    its negation (distance 384): that record is longer than the LDS window, so
-    its tail comes from the global record."""
+    """Wide chunk records.  (a) 40 chunks of 1024, budget 38000 (every chunk
+    complete); one key equals query head 0, so the least dmin is 0 and the
+    threshold lies more than one round of candidate distances (128) past it:
+    the search takes a second round.  (b) 4 chunks, where one query's transform is
+    exactly a +-1 vector (codes 0 and 3 only) and chunk 0 holds keys equal to
+    that query (distance 0) and to its negation (distance 384): that record is
+    longer than the LDS window, so its tail comes from the global record."""
     A, torch, oracle = env
-    wa = W.llama(50, cap=40000, budget=1024, B=1, Hq=8, Hkv=2)
+    wa = W.llama(50, cap=40000, budget=38000, B=1, Hq=8, Hkv=2)
     wa.k[0, 0, 2600] = wa.q[0, 0]
     wb = W.llama(51, cap=2048, budget=520, B=1, Hq=2, Hkv=1)
     H = np.array([[1.0]], np.float32)
@@ -213,8 +228,9 @@ def test_decode_record_window_overflow(env):
     for wl in (wa, wb):
         codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
         _, _, dist_r, _ = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, wl.budget, wl.scale, threads=8)
-        assert threshold_past_window(wl, dist_r, wl.budget), "case does not need the remaining counts"
-        if wl is wb:
+        if wl is wa:
+            assert threshold_search_rounds(wl, dist_r, wl.budget) >= 2, "case (a) search takes one round"
+        else:
             worst, window = widest_record(wl, dist_r, wl.budget)
             assert worst > window, "case (b) record fits the LDS window (%d <= %d)" % (worst, window)
         check_decode(DeviceCase(wl, A, torch), oracle)
