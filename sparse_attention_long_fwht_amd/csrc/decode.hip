@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   int p = min(p0 + tid, a.cap - 1);
   uint4 klo = cbase[(size_t)p * 2];
   uint4 khi = cbase[(size_t)p * 2 + 1];
-  const int len = a.kv_len[b];
+  const int len = min(a.kv_len[b], a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
 
   __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins 385.. stay 0)
   __shared__ uint32_t s_code[R + 1][8];      // query codes, then the appended key's
@@ -430,6 +430,7 @@ struct SortedEmit {
   int pre_slots, chunk, nch_b, len;
   uint32_t quota;
   int lo_rank, hi_rank;
+  int c_lo, c_hi;          // the chunks holding ranks of this split (c_lo > c_hi: none)
   int* list;               // LDS rows of this split
   int32_t* sel;            // optional sel_idx row of the head
 };
@@ -441,7 +442,7 @@ __device__ __forceinline__ void emit_sorted(const SortedEmit& e) {
   const int j = lane & (S - 1);
   const uint64_t gmask = S == 64 ? ~0ull : (((1ull << S) - 1ull) << (lane & ~(S - 1)));
 #pragma unroll 1
-  for (int c0 = wave * cpi; c0 < e.nch_b; c0 += kSAWaves * cpi) {
+  for (int c0 = e.c_lo / cpi * cpi + wave * cpi; c0 <= e.c_hi; c0 += kSAWaves * cpi) {
     const int cc = c0 + lane / S;
     // (c0 .. c0 + cpi - 1 lie in one group of 64 chunks: the group is wave-uniform)
     const uint4 src = c0 < 64 ? e.ci[0] : e.ci[1];
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // ---- A. loads: kv_len, the query fragment, the first rec_win words of every
   // chunk record (headers also to s_hdr) and the first pre_slots sorted slots
   // of every chunk.
-  const int len = a.kv_len[b];
+  const int len = min(a.kv_len[b], a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
   const int col = lane & 15;
   const int kg = lane >> 4;
   uint4 qf[4];
@@ -721,12 +722,18 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   const uint16_t* Kg = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
   const uint16_t* Vg = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
   uint32_t pf[2][2][4];
+  int c_lo = 1 << 30, c_hi = -1;  // the chunks holding ranks of this split (kept ranks grow with the chunk)
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int cc = 64 * gi + lane;
     const uint4 c = ci[gi];
     const uint32_t kept = c.y + min(c.x - c.y, quota > c.w ? quota - c.w : 0u);  // lt + kept ties
     const bool mine = cc < nch_b && kept > 0u && (int)c.z < hi_rank && (int)(c.z + kept) > lo_rank;
+    const uint64_t mb = __ballot(mine);
+    if (mb) {
+      c_lo = min(c_lo, 64 * gi + __builtin_ctzll(mb));
+      c_hi = max(c_hi, 64 * gi + 63 - __builtin_clzll(mb));
+    }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = wave + kSAWaves * jj;
@@ -748,7 +755,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     // position (key = 2 * position + [at T]); a tie is kept while its rank
     // among all ties stays below the quota; ranks by ballot.
     const SortedEmit e{{ci[0], ci[1]}, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, len, quota, lo_rank, hi_rank,
-                       s_list, a.sel_idx ? a.sel_idx + (size_t)bh * a.budget : nullptr};
+                       c_lo, c_hi, s_list, a.sel_idx ? a.sel_idx + (size_t)bh * a.budget : nullptr};
     if (max_m <= 1) emit_sorted<1>(e);
     else if (max_m <= 2) emit_sorted<2>(e);
     else if (max_m <= 4) emit_sorted<4>(e);

@@ -179,20 +179,43 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// The value held by lane (lane ^ X), X = 1, 2, 3, 4, 7, 8, 15, 16, 31 or 63:
-// DPP where a row permute does it, else a swizzle or a permute through LDS.
+// The value held by lane (lane ^ X), X = 1, 2, 3, 4, 7, 8, 15, 16, 31 or 63,
+// without the LDS crossbar: DPP row permutes inside 16-lane rows (xor 4 as a
+// shift left or right by 4, whichever stays inside the lane's group of 8), the
+// gfx950 lane-swap instructions across rows (v_permlane16_swap exchanges lanes
+// l and l ^ 16, v_permlane32_swap lanes l and l ^ 32), and compositions of
+// these (xor 31 = xor 16 of xor 15, xor 63 = xor 32 of xor 31).
 constexpr int kQuadMirror = 0x1B;   // quad_perm [3,2,1,0] = xor 3
 constexpr int kDppRowRor8 = 0x128;  // rotate by 8 inside a 16-lane row = xor 8
+constexpr int kDppRowShl4 = 0x104;  // lane l takes lane l + 4 (inside the row)
+
+__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // {rows 1,3 <- rows 0,2; rows 0,2 <- rows 1,3}
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // {lanes 32.. <- 0..; lanes 0.. <- 32..}
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
 template <int X>
 __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
   if constexpr (X == 1) return dpp_u<kQuadXor1>(v);
   else if constexpr (X == 2) return dpp_u<kQuadXor2>(v);
   else if constexpr (X == 3) return dpp_u<kQuadMirror>(v);
+  else if constexpr (X == 4) {
+    // (both shifts with every lane active, then a branch-free pick: a
+    // conditional expression here becomes a branch, and a DPP read from a
+    // lane outside the branch returns nothing)
+    const uint32_t from_below = dpp_u<kDppRowShr4>(v), from_above = dpp_u<kDppRowShl4>(v);
+    const uint32_t pick = 0u - ((threadIdx.x >> 2) & 1u);
+    return from_above ^ ((from_below ^ from_above) & pick);
+  }
   else if constexpr (X == 7) return dpp_u<kDppRowHalfMirror>(v);
   else if constexpr (X == 8) return dpp_u<kDppRowRor8>(v);
   else if constexpr (X == 15) return dpp_u<kDppRowMirror>(v);
-  else if constexpr (X < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (X << 10));
-  else return (uint32_t)__shfl_xor((int)v, X, 64);
+  else if constexpr (X == 16) return xor16_u32(v);
+  else if constexpr (X == 31) return xor16_u32(dpp_u<kDppRowMirror>(v));
+  else return xor32_u32(xor16_u32(dpp_u<kDppRowMirror>(v)));  // X == 63
 }
 
 // One compare-exchange step: the lower lane of each pair keeps the minimum.
