@@ -51,7 +51,7 @@ __device__ __forceinline__ float xor_partner(float v) {
   if constexpr (H == 1) return quad_swap<kQuadXor1>(v);
   else if constexpr (H == 2) return quad_swap<kQuadXor2>(v);
   else if constexpr (H < 32) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (H << 10)));
-  else return __shfl_xor(v, 32, 64);
+  else return __uint_as_float(xor32_u32(__float_as_uint(v)));  // (gfx950 lane swap, no LDS)
 }
 
 template <int H>
@@ -868,8 +868,8 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     const float sj = (lane < 16 && t0 + 16 * wave + lane < nrows) ? acc[0] * a.qscale : -INFINITY;
     const float m_new = fmaxf(m_w, wave_max(sj));
     if (m_new != -INFINITY) {  // (wave-uniform) the wave has rows
-      const float corr = exp2f(m_w - m_new);  // 0 while m_w is -inf
-      const float pj = sj == -INFINITY ? 0.f : exp2f(sj - m_new);
+      const float corr = __builtin_amdgcn_exp2f(m_w - m_new);  // 0 while m_w is -inf
+      const float pj = sj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sj - m_new);
       l_w = __builtin_fmaf(l_w, corr, wave_sum(pj));
       m_w = m_new;
 #pragma unroll
@@ -891,8 +891,8 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float v = o[j];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+    v += __uint_as_float(xor16_u32(__float_as_uint(v)));
+    v += __uint_as_float(xor32_u32(__float_as_uint(v)));
     o[j] = v;
   }
   if (kg == 0) {
@@ -913,12 +913,12 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll
     for (int w = 0; w < kSAWaves; ++w) {
       const float mw = s_wm[w];
-      const float wgt = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      const float wgt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L = __builtin_fmaf(s_wl[w], wgt, L);
       O = __builtin_fmaf(s_red[w][tid], wgt, O);
     }
     if (a.splits == 1) {
-      a.out[(size_t)bh * kHeadDim + tid] = O / L;
+      a.out[(size_t)bh * kHeadDim + tid] = O * __builtin_amdgcn_rcpf(L);
     } else {
       // several splits: publish (m, l, o) write-through; the last split of
       // this head merges them
@@ -975,13 +975,13 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (s0 + u < a.splits && mv[u] != -INFINITY) {
-          const float wgt = exp2f(mv[u] - M);
+          const float wgt = __builtin_amdgcn_exp2f(mv[u] - M);
           L = __builtin_fmaf(lv[u], wgt, L);
           O = __builtin_fmaf(ov[u], wgt, O);
         }
       }
     }
-    a.out[(size_t)bh * kHeadDim + tid] = O / L;
+    a.out[(size_t)bh * kHeadDim + tid] = O * __builtin_amdgcn_rcpf(L);
   }
 }
 
