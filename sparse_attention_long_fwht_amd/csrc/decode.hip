@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     const uint16_t* qrow = a.q + (size_t)bh * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      qf[s] = col == 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * kg) : make_uint4(0, 0, 0, 0);
+      qf[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * kg);  // (B operand: q in every column)
   }
   const uint16_t* grec = a.rec + (size_t)bh * a.nch * kRecStride;
   const uint16_t* gsorted = a.sorted + (size_t)bh * a.nch * a.chunk;
@@ -840,48 +840,62 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 
   // ---- I. attention over the split's rows: tiles of 128 rows, 16 per wave.
   // Each wave keeps its own running max, sum and output over its rows.
-  // Scores: q (A operand, row 0) times the rows (B operand) puts row j's score
-  // in lane j.
+  // Scores: the rows (A operand, lane (col, kg) holds row col's k-range 8 kg
+  // of each 32) times q in every column (B operand) give C[r][j] = score of
+  // row r for every j, so lane (col, kg) holds the scores of rows 4 kg + i in
+  // acc[i] -- the rows whose V it multiplies (dims 8 col .. 8 col + 7).
   float o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.f;
   float m_w = -INFINITY, l_w = 0.f;
 #pragma unroll 1
   for (int t0 = 0; t0 < nrows; t0 += kSATile) {
+    const int r0 = t0 + 16 * wave;  // the wave's first row
     uint4 ka[4], vv[4];
     {
-      const int ia = t0 + 16 * wave + col;
+      const int ia = r0 + col;
       const int pa = min(max(s_list[ia < nrows ? ia : 0], 0), len - 1);  // (clamped: a position of the cache)
       const uint16_t* kr = Kg + (size_t)pa * kHeadDim + 8 * kg;
 #pragma unroll
       for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int iv = t0 + 16 * wave + 4 * i + kg;
+        const int iv = r0 + 4 * kg + i;
         const int pv = min(max(s_list[iv < nrows ? iv : 0], 0), len - 1);
         vv[i] = *reinterpret_cast<const uint4*>(Vg + (size_t)pv * kHeadDim + 8 * col);
       }
     }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_16x16x32_bf16(qf[s], ka[s], acc);
-    const float sj = (lane < 16 && t0 + 16 * wave + lane < nrows) ? acc[0] * a.qscale : -INFINITY;
-    const float m_new = fmaxf(m_w, wave_max(sj));
+    for (int s = 0; s < 4; ++s) acc = mfma_16x16x32_bf16(ka[s], qf[s], acc);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = r0 + 4 * kg + i < nrows ? acc[i] * a.qscale : -INFINITY;
+    // tile max and sum over the 16 rows: the four of this lane, then across
+    // the wave's four 16-lane rows (lane swaps)
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __uint_as_float(xor16_u32(__float_as_uint(mx))));
+    mx = fmaxf(mx, __uint_as_float(xor32_u32(__float_as_uint(mx))));
+    const float m_new = fmaxf(m_w, mx);
     if (m_new != -INFINITY) {  // (wave-uniform) the wave has rows
       const float corr = __builtin_amdgcn_exp2f(m_w - m_new);  // 0 while m_w is -inf
-      const float pj = sj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sj - m_new);
-      l_w = __builtin_fmaf(l_w, corr, wave_sum(pj));
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = sc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[i] - m_new);
+      float ls = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      ls += __uint_as_float(xor16_u32(__float_as_uint(ls)));
+      ls += __uint_as_float(xor32_u32(__float_as_uint(ls)));
+      l_w = __builtin_fmaf(l_w, corr, ls);
       m_w = m_new;
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] *= corr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pr = __shfl(pj, 4 * i + kg, 64);  // row 4i + kg of the wave's 16
         const uint32_t vw[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          o[2 * j] = __builtin_fmaf(pr, bf16_lo(vw[j]), o[2 * j]);
-          o[2 * j + 1] = __builtin_fmaf(pr, bf16_hi(vw[j]), o[2 * j + 1]);
+          o[2 * j] = __builtin_fmaf(pr[i], bf16_lo(vw[j]), o[2 * j]);
+          o[2 * j + 1] = __builtin_fmaf(pr[i], bf16_hi(vw[j]), o[2 * j + 1]);
         }
       }
     }
