@@ -272,40 +272,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int n_c = p1 - p0;
   const int kk = min(min(a.budget, len), n_c);
   if (wave < R) {
+    // (branch-free: selects instead of a search loop; cross-lane reads in
+    // uniform code only -- a value read from lane lk must have been computed
+    // with lane lk active)
     const int r = wave;
-    uint32_t cnt[7], loc = 0;
+    uint32_t cnt[7], cum[7], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) cnt[j] = s_hist[r][7 * lane + j];  // bins past 384 are zero
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
-      cnt[j] = s_hist[r][7 * lane + j];  // bins past 384 are zero
       loc += cnt[j];
+      cum[j] = loc;  // inclusive, inside the lane
     }
     const uint32_t inc = wave_inclusive_scan_u32(loc);
+    const uint32_t base = inc - loc;
     const int lmin = __builtin_ffsll((long long)__ballot(loc > 0)) - 1;            // n_c >= 1
     const int lk = __builtin_ffsll((long long)__ballot(inc >= (uint32_t)kk)) - 1;  // total n_c >= kk
-    uint32_t run = inc - loc;
-    int dmin_l = 0, localk_l = 0;
-    uint32_t limit_l = 0;
-    bool fmin = false, fk = false;
+    int fj = 7, kj = 7;  // this lane's first non-empty bin and first bin reaching kk
+#pragma unroll
+    for (int j = 6; j >= 0; --j) {
+      fj = cnt[j] > 0u ? j : fj;
+      kj = base + cum[j] >= (uint32_t)kk ? j : kj;
+    }
+    uint32_t lim_l = 0;  // positions up to that bin
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
-      const int d = 7 * lane + j;
-      s_hist[r][d] = run;  // exclusive offset of bin d
-      run += cnt[j];
-      if (!fmin && cnt[j] > 0) {
-        fmin = true;
-        dmin_l = d;
-      }
-      if (!fk && run >= (uint32_t)kk) {
-        fk = true;
-        localk_l = d;
-        limit_l = run;
-      }
+      lim_l = j == kj ? base + cum[j] : lim_l;
+      s_hist[r][7 * lane + j] = base + cum[j] - cnt[j];  // exclusive offset of the bin
     }
-    // (cross-lane reads stay outside lane-divergent code: a value read from
-    // lane lk must have been computed with lane lk active)
-    const int dmin = __builtin_amdgcn_readlane(dmin_l, lmin);
-    const int localk = __builtin_amdgcn_readlane(localk_l, lk);
-    const uint32_t limit = (uint32_t)__builtin_amdgcn_readlane((int)limit_l, lk);
+    const int dmin = 7 * lmin + __builtin_amdgcn_readlane(fj, lmin);
+    const int localk = 7 * lk + __builtin_amdgcn_readlane(kj, lk);
+    const uint32_t limit = (uint32_t)__builtin_amdgcn_readlane((int)lim_l, lk);
     uint16_t* rec = s_rec[r];
     if (lane == 0) {
       rec[0] = (uint16_t)dmin;
@@ -316,28 +313,34 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       s_limit[r] = limit;
       s_recw[r] = (uint32_t)(kRecHead + localk - dmin + 1 + 7) / 8;
     }
-    run = inc - loc;
+    // cum(d) for d = dmin .. localk; the other bins write the last (padding)
+    // word of the record, which nothing reads
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       const int d = 7 * lane + j;
-      run += cnt[j];
-      if (d >= dmin && d <= localk) rec[kRecHead + d - dmin] = (uint16_t)run;  // cum(d)
+      rec[d >= dmin && d <= localk ? kRecHead + d - dmin : kRecStride - 1] = (uint16_t)(base + cum[j]);
     }
   }
   __syncthreads();
 
-  // scatter the chunk-local positions of distances <= localk, ordered by
-  // distance, into LDS
+  // scatter the chunk-local positions, ordered by distance, into LDS: first
+  // every slot (bin offset + rank), then every store.  Positions past a
+  // head's kept slots are stored too (slots stay below the chunk length);
+  // nothing reads them.
 #pragma unroll
   for (int pass = 0; pass < kScanPasses; ++pass) {
     const int pp = p0 + pass * kScanThreads + tid;
-    if (pp < p1) {
+    if (p0 + pass * kScanThreads < p1 && pp < p1) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t d = dr[pass][r] >> 16;
-        const uint32_t slot = s_hist[r][d] + (dr[pass][r] & 0xFFFFu);
-        if (slot < s_limit[r]) s_sorted[r * a.chunk + slot] = (uint16_t)(pp - p0);
-      }
+      for (int r = 0; r < R; ++r) dr[pass][r] = s_hist[r][dr[pass][r] >> 16] + (dr[pass][r] & 0xFFFFu);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < kScanPasses; ++pass) {
+    const int pp = p0 + pass * kScanThreads + tid;
+    if (p0 + pass * kScanThreads < p1 && pp < p1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s_sorted[r * a.chunk + dr[pass][r]] = (uint16_t)(pp - p0);
     }
   }
   __syncthreads();
@@ -568,10 +571,12 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // where G' first reaches k_eff, and quota = k_eff - G(T-1) ties at T are
   // kept.  T lies in [lo, hi]: lo = the least dmin, hi = min(D*, the largest
   // localk).  Every wave reads the chunk headers (lane l: chunks l, 64 + l).
-  uint2 hd[2];
+  const bool two_groups = nch_b > 64;  // (wave-uniform) chunks 64.. exist
+  uint2 hd[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
   uint32_t lo_n = 0, dstar_n = 0, lkmax = 0;  // (lo and D* as 511 - x: every reduction a maximum)
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
+    if (gi == 1 && !two_groups) break;
     const int cc = 64 * gi + lane;
     hd[gi] = s_hdr[min(cc, kSelMaxChunks - 1)];
     if (cc >= nch_b) hd[gi] = make_uint2(0u, 0u);
@@ -690,12 +695,13 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // min(ties in earlier chunks, quota).
   const int lo_rank = split * a.rows_per_split;
   const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
-  uint4 ci[2];
+  uint4 ci[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
   uint32_t max_m;
   {
     uint32_t lt_carry = 0, tie_carry = 0, mm = 0;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
+      if (gi == 1 && !two_groups) break;
       const int cc = min(64 * gi + lane, max(nch_b - 1, 0));  // (headers of lanes past nch_b are zero)
       const int dm = (int)(hd[gi].x & 0xFFFFu), wd = (int)(hd[gi].x >> 16) - dm;
       const uint32_t n = hd[gi].y >> 16;
@@ -721,10 +727,11 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // the LDS prefix); lane l chunks l and 64 + l.
   const uint16_t* Kg = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
   const uint16_t* Vg = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
-  uint32_t pf[2][2][4];
+  uint32_t pf[2][2][4] = {};
   int c_lo = 1 << 30, c_hi = -1;  // the chunks holding ranks of this split (kept ranks grow with the chunk)
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
+    if (gi == 1 && !two_groups) break;
     const int cc = 64 * gi + lane;
     const uint4 c = ci[gi];
     const uint32_t kept = c.y + min(c.x - c.y, quota > c.w ? quota - c.w : 0u);  // lt + kept ties
@@ -737,8 +744,6 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = wave + kSAWaves * jj;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pf[gi][jj][u] = 0u;
       if (mine && j < (int)c.x && j < a.pre_slots) {
         const int lp = min((int)s_pre[(size_t)cc * a.pre_slots + j], min(a.chunk, len - cc * a.chunk) - 1);
         const size_t row = (size_t)(cc * a.chunk + lp) * kHeadDim;
