@@ -853,23 +853,29 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.f;
   float m_w = -INFINITY, l_w = 0.f;
+  // K and V of the wave's rows of tile t0 (rows past nrows read a valid row;
+  // their scores are masked)
+  auto gather = [&](int t0, uint4 (&ka)[4], uint4 (&vv)[4]) {
+    const int r0 = t0 + 16 * wave;
+    const int ia = r0 + col;
+    const int pa = min(max(s_list[ia < nrows ? ia : 0], 0), len - 1);  // (clamped: a position of the cache)
+    const uint16_t* kr = Kg + (size_t)pa * kHeadDim + 8 * kg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int iv = r0 + 4 * kg + i;
+      const int pv = min(max(s_list[iv < nrows ? iv : 0], 0), len - 1);
+      vv[i] = *reinterpret_cast<const uint4*>(Vg + (size_t)pv * kHeadDim + 8 * col);
+    }
+  };
+  uint4 ka[4], vv[4];
+  if (nrows > 0) gather(0, ka, vv);
 #pragma unroll 1
   for (int t0 = 0; t0 < nrows; t0 += kSATile) {
     const int r0 = t0 + 16 * wave;  // the wave's first row
-    uint4 ka[4], vv[4];
-    {
-      const int ia = r0 + col;
-      const int pa = min(max(s_list[ia < nrows ? ia : 0], 0), len - 1);  // (clamped: a position of the cache)
-      const uint16_t* kr = Kg + (size_t)pa * kHeadDim + 8 * kg;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int iv = r0 + 4 * kg + i;
-        const int pv = min(max(s_list[iv < nrows ? iv : 0], 0), len - 1);
-        vv[i] = *reinterpret_cast<const uint4*>(Vg + (size_t)pv * kHeadDim + 8 * col);
-      }
-    }
+    uint4 kn[4], vn[4];  // the next tile's rows, requested before this tile is used
+    if (t0 + kSATile < nrows) gather(t0 + kSATile, kn, vn);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma_16x16x32_bf16(ka[s], qf[s], acc);
@@ -903,6 +909,11 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
           o[2 * j + 1] = __builtin_fmaf(pr[i], bf16_hi(vw[j]), o[2 * j + 1]);
         }
       }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      ka[s] = kn[s];
+      vv[s] = vn[s];
     }
   }
   // ---- J. merge: o over the four k-groups of each wave, then the waves'
