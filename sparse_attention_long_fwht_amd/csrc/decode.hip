@@ -156,8 +156,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int wave = wave_id();
   const int p0 = c * a.chunk;
 
-  // the query rows first (wave w < R encodes query w), so that the encode does
-  // not wait behind the key-code loads
+  // kv_len, then the query rows (wave w < R encodes query w), then the key
+  // codes: vector loads complete in order, so a wait for one waits for every
+  // one issued before it -- the encode must not wait behind the key codes
+  const int len = min(a.kv_len[b], a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
   const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)(g * R + min(wave, R - 1))) * kHeadDim;
   const uint16_t q_lo = qrow[lane], q_hi = qrow[lane + 64];
   // first pass of key codes, addresses clamped to the capacity so that they
@@ -166,7 +168,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   int p = min(p0 + tid, a.cap - 1);
   uint4 klo = cbase[(size_t)p * 2];
   uint4 khi = cbase[(size_t)p * 2 + 1];
-  const int len = min(a.kv_len[b], a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
 
   __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins 385.. stay 0)
   __shared__ uint32_t s_code[R + 1][8];      // query codes, then the appended key's
