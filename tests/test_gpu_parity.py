@@ -131,14 +131,39 @@ def test_decode_group_sizes(env, Hq, Hkv):
     check_decode(DeviceCase(wl, A, torch), oracle)
 
 
-def test_decode_heavy_ties(env):
-    """Many keys share one code, so the threshold bin holds hundreds of ties:
-    the lower positions must win."""
+@pytest.mark.parametrize("distinct", [8, 4])
+def test_decode_heavy_ties(env, distinct):
+    """Many keys share one code (`distinct` codes tiled over the cache), so the
+    threshold bin holds hundreds of ties: the lower positions must win.  With 4
+    codes a chunk holds more than 64 entries at or below the threshold, which
+    takes the select kernel's bitmap emission; with 8, exactly 64 (the widest
+    in-register sort)."""
     A, torch, oracle = env
     wl = W.llama(34, cap=4096, budget=300, B=1, Hq=4, Hkv=1)
-    rep = wl.k[0, 0, :8].copy()
-    wl.k[0, 0] = np.tile(rep, (512, 1))
+    rep = wl.k[0, 0, :distinct].copy()
+    wl.k[0, 0] = np.tile(rep, (4096 // distinct, 1))
+    codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
+    _, _, dist_r, _ = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, wl.budget, wl.scale, threads=8)
+    widest = max_chunk_entries(wl, dist_r, wl.budget)
+    assert (widest > 64) if distinct == 4 else (widest == 64), widest
     check_decode(DeviceCase(wl, A, torch), oracle)
+
+
+def max_chunk_entries(wl, dist, budget):
+    """Largest number of positions at or below the threshold distance T in one
+    chunk, over all heads (the select kernel sorts up to 64 of them in
+    registers, more through a bitmap)."""
+    chunk, _ = chunking(wl.cap, wl.B * wl.Hkv)
+    worst = 0
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        k_eff = min(budget, L)
+        for h in range(wl.Hq):
+            d = dist[b, h, :L].astype(np.int64)
+            T = int(np.sort(d)[k_eff - 1])
+            for c0 in range(0, L, chunk):
+                worst = max(worst, int((d[c0:c0 + chunk] <= T).sum()))
+    return worst
 
 
 def chunking(cap, groups=1):
