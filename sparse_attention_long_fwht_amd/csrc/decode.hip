@@ -381,6 +381,7 @@ struct SelAttArgs {
   float* out;              // [B][Hq][128]
   float qscale;            // softmax scale * log2(e)
   int Hq, Hkv, R, cap, budget, chunk, nch, rec_win, pre_slots, splits, rows_per_split, bitmap_words;
+  int early_prefetch;  // speculative prefetch of the likely rows right after the record loads
 };
 
 constexpr int kSAThreads = 512;
@@ -556,6 +557,35 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   }
   __syncthreads();
 
+  // ---- early prefetch (speculative).  The first slots of a chunk's sorted
+  // prefix hold its smallest distances, the positions most likely kept: long
+  // before the selection is known, one word of each 128-byte line of their K
+  // and V rows is loaded (thread (cc, j): slot j < U of chunk cc, U about
+  // k_eff / chunks, over the chunks this split's ranks most likely fall in).
+  // The exact rows are prefetched again after E; the words are read only at
+  // the block's end, so nothing waits for these loads.  Only where the rows
+  // stay in L2 until used (a few heads, one block each: plan.h).
+  const int lo_rank = split * a.rows_per_split;
+  const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
+  const uint16_t* Kg = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
+  const uint16_t* Vg = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
+  uint32_t pe[4] = {0u, 0u, 0u, 0u};
+  if (a.early_prefetch && k_eff > 0) {
+    int ulog = 0;  // U = 1 << ulog
+    while ((1 << ulog) < a.pre_slots && (nch_b << ulog) < k_eff) ++ulog;
+    const int cs0 = (int)((int64_t)lo_rank * nch_b / k_eff);
+    const int cs1 = min(nch_b, (int)(((int64_t)hi_rank * nch_b + k_eff - 1) / k_eff) + 1);
+    if (tid < ((cs1 - cs0) << ulog)) {
+      const int cc = cs0 + (tid >> ulog), j = tid & ((1 << ulog) - 1);
+      const int lp = min((int)s_pre[(size_t)cc * a.pre_slots + j], min(a.chunk, len - cc * a.chunk) - 1);
+      const size_t row = (size_t)(cc * a.chunk + lp) * kHeadDim;
+      pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
+      pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
+      pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
+      pe[3] = *reinterpret_cast<const uint32_t*>(Vg + row + 64);
+    }
+  }
+
   // Record word idx of chunk cc: from the LDS window, else from the global
   // record (volatile: never merged with the LDS read into one generic load).
   auto rec_word = [&](int cc, int idx) -> uint32_t {
@@ -694,8 +724,6 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // positions at T (the next slots).  Ties are kept in position order, so a
   // chunk's first kept rank is (positions below T in earlier chunks) +
   // min(ties in earlier chunks, quota).
-  const int lo_rank = split * a.rows_per_split;
-  const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
   uint4 ci[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
   uint32_t max_m;
   {
@@ -726,8 +754,6 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // words until the block's last instructions (pf_sink), so nothing waits for
   // these loads before the gather does.  Wave w takes slots w and w + 8 (within
   // the LDS prefix); lane l chunks l and 64 + l.
-  const uint16_t* Kg = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
-  const uint16_t* Vg = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
   uint32_t pf[2][2][4] = {};
   int c_lo = 1 << 30, c_hi = -1;  // the chunks holding ranks of this split (kept ranks grow with the chunk)
 #pragma unroll
@@ -970,6 +996,8 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int u = 0; u < 4; ++u) pf_sink ^= pf[gi][jj][u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pf_sink ^= pe[u];
     if (a.budget < 0) a.out[tid] = (float)pf_sink;
   }
   if (a.splits == 1) return;
@@ -1068,7 +1096,7 @@ hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, co
   }
   SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
                 scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch, p.rec_win,
-                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words};
+                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words, p.early_prefetch ? 1 : 0};
   if (p.lds_select > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_attend_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_select);

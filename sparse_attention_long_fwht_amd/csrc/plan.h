@@ -37,6 +37,7 @@ struct Plan {
   int bitmap_words;    // ceil(cap / 32)
   size_t lds_select;   // dynamic LDS of the select/attend kernel
   bool supported;      // false: the select/attend kernel's LDS would not fit this shape and budget
+  bool early_prefetch; // select/attend prefetches the likely rows before the selection is known
   size_t off_sorted, off_rec, off_part, off_count, total;
 };
 
@@ -53,6 +54,7 @@ inline int choose_chunk(int cap, int min_chunk, int max_chunks) {
 // units idle (about kSelectBlocks blocks wanted) or a block would attend more
 // than 16 tiles; at most 64 blocks share a head.
 constexpr int kSelectBlocks = 256;
+constexpr int kEarlyPrefetchHeads = 64;
 inline int choose_rows_per_split(int budget, int heads) {
   int splits = (kSelectBlocks + heads - 1) / heads;
   const int tiles = (budget + 127) / 128;
@@ -103,6 +105,11 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   p.rows_per_split = choose_rows_per_split(budget, B * Hq);
   p.splits = (budget + p.rows_per_split - 1) / p.rows_per_split;
   p.bitmap_words = ((cap + 31) / 32 + 3) / 4 * 4;  // keeps the record area 16-byte aligned
+  // The speculative prefetch pays where the selection is latency-bound: a few
+  // heads, one block each, whose rows stay in L2 until the gather.  With many
+  // blocks the extra rows evict each other (measured: batch 16 x 32 heads,
+  // 53.7 -> 64.5 us) and the gather is bandwidth-bound anyway.
+  p.early_prefetch = p.splits == 1 && (int64_t)B * Hq <= kEarlyPrefetchHeads;
   size_t rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);
   const size_t tie_bytes = (size_t)p.bitmap_words * sizeof(uint32_t);
   auto lds_for = [&](int pre) {
