@@ -16,6 +16,7 @@ _lib = None
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _u8p = ctypes.POINTER(ctypes.c_uint8)
 _i32p = ctypes.POINTER(ctypes.c_int32)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
 _f32p = ctypes.POINTER(ctypes.c_float)
 
 
@@ -50,6 +51,12 @@ def lib():
         L.oracle_decode_step.argtypes = [i32, i32, i32, i32, _u16p, _u16p, _u16p, _u8p, _i32p, i32,
                                          ctypes.c_float, _f32p, _i32p, _u16p, _u8p, i32]
         L.oracle_decode_step.restype = ctypes.c_int
+        L.oracle_topk_forced.argtypes = [_u16p, _u8p, i32, i32, _i32p]
+        L.oracle_topk_forced.restype = i32
+        L.oracle_decode_step_forced.argtypes = [i32, i32, i32, i32, _u16p, _u16p, _u16p, _u8p, _i32p, i32,
+                                                ctypes.c_float, i32, i32, _u32p, i32, _f32p, _i32p, _u16p,
+                                                _u8p, i32]
+        L.oracle_decode_step_forced.restype = ctypes.c_int
         L.oracle_dense_attention.argtypes = [i32, i32, i32, i32, _u16p, _u16p, _u16p, _i32p,
                                              ctypes.c_float, _f32p, i32]
         L.oracle_dense_attention.restype = ctypes.c_int
@@ -128,6 +135,17 @@ def topk(dist, budget):
     return sel, int(k_eff)
 
 
+def topk_forced(dist, forced, budget):
+    """Top-k with forced positions (forced: bool/uint8 array like dist, or None)."""
+    d = _c(dist, np.uint16)
+    f = None if forced is None else _c(forced, np.uint8)
+    assert f is None or f.shape == d.shape
+    sel = np.empty(budget, np.int32)
+    k_eff = lib().oracle_topk_forced(_ptr(d, _u16p), _ptr(f, _u8p), int(d.shape[0]), int(budget),
+                                     _ptr(sel, _i32p))
+    return sel, int(k_eff)
+
+
 def attention_rows(q, k_head, v_head, pos, scale):
     q = _c(q, np.uint16)
     kh = _c(k_head, np.uint16)
@@ -162,10 +180,13 @@ def encode_keys(k, end, start=None, codes=None):
     return codes
 
 
-def decode_step(q, k, v, codes, kv_len, budget, scale, threads=1, want_dist=True):
+def decode_step(q, k, v, codes, kv_len, budget, scale, threads=1, want_dist=True, sink=0, recent=0,
+                mask=None):
     """Full decode step on the host.  Returns (out, sel_idx, dist, q_codes).
 
     dist rows are zero at positions >= kv_len[b] (never written by the oracle).
+    sink / recent / mask (uint32 [B][words], bit p % 32 of word p / 32) name
+    the forced positions; all three absent gives the plain top-k.
     """
     q = _c(q, np.uint16)
     k = _c(k, np.uint16)
@@ -179,10 +200,19 @@ def decode_step(q, k, v, codes, kv_len, budget, scale, threads=1, want_dist=True
     sel = np.empty((B, Hq, budget), np.int32)
     dist = np.zeros((B, Hq, cap), np.uint16) if want_dist else None
     qc = np.empty((B, Hq, 32), np.uint8)
-    rc = lib().oracle_decode_step(B, Hq, Hkv, cap, _ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p),
-                                  _ptr(codes, _u8p), _ptr(kv_len, _i32p), int(budget), float(scale),
-                                  _ptr(out, _f32p), _ptr(sel, _i32p), _ptr(dist, _u16p), _ptr(qc, _u8p),
-                                  int(threads))
+    if sink == 0 and recent == 0 and mask is None:
+        rc = lib().oracle_decode_step(B, Hq, Hkv, cap, _ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p),
+                                      _ptr(codes, _u8p), _ptr(kv_len, _i32p), int(budget), float(scale),
+                                      _ptr(out, _f32p), _ptr(sel, _i32p), _ptr(dist, _u16p), _ptr(qc, _u8p),
+                                      int(threads))
+    else:
+        m = None if mask is None else _c(mask, np.uint32)
+        assert m is None or (m.ndim == 2 and m.shape[0] == B)
+        rc = lib().oracle_decode_step_forced(B, Hq, Hkv, cap, _ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p),
+                                             _ptr(codes, _u8p), _ptr(kv_len, _i32p), int(budget), float(scale),
+                                             int(sink), int(recent), _ptr(m, _u32p),
+                                             0 if m is None else int(m.shape[1]), _ptr(out, _f32p),
+                                             _ptr(sel, _i32p), _ptr(dist, _u16p), _ptr(qc, _u8p), int(threads))
     if rc != 0:
         raise ValueError("oracle_decode_step: invalid arguments")
     return out, sel, dist, qc

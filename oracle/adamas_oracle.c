@@ -13,7 +13,9 @@
  *             mlsanity.com citation map).
  *   [blog]    "ADAMAS：稀疏注意力优化技术解析与应用实践" (jsqmd.com), with its
  *             section numbers (§2.1 Hadamard, §2.2 bucketing, §2.3 Manhattan
- *             distance, §3.1 compressed cache).
+ *             distance, §3.1 compressed cache, §3.2 precision tuning, §6
+ *             practice advice).
+ *   [map]     the mlsanity.com citation-map page of the paper, "Builds on" list.
  *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math (no FMA contraction,
  * no reassociation: each float add/sub rounds once, in the order written).
@@ -195,6 +197,51 @@ int oracle_topk(const uint16_t* dist, int32_t len, int32_t budget, int32_t* sel)
   return k_eff;
 }
 
+typedef struct {
+  uint8_t cls; /* 0: forced, 1: ranked by distance */
+  uint16_t d;
+  int32_t p;
+} forced_dist_pos;
+
+static int cmp_forced(const void* x, const void* y) {
+  const forced_dist_pos* a = (const forced_dist_pos*)x;
+  const forced_dist_pos* b = (const forced_dist_pos*)y;
+  if (a->cls != b->cls) return a->cls < b->cls ? -1 : 1;
+  if (a->cls == 1 && a->d != b->d) return a->d < b->d ? -1 : 1;
+  if (a->p != b->p) return a->p < b->p ? -1 : 1;
+  return 0;
+}
+
+/*
+ * Top-k with forced positions.  [blog §3.2] and [blog §6]: special tokens (a
+ * leading [CLS] is the example) should keep full attention, i.e. never be
+ * dropped by the sparse selection; [map]: the paper builds on the
+ * attention-sink work, whose first tokens are always attended.
+ * Reading: forced[p] != 0 marks position p as forced.  The k_eff = min(budget,
+ * len) kept positions are taken in this order: first the forced positions, in
+ * position order; then the others by (distance, position) as in oracle_topk.
+ * So every forced position is kept while they fit the budget, and the rest of
+ * the budget goes to the closest other positions; if more than k_eff positions
+ * are forced, the k_eff lowest of them are kept.  forced == NULL: no position
+ * is forced (the result is oracle_topk's).  Output as in oracle_topk.
+ */
+int oracle_topk_forced(const uint16_t* dist, const uint8_t* forced, int32_t len, int32_t budget,
+                       int32_t* sel) {
+  int32_t k_eff = budget < len ? budget : len;
+  forced_dist_pos* v = (forced_dist_pos*)malloc(sizeof(forced_dist_pos) * (size_t)(len > 0 ? len : 1));
+  for (int32_t p = 0; p < len; ++p) {
+    v[p].cls = (forced && forced[p]) ? 0 : 1;
+    v[p].d = dist[p];
+    v[p].p = p;
+  }
+  qsort(v, (size_t)len, sizeof(forced_dist_pos), cmp_forced);
+  for (int32_t i = 0; i < k_eff; ++i) sel[i] = v[i].p;
+  qsort(sel, (size_t)k_eff, sizeof(int32_t), cmp_i32);
+  for (int32_t i = k_eff; i < budget; ++i) sel[i] = -1;
+  free(v);
+  return k_eff;
+}
+
 /*
  * Exact softmax attention of one query over the listed rows of one KV head
  * ([v2-abs]: the selected positions gather the original K/V for sparse
@@ -266,16 +313,24 @@ int oracle_encode_keys(int32_t B, int32_t Hkv, int32_t cap, const uint16_t* k,
  *   2. dist[p] = Manhattan distance to codes[b][g][p] for p < kv_len[b]
  *      (optional output; entries at p >= kv_len[b] are left untouched)
  *   3. top-k with k_eff = min(budget, kv_len[b])       -> sel_idx (optional)
+ *      with the forced positions of oracle_topk_forced: p < sink, or
+ *      p >= kv_len[b] - recent, or bit p % 32 of mask[b * mask_words + p / 32]
+ *      (mask may be NULL)
  *   4. exact fp64 softmax attention over the selected original K/V rows -> out
  * g = h / (Hq / Hkv).  threads > 1 runs independent (b, h) pairs in parallel
- * (no change to any arithmetic).  Returns 0, or 1 on invalid arguments.
+ * (no change to any arithmetic).  Returns 0, or 1 on invalid arguments
+ * (including sink < 0, recent < 0, sink + recent > budget, or a mask with
+ * fewer than ceil(cap / 32) words per batch entry).
  */
-int oracle_decode_step(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
-                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                       const uint8_t* codes, const int32_t* kv_len, int32_t budget,
-                       float scale, float* out, int32_t* sel_idx, uint16_t* dist,
-                       uint8_t* q_codes, int32_t threads) {
+int oracle_decode_step_forced(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
+                              const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const uint8_t* codes, const int32_t* kv_len, int32_t budget,
+                              float scale, int32_t sink, int32_t recent, const uint32_t* mask,
+                              int32_t mask_words, float* out, int32_t* sel_idx, uint16_t* dist,
+                              uint8_t* q_codes, int32_t threads) {
   if (bad_dims(B, Hq, Hkv, cap) || budget < 1) return 1;
+  if (sink < 0 || recent < 0 || (int64_t)sink + recent > budget) return 1;
+  if (mask && (int64_t)mask_words * 32 < cap) return 1;
   for (int32_t b = 0; b < B; ++b)
     if (kv_len[b] < 1 || kv_len[b] > cap) return 1;
   const int32_t group = Hq / Hkv;
@@ -295,8 +350,14 @@ int oracle_decode_step(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
     for (int32_t p = 0; p < len; ++p)
       d[p] = (uint16_t)oracle_distance(qc, codes + (kvbase + (size_t)p) * CODE_BYTES);
     if (dist) memcpy(dist + (size_t)bh * cap, d, sizeof(uint16_t) * (size_t)len);
+    uint8_t* f = (uint8_t*)malloc((size_t)len);
+    for (int32_t p = 0; p < len; ++p) {
+      const int in_mask = mask ? (int)((mask[(size_t)b * mask_words + (size_t)(p / 32)] >> (p % 32)) & 1u) : 0;
+      f[p] = (uint8_t)(p < sink || p >= len - recent || in_mask);
+    }
     int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)budget);
-    int32_t k_eff = oracle_topk(d, len, budget, sel);
+    int32_t k_eff = oracle_topk_forced(d, f, len, budget, sel);
+    free(f);
     if (sel_idx) memcpy(sel_idx + (size_t)bh * budget, sel, sizeof(int32_t) * (size_t)budget);
     oracle_attention_rows(q + (size_t)bh * HD, k + kvbase * HD, v + kvbase * HD, sel, k_eff,
                           (double)scale, out + (size_t)bh * HD);
@@ -304,6 +365,16 @@ int oracle_decode_step(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
     free(d);
   }
   return 0;
+}
+
+/* The decode step with no forced positions. */
+int oracle_decode_step(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
+                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const uint8_t* codes, const int32_t* kv_len, int32_t budget,
+                       float scale, float* out, int32_t* sel_idx, uint16_t* dist,
+                       uint8_t* q_codes, int32_t threads) {
+  return oracle_decode_step_forced(B, Hq, Hkv, cap, q, k, v, codes, kv_len, budget, scale, 0, 0,
+                                   NULL, 0, out, sel_idx, dist, q_codes, threads);
 }
 
 /*

@@ -328,6 +328,125 @@ def test_topk_all_equal_and_budget_over_len(oracle_mod):
     assert k_eff == 50 and list(sel[:50]) == list(range(50)) and np.all(sel[50:] == -1)
 
 
+# ---------------------------------------------------------------- forced positions
+# Blog sections 3.2 and 6 (special tokens keep full attention); the paper builds
+# on attention-sink work (citation map).  Reading: forced positions are kept
+# first, in position order, then the budget's rest by (distance, position).
+
+
+def test_topk_forced_brute_force_tiny(oracle_mod):
+    """Exhaustive: the chosen k-subset contains min(k, |F|) forced positions (the
+    lowest ones) and, among subsets that do, minimises the sorted (d, p) list of
+    its unforced members."""
+    from itertools import combinations
+    rng = np.random.default_rng(31)
+    for _ in range(200):
+        n = int(rng.integers(1, 9))
+        d = rng.integers(0, 3, n).astype(np.uint16)
+        f = rng.random(n) < 0.3
+        k = int(rng.integers(1, n + 1))
+        F = [p for p in range(n) if f[p]]
+        want_forced = set(F[:min(k, len(F))])
+        subsets = [s for s in combinations(range(n), k) if want_forced <= set(s)]
+        best = min(subsets, key=lambda s: sorted((int(d[p]), p) for p in s if p not in want_forced))
+        sel, k_eff = oracle_mod.topk_forced(d, f.astype(np.uint8), k)
+        assert k_eff == k and list(sel[:k_eff]) == sorted(best)
+
+
+def test_topk_forced_reductions(oracle_mod):
+    rng = np.random.default_rng(32)
+    for _ in range(100):
+        n = int(rng.integers(1, 60))
+        d = rng.integers(0, 6, n).astype(np.uint16)
+        budget = int(rng.integers(1, n + 4))
+        plain = oracle_mod.topk(d, budget)
+        # no forced position (and a NULL mask): the plain top-k
+        none = oracle_mod.topk_forced(d, np.zeros(n, np.uint8), budget)
+        assert np.array_equal(none[0], plain[0]) and none[1] == plain[1]
+        nul = oracle_mod.topk_forced(d, None, budget)
+        assert np.array_equal(nul[0], plain[0])
+        # forcing positions the plain top-k keeps anyway changes nothing
+        f = np.zeros(n, np.uint8)
+        kept = plain[0][:plain[1]]
+        f[kept[rng.random(kept.size) < 0.5]] = 1
+        assert np.array_equal(oracle_mod.topk_forced(d, f, budget)[0], plain[0])
+        # forced = exactly k positions: the selection is the forced set
+        k = min(budget, n)
+        F = np.sort(rng.choice(n, k, replace=False))
+        f = np.zeros(n, np.uint8)
+        f[F] = 1
+        sel, k_eff = oracle_mod.topk_forced(d, f, budget)
+        assert k_eff == k and np.array_equal(sel[:k], F)
+
+
+def test_topk_forced_distances_shifted_equivalence(oracle_mod):
+    """Giving every forced position a distance below all others (a transform
+    done here in numpy on the inputs) makes the plain top-k agree, as long as
+    at most k_eff positions are forced."""
+    rng = np.random.default_rng(33)
+    for _ in range(100):
+        n = int(rng.integers(1, 80))
+        d = rng.integers(0, 385, n).astype(np.uint16)
+        budget = int(rng.integers(1, n + 4))
+        k_eff = min(budget, n)
+        nf = int(rng.integers(0, k_eff + 1))
+        f = np.zeros(n, np.uint8)
+        f[rng.choice(n, nf, replace=False)] = 1
+        shifted = np.where(f == 1, 0, d.astype(np.int64) + 1).astype(np.uint16)
+        assert np.array_equal(oracle_mod.topk_forced(d, f, budget)[0], oracle_mod.topk(shifted, budget)[0])
+
+
+def test_decode_forced_sink_recent_mask(oracle_mod):
+    """The whole step with sinks, a recent window and a mask: every forced
+    position is selected, the rest is the plain top-k of the others (numpy
+    lexsort over the oracle's own distances), and out is attention over it."""
+    wl = small_case(seed=24)
+    codes = oracle_mod.encode_keys(wl.k, wl.kv_len)
+    sink, recent, budget = 4, 6, 40
+    words = (wl.cap + 31) // 32
+    mask = np.zeros((wl.B, words), np.uint32)
+    special = [(0, 77), (0, 250), (1, 3), (1, 120), (1, 200)]  # (b, position); 200 >= len of b = 1
+    for b, p in special:
+        mask[b, p // 32] |= np.uint32(1 << (p % 32))
+    out, sel, dist, _ = oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, budget, wl.scale,
+                                               sink=sink, recent=recent, mask=mask)
+    group = wl.Hq // wl.Hkv
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        F = set(range(sink)) | set(range(L - recent, L)) | {p for bb, p in special if bb == b and p < L}
+        for h in range(wl.Hq):
+            k_eff = min(budget, L)
+            S = sel[b, h, :k_eff]
+            assert F <= set(S.tolist()) and np.all(sel[b, h, k_eff:] == -1)
+            rest = np.array(sorted(set(range(L)) - F))
+            d = dist[b, h, rest].astype(np.int64)
+            others = np.sort(rest[np.lexsort((rest, d))[:k_eff - len(F)]])
+            assert np.array_equal(np.sort(np.concatenate([np.array(sorted(F)), others])), S)
+            g = h // group
+            # (the step takes the scale as fp32)
+            o = oracle_mod.attention_rows(wl.q[b, h], wl.k[b, g], wl.v[b, g], S, float(np.float32(wl.scale)))
+            assert np.array_equal(out[b, h], o)
+
+
+def test_decode_forced_full_window_is_dense(oracle_mod):
+    """recent = budget >= kv_len: every position is forced, so the step is dense attention."""
+    wl = small_case(seed=25)
+    codes = oracle_mod.encode_keys(wl.k, wl.kv_len)
+    out, _, _, _ = oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, 300, wl.scale, recent=300)
+    dense = oracle_mod.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale)
+    assert np.array_equal(out, dense)
+
+
+def test_decode_forced_invalid_arguments(oracle_mod):
+    wl = small_case()
+    codes = oracle_mod.encode_keys(wl.k, wl.kv_len)
+    for kw in (dict(sink=-1), dict(recent=-2), dict(sink=20, recent=13)):
+        with pytest.raises(ValueError):
+            oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, 32, 0.1, **kw)
+    with pytest.raises(ValueError):  # mask narrower than ceil(cap / 32) words
+        oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, 32, 0.1, mask=np.zeros((2, 9), np.uint32))
+
+
 # ---------------------------------------------------------------- attention
 
 
