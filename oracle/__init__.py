@@ -136,7 +136,8 @@ def topk(dist, budget):
 
 
 def topk_forced(dist, forced, budget):
-    """Top-k with forced positions (forced: bool/uint8 array like dist, or None)."""
+    """Top-k with forced positions.  forced: uint8 array like dist (2 = always
+    kept, 1 = preferred, 0 = ordinary), or None."""
     d = _c(dist, np.uint16)
     f = None if forced is None else _c(forced, np.uint8)
     assert f is None or f.shape == d.shape

@@ -198,7 +198,7 @@ int oracle_topk(const uint16_t* dist, int32_t len, int32_t budget, int32_t* sel)
 }
 
 typedef struct {
-  uint8_t cls; /* 0: forced, 1: ranked by distance */
+  uint8_t cls; /* 0: always kept, 1: preferred, 2: ranked by distance */
   uint16_t d;
   int32_t p;
 } forced_dist_pos;
@@ -207,7 +207,7 @@ static int cmp_forced(const void* x, const void* y) {
   const forced_dist_pos* a = (const forced_dist_pos*)x;
   const forced_dist_pos* b = (const forced_dist_pos*)y;
   if (a->cls != b->cls) return a->cls < b->cls ? -1 : 1;
-  if (a->cls == 1 && a->d != b->d) return a->d < b->d ? -1 : 1;
+  if (a->cls == 2 && a->d != b->d) return a->d < b->d ? -1 : 1;
   if (a->p != b->p) return a->p < b->p ? -1 : 1;
   return 0;
 }
@@ -217,20 +217,24 @@ static int cmp_forced(const void* x, const void* y) {
  * leading [CLS] is the example) should keep full attention, i.e. never be
  * dropped by the sparse selection; [map]: the paper builds on the
  * attention-sink work, whose first tokens are always attended.
- * Reading: forced[p] != 0 marks position p as forced.  The k_eff = min(budget,
- * len) kept positions are taken in this order: first the forced positions, in
- * position order; then the others by (distance, position) as in oracle_topk.
- * So every forced position is kept while they fit the budget, and the rest of
- * the budget goes to the closest other positions; if more than k_eff positions
- * are forced, the k_eff lowest of them are kept.  forced == NULL: no position
- * is forced (the result is oracle_topk's).  Output as in oracle_topk.
+ * Reading: force[p] = 2 marks a position that is always kept (a sink or a
+ * recent-window position; the caller guarantees at most k_eff of them), 1 a
+ * preferred position (a special token of the caller's mask), 0 an ordinary
+ * one.  The k_eff = min(budget, len) kept positions are taken in this order:
+ * the force-2 positions; then the force-1 positions, lower positions first;
+ * then the ordinary positions by (distance, position) as in oracle_topk.  So
+ * the rest of the budget after the always-kept positions goes to the special
+ * tokens (the lowest ones if they do not all fit) and then to the closest
+ * ordinary positions.  force == NULL: every position is ordinary (the result is
+ * oracle_topk's).  Output as in oracle_topk.
  */
-int oracle_topk_forced(const uint16_t* dist, const uint8_t* forced, int32_t len, int32_t budget,
+int oracle_topk_forced(const uint16_t* dist, const uint8_t* force, int32_t len, int32_t budget,
                        int32_t* sel) {
   int32_t k_eff = budget < len ? budget : len;
   forced_dist_pos* v = (forced_dist_pos*)malloc(sizeof(forced_dist_pos) * (size_t)(len > 0 ? len : 1));
   for (int32_t p = 0; p < len; ++p) {
-    v[p].cls = (forced && forced[p]) ? 0 : 1;
+    const int f = force ? force[p] : 0;
+    v[p].cls = (uint8_t)(f >= 2 ? 0 : (f == 1 ? 1 : 2));
     v[p].d = dist[p];
     v[p].p = p;
   }
@@ -313,9 +317,10 @@ int oracle_encode_keys(int32_t B, int32_t Hkv, int32_t cap, const uint16_t* k,
  *   2. dist[p] = Manhattan distance to codes[b][g][p] for p < kv_len[b]
  *      (optional output; entries at p >= kv_len[b] are left untouched)
  *   3. top-k with k_eff = min(budget, kv_len[b])       -> sel_idx (optional)
- *      with the forced positions of oracle_topk_forced: p < sink, or
- *      p >= kv_len[b] - recent, or bit p % 32 of mask[b * mask_words + p / 32]
- *      (mask may be NULL)
+ *      with the forced positions of oracle_topk_forced: always kept are
+ *      p < sink and p >= kv_len[b] - recent (sink + recent <= budget, so they
+ *      fit); preferred are the positions whose bit p % 32 of
+ *      mask[b * mask_words + p / 32] is set (mask may be NULL)
  *   4. exact fp64 softmax attention over the selected original K/V rows -> out
  * g = h / (Hq / Hkv).  threads > 1 runs independent (b, h) pairs in parallel
  * (no change to any arithmetic).  Returns 0, or 1 on invalid arguments
@@ -353,7 +358,7 @@ int oracle_decode_step_forced(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
     uint8_t* f = (uint8_t*)malloc((size_t)len);
     for (int32_t p = 0; p < len; ++p) {
       const int in_mask = mask ? (int)((mask[(size_t)b * mask_words + (size_t)(p / 32)] >> (p % 32)) & 1u) : 0;
-      f[p] = (uint8_t)(p < sink || p >= len - recent || in_mask);
+      f[p] = (uint8_t)((p < sink || p >= len - recent) ? 2 : (in_mask ? 1 : 0));
     }
     int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)budget);
     int32_t k_eff = oracle_topk_forced(d, f, len, budget, sel);

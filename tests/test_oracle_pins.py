@@ -330,26 +330,31 @@ def test_topk_all_equal_and_budget_over_len(oracle_mod):
 
 # ---------------------------------------------------------------- forced positions
 # Blog sections 3.2 and 6 (special tokens keep full attention); the paper builds
-# on attention-sink work (citation map).  Reading: forced positions are kept
-# first, in position order, then the budget's rest by (distance, position).
+# on attention-sink work (citation map).  Reading: sinks and the recent window
+# (force 2) are always kept; special tokens of the caller's mask (force 1) take
+# the rest of the budget first, lower positions first; then the other positions
+# by (distance, position).
 
 
 def test_topk_forced_brute_force_tiny(oracle_mod):
-    """Exhaustive: the chosen k-subset contains min(k, |F|) forced positions (the
-    lowest ones) and, among subsets that do, minimises the sorted (d, p) list of
-    its unforced members."""
+    """Exhaustive: the chosen k-subset holds every force-2 position, then the
+    lowest force-1 positions that fit, and, among subsets that hold those,
+    minimises the sorted (d, p) list of its other members."""
     from itertools import combinations
     rng = np.random.default_rng(31)
-    for _ in range(200):
+    for _ in range(300):
         n = int(rng.integers(1, 9))
         d = rng.integers(0, 3, n).astype(np.uint16)
-        f = rng.random(n) < 0.3
         k = int(rng.integers(1, n + 1))
-        F = [p for p in range(n) if f[p]]
-        want_forced = set(F[:min(k, len(F))])
-        subsets = [s for s in combinations(range(n), k) if want_forced <= set(s)]
-        best = min(subsets, key=lambda s: sorted((int(d[p]), p) for p in s if p not in want_forced))
-        sel, k_eff = oracle_mod.topk_forced(d, f.astype(np.uint8), k)
+        f = np.where(rng.random(n) < 0.3, 1, 0).astype(np.uint8)
+        always = rng.choice(n, int(rng.integers(0, k + 1)), replace=False)
+        f[always] = 2
+        A = set(always.tolist())
+        P = [p for p in range(n) if f[p] == 1]
+        want = A | set(P[:k - len(A)])
+        subsets = [s for s in combinations(range(n), k) if want <= set(s)]
+        best = min(subsets, key=lambda s: sorted((int(d[p]), p) for p in s if p not in want))
+        sel, k_eff = oracle_mod.topk_forced(d, f, k)
         assert k_eff == k and list(sel[:k_eff]) == sorted(best)
 
 
@@ -370,13 +375,18 @@ def test_topk_forced_reductions(oracle_mod):
         kept = plain[0][:plain[1]]
         f[kept[rng.random(kept.size) < 0.5]] = 1
         assert np.array_equal(oracle_mod.topk_forced(d, f, budget)[0], plain[0])
-        # forced = exactly k positions: the selection is the forced set
+        # forced (either kind) = exactly k positions: the selection is that set
         k = min(budget, n)
         F = np.sort(rng.choice(n, k, replace=False))
-        f = np.zeros(n, np.uint8)
-        f[F] = 1
+        for kind in (1, 2):
+            f = np.zeros(n, np.uint8)
+            f[F] = kind
+            sel, k_eff = oracle_mod.topk_forced(d, f, budget)
+            assert k_eff == k and np.array_equal(sel[:k], F)
+        # more preferred positions than the budget: the lowest ones
+        f = np.ones(n, np.uint8)
         sel, k_eff = oracle_mod.topk_forced(d, f, budget)
-        assert k_eff == k and np.array_equal(sel[:k], F)
+        assert np.array_equal(sel[:k], np.arange(k))
 
 
 def test_topk_forced_distances_shifted_equivalence(oracle_mod):
@@ -426,6 +436,25 @@ def test_decode_forced_sink_recent_mask(oracle_mod):
             # (the step takes the scale as fp32)
             o = oracle_mod.attention_rows(wl.q[b, h], wl.k[b, g], wl.v[b, g], S, float(np.float32(wl.scale)))
             assert np.array_equal(out[b, h], o)
+
+
+def test_decode_forced_window_kept_when_mask_overflows(oracle_mod):
+    """A mask with more special tokens than the budget: the sinks and the
+    window are still all kept, and the lowest special tokens outside them fill
+    the rest."""
+    wl = small_case(seed=26)
+    codes = oracle_mod.encode_keys(wl.k, wl.kv_len)
+    words = (wl.cap + 31) // 32
+    mask = np.full((wl.B, words), 0x55555555, np.uint32)  # every even position
+    sink, recent, budget = 3, 8, 30
+    _, sel, _, _ = oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, budget, wl.scale, sink=sink,
+                                          recent=recent, mask=mask)
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        always = list(range(sink)) + list(range(L - recent, L))
+        evens = [p for p in range(sink, L - recent) if p % 2 == 0][:budget - len(always)]
+        for h in range(wl.Hq):
+            assert np.array_equal(sel[b, h], np.array(sorted(always + evens)))
 
 
 def test_decode_forced_full_window_is_dense(oracle_mod):
