@@ -277,6 +277,16 @@ def main():
             extra["step_us_budget1024"] = round(ms_1k * 1e3, 3)
             log("[bench] budget 1024: %.2f us" % (ms_1k * 1e3))
             del g_1k
+        # forced positions: 4 sinks and a 64-token window (same budget, same data)
+        if budget > 68:
+            def forced_step(c):
+                q, k, v, codes = c
+                A.decode_step(q, k, v, codes, kv_len, budget, wl.scale, out, ws, append=True, sink=4, recent=64)
+            g_f = graph_of(forced_step, copies)
+            ms_f, _ = time_graph(g_f, R, args.steps, args.warmup)
+            extra["step_us_forced_sink4_recent64"] = round(ms_f * 1e3, 3)
+            log("[bench] forced (4 sinks, 64 recent): %.2f us" % (ms_f * 1e3))
+            del g_f
         # full-cache key encode (prefill) pass, cold rotation
         g_enc = graph_of(lambda c: A.encode_keys(c[1], kv_len, c[3]), copies[:16])
         ms_enc, _ = time_graph(g_enc, 16, 64, 16)

@@ -150,6 +150,49 @@ adamas_status adamas_append_decode_step(const adamas_dims* d, const void* q, con
                                         uint16_t* dist, uint8_t* q_codes, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/*
+ * Positions a decode step always selects, whatever their distance.  The blog
+ * (section 3.2, precision tuning; section 6, practice advice) keeps special
+ * tokens such as a leading [CLS] at full attention; the paper builds on the
+ * attention-sink work (the mlsanity.com citation map lists it), whose first
+ * tokens are always attended; a window of the latest tokens is the usual
+ * companion.  For a position p < kv_len[b]:
+ *   always kept   p < sink, or p >= kv_len[b] - recent;
+ *   preferred     (mask != NULL) bit p % 32 of mask[b * mask_words + p / 32] set.
+ *   sink, recent  >= 0 with sink + recent <= budget (so the always-kept
+ *                 positions fit the budget)
+ *   mask          optional device bitmap uint32 [batch][mask_words], 4-byte
+ *                 aligned; bits at p >= kv_len[b] are ignored
+ *   mask_words    words per batch entry, >= ceil(capacity / 32) when mask != NULL
+ */
+typedef struct adamas_forced {
+  int32_t sink;
+  int32_t recent;
+  const uint32_t* mask;
+  int32_t mask_words;
+} adamas_forced;
+
+/*
+ * The decode step with forced positions.  The k_b = min(budget, kv_len[b])
+ * selected positions are, in this order of preference: every always-kept
+ * position; the preferred positions, lower positions first; then the other
+ * positions by (dist, position).  So the sinks and the window are always
+ * attended, every special token of the mask is too whenever they fit the rest
+ * of the budget (the lowest ones otherwise), and what remains goes to the
+ * closest other positions.  With sink = recent = 0 and mask = NULL the result is
+ * adamas_decode_step's (append = 0) or adamas_append_decode_step's (append = 1).
+ * `dist` still reports the plain Manhattan distances.  Arguments, layouts,
+ * workspace size and errors as adamas_append_decode_step (codes are written
+ * only when append = 1), plus INVALID_ARGUMENT for a NULL `forced`, append not
+ * 0 or 1, sink or recent < 0, sink + recent > budget, or a misaligned or too
+ * narrow mask.
+ */
+adamas_status adamas_forced_decode_step(const adamas_dims* d, const adamas_forced* forced, int32_t append,
+                                        const void* q, const void* k, const void* v, uint8_t* codes,
+                                        const int32_t* kv_len, int32_t budget, float scale, float* out,
+                                        int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace dense_decode_attention needs (0 if the dims are invalid). */
 size_t dense_decode_workspace_size(const adamas_dims* d);
 
@@ -169,8 +212,9 @@ adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const 
  * CALLING THREAD: launch i of a call (counting from 0) is bracketed by the HIP
  * events events[2*i] (start) and events[2*i+1] (stop), recorded on the call's
  * stream by the kernel dispatch itself, for every i with 2*i+1 < n_events.
- * Launch order: adamas_encode_keys -> 0 encode; adamas_decode_step and
- * adamas_append_decode_step -> 0 scan, 1 select+attend; dense_decode_attention ->
+ * Launch order: adamas_encode_keys -> 0 encode; adamas_decode_step,
+ * adamas_append_decode_step and adamas_forced_decode_step -> 0 scan, 1
+ * select+attend; dense_decode_attention ->
  * 0 attend, 1 combine.  While timing is on, a call waits (on the host) for each
  * of its kernels before launching the next, so that every event pair brackets
  * one kernel and not the dispatch gap after the previous one.

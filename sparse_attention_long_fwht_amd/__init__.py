@@ -36,6 +36,11 @@ class Dims(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
+class Forced(ctypes.Structure):
+    _fields_ = [("sink", ctypes.c_int32), ("recent", ctypes.c_int32), ("mask", ctypes.c_void_p),
+                ("mask_words", ctypes.c_int32)]
+
+
 _vp = ctypes.c_void_p
 _dims_p = ctypes.POINTER(Dims)
 _lib.adamas_encode_keys.argtypes = [_dims_p, _vp, _vp, _vp, _vp, _vp]
@@ -47,6 +52,10 @@ _lib.adamas_decode_step.argtypes = [_dims_p, _vp, _vp, _vp, _vp, _vp, ctypes.c_i
 _lib.adamas_decode_step.restype = ctypes.c_int
 _lib.adamas_append_decode_step.argtypes = _lib.adamas_decode_step.argtypes
 _lib.adamas_append_decode_step.restype = ctypes.c_int
+_lib.adamas_forced_decode_step.argtypes = [_dims_p, ctypes.POINTER(Forced), ctypes.c_int32, _vp, _vp, _vp, _vp, _vp,
+                                           ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                           _vp]
+_lib.adamas_forced_decode_step.restype = ctypes.c_int
 _lib.dense_decode_workspace_size.argtypes = [_dims_p]
 _lib.dense_decode_workspace_size.restype = ctypes.c_size_t
 _lib.dense_decode_attention.argtypes = [_dims_p, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
@@ -60,8 +69,8 @@ _lib.adamas_abi_version.argtypes = []
 _lib.adamas_abi_version.restype = ctypes.c_int32
 
 EXPORTED_SYMBOLS = ("adamas_encode_keys", "adamas_decode_workspace_size", "adamas_decode_step",
-                    "adamas_append_decode_step", "dense_decode_workspace_size", "dense_decode_attention", "adamas_profile_events",
-                    "adamas_status_string", "adamas_abi_version")
+                    "adamas_append_decode_step", "adamas_forced_decode_step", "dense_decode_workspace_size",
+                    "dense_decode_attention", "adamas_profile_events", "adamas_status_string", "adamas_abi_version")
 
 
 class AdamasError(RuntimeError):
@@ -132,22 +141,30 @@ def alloc_workspace(nbytes, device=None):
 
 
 def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=None, dist=None, q_codes=None,
-                stream=None, append=False):
+                stream=None, append=False, sink=None, recent=None, mask=None):
     """One Adamas decode step; writes out [B][Hq][128] fp32 (and the optional outputs).
 
     append=True calls adamas_append_decode_step: the key at kv_len[b]-1 is
-    encoded into `codes` first (no separate encode launch)."""
+    encoded into `codes` first (no separate encode launch).  Any of sink /
+    recent / mask (int32 [B][words] device bitmap, bit p % 32 of word p / 32)
+    calls adamas_forced_decode_step with those forced positions."""
     B, Hq, hd = q.shape
     _, Hkv, cap, _ = k.shape
     d = dims(B, Hq, Hkv, cap, hd)
-    fn = _lib.adamas_append_decode_step if append else _lib.adamas_decode_step
-    st = fn(ctypes.byref(d), _ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2),
-                                 _ptr(codes, "codes", 1), _ptr(kv_len, "kv_len", 4), int(budget), float(scale),
-                                 _ptr(out, "out", 4), _ptr(sel_idx, "sel_idx", 4, optional=True),
-                                 _ptr(dist, "dist", 2, optional=True), _ptr(q_codes, "q_codes", 1, optional=True),
-                                 _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                                 _stream(stream))
-    _check(st, "adamas_append_decode_step" if append else "adamas_decode_step")
+    tail = (_ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2), _ptr(codes, "codes", 1), _ptr(kv_len, "kv_len", 4),
+            int(budget), float(scale), _ptr(out, "out", 4), _ptr(sel_idx, "sel_idx", 4, optional=True),
+            _ptr(dist, "dist", 2, optional=True), _ptr(q_codes, "q_codes", 1, optional=True),
+            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    if sink is None and recent is None and mask is None:
+        fn = _lib.adamas_append_decode_step if append else _lib.adamas_decode_step
+        _check(fn(ctypes.byref(d), *tail), "adamas_append_decode_step" if append else "adamas_decode_step")
+        return
+    if mask is not None and mask.dim() != 2:
+        raise ValueError("mask must be [batch][words]")
+    f = Forced(int(sink or 0), int(recent or 0), _ptr(mask, "mask", 4, optional=True),
+               0 if mask is None else int(mask.shape[1]))
+    st = _lib.adamas_forced_decode_step(ctypes.byref(d), ctypes.byref(f), 1 if append else 0, *tail)
+    _check(st, "adamas_forced_decode_step")
 
 
 def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None):

@@ -87,12 +87,20 @@ size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget) {
 namespace {
 
 adamas_status decode_common(const adamas_dims* d, const void* q, const void* k, const void* v, uint8_t* codes,
-                            bool append, const int32_t* kv_len, int32_t budget, float scale, float* out,
-                            int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            bool append, const adamas_forced* forced, const int32_t* kv_len, int32_t budget,
+                            float scale, float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   adamas_status st = check_dims(d, true);
   if (st != ADAMAS_OK) return st;
   if (!q || !k || !v || !codes || !kv_len || !out || budget < 1) return ADAMAS_ERR_INVALID_ARGUMENT;
+  adamas::Forced f{0, 0, nullptr, 0};
+  if (forced) {
+    if (forced->sink < 0 || forced->recent < 0 || (int64_t)forced->sink + forced->recent > budget)
+      return ADAMAS_ERR_INVALID_ARGUMENT;
+    if (forced->mask && (!aligned(forced->mask, 4) || (int64_t)forced->mask_words * 32 < d->capacity))
+      return ADAMAS_ERR_INVALID_ARGUMENT;
+    f = adamas::Forced{forced->sink, forced->recent, forced->mask, forced->mask ? forced->mask_words : 0};
+  }
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(codes, 16) || !aligned(kv_len, 4) ||
       !aligned(out, 4) || (sel_idx && !aligned(sel_idx, 4)) || (dist && !aligned(dist, 2)) ||
       (q_codes && !aligned(q_codes, 4)))
@@ -101,7 +109,7 @@ adamas_status decode_common(const adamas_dims* d, const void* q, const void* k, 
   if (!p.supported) return ADAMAS_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return ADAMAS_ERR_WORKSPACE;
   hipError_t e = adamas::launch_decode(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                       static_cast<const uint16_t*>(v), codes, append, kv_len, scale, out, sel_idx,
+                                       static_cast<const uint16_t*>(v), codes, append, f, kv_len, scale, out, sel_idx,
                                        dist, q_codes, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
 }
@@ -115,16 +123,26 @@ adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void
                                  float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   // codes are only read on this path
-  return decode_common(d, q, k, v, const_cast<uint8_t*>(codes), false, kv_len, budget, scale, out, sel_idx, dist,
-                       q_codes, workspace, workspace_bytes, stream);
+  return decode_common(d, q, k, v, const_cast<uint8_t*>(codes), false, nullptr, kv_len, budget, scale, out, sel_idx,
+                       dist, q_codes, workspace, workspace_bytes, stream);
 }
 
 adamas_status adamas_append_decode_step(const adamas_dims* d, const void* q, const void* k, const void* v,
                                         uint8_t* codes, const int32_t* kv_len, int32_t budget, float scale,
                                         float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(d, q, k, v, codes, true, kv_len, budget, scale, out, sel_idx, dist, q_codes, workspace,
-                       workspace_bytes, stream);
+  return decode_common(d, q, k, v, codes, true, nullptr, kv_len, budget, scale, out, sel_idx, dist, q_codes,
+                       workspace, workspace_bytes, stream);
+}
+
+adamas_status adamas_forced_decode_step(const adamas_dims* d, const adamas_forced* forced, int32_t append,
+                                        const void* q, const void* k, const void* v, uint8_t* codes,
+                                        const int32_t* kv_len, int32_t budget, float scale, float* out,
+                                        int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (!forced || (append != 0 && append != 1)) return ADAMAS_ERR_INVALID_ARGUMENT;
+  return decode_common(d, q, k, v, codes, append != 0, forced, kv_len, budget, scale, out, sel_idx, dist, q_codes,
+                       workspace, workspace_bytes, stream);
 }
 
 size_t dense_decode_workspace_size(const adamas_dims* d) {

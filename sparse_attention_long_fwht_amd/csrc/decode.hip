@@ -24,6 +24,12 @@
 //                      P.V).  With several splits each block takes a slice of the
 //                      selection and the last one merges the slices' (m, l, o)
 //                      partials.
+//
+// Forced positions (sinks, a recent window, a caller bitmap; the blog's
+// sections 3.2 and 6 keep special tokens at full attention) need no change past
+// the scan: the scan ranks by a key that is 0 for a forced position and distance
+// + 1 for the others, so forced positions come first, in position order, and the
+// others follow by (distance, position).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -106,17 +112,20 @@ __device__ __forceinline__ void encode_wave(uint32_t qlo_bits, uint32_t qhi_bits
 // Per (query head, chunk) the scan leaves two things in the workspace:
 //   sorted[slot]  chunk-local positions ordered by distance (any order inside a
 //                 distance), kept only for distances <= localk, where localk is
-//                 the smallest distance with at least kk = min(k_eff, n_c)
+//                 the smallest distance with at least kk = min(k, n_c)
 //                 positions at or below it (n_c = positions in the chunk);
 //   record        dmin, localk, complete (kk == n_c), n_c, a zero (cum(dmin - 1)),
 //                 then the cumulative count cum(d) for d = dmin .. localk.
-// The k_eff smallest distances overall never go past localk of a chunk that is
-// not complete (that chunk alone has kk = k_eff positions at or below localk),
+// (k = the ranked budget, k_eff less the always-kept positions; distances
+// mean selection keys.)  The k smallest distances overall never go past localk
+// of a chunk that is not complete (that chunk alone has kk = k positions at or
+// below localk),
 // and a complete chunk keeps all of its positions; so the records determine the
 // threshold and the sorted prefixes hold every selected position.
 
 constexpr int kScanThreads = 512;  // one key per thread per pass
-constexpr int kHistBins = 7 * 64;  // bins as scanned by one wave: 7 per lane (385 used)
+constexpr int kHistBins = 7 * 64;  // bins as scanned by one wave: 7 per lane (up to kMaxKey + 1 used)
+static_assert(kHistBins > kMaxKey, "every selection key has a bin");
 constexpr int kScanPasses = kScanMaxChunk / kScanThreads;
 
 struct ScanArgs {
@@ -129,7 +138,10 @@ struct ScanArgs {
   uint16_t* dist_out;  // optional [B][Hq][cap]
   uint8_t* q_codes;    // optional [B][Hq][32]
   uint32_t* counters;  // [B][Hq], cleared here for select_attend_kernel
+  const uint32_t* fmask;  // optional [B][fmask_words] bitmap of forced positions
   int Hq, Hkv, cap, chunk, nch, budget, append;
+  int sink, recent;    // always-kept sinks and recent window (not ranked)
+  int fmask_words;     // (sink, recent, fmask: scan_kernel<R, true> only)
 };
 
 // Blocks are dealt to the eight XCDs round-robin by linear block index.  When
@@ -137,7 +149,9 @@ struct ScanArgs {
 // same XCD, so the group's query rows are fetched into one L2 only.
 constexpr int kXcds = 8;
 
-template <int R>
+// kForced: sinks / recent window / special tokens in use (a separate
+// instantiation, so that the plain step pays nothing for them).
+template <int R, bool kForced>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int G = (int)gridDim.x / a.nch;  // (b, kv head) groups
   int bg, c;
@@ -169,7 +183,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   uint4 klo = cbase[(size_t)p * 2];
   uint4 khi = cbase[(size_t)p * 2 + 1];
 
-  __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins 385.. stay 0)
+  __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins past kMaxKey stay 0)
   __shared__ uint32_t s_code[R + 1][8];      // query codes, then the appended key's
   __shared__ uint32_t s_limit[R];                    // sorted slots kept per head
   __shared__ uint32_t s_recw[R];                     // 16-byte words of each head's record
@@ -207,6 +221,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __syncthreads();
   if (p0 >= len) return;
   const int p1 = min(p0 + a.chunk, len);
+  // The sinks [0, s_b) and the recent window [len - r_b, len) are always kept
+  // and take no part in the ranking: the chunk ranks its share [m0, m1) (maybe
+  // empty) of the middle, for the k_mid = k_eff - s_b - r_b remaining slots.
+  const int s_b = kForced ? min(a.sink, len) : 0, r_b = kForced ? min(a.recent, len - s_b) : 0;
+  const int m0 = kForced ? max(p0, s_b) : p0, m1 = kForced ? min(p1, len - r_b) : p1;
+  const int k_mid = min(a.budget, len) - s_b - r_b;  // >= 0: sink + recent <= budget
 
   // thermometer words of the query codes: t1 = lo|hi, t2 = hi, t3 = lo&hi
   uint32_t qt[R][12];
@@ -221,9 +241,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       qt[r][8 + w] = lo & hi;
     }
 
-  // distances; each (key, head) takes the next rank in its distance's bin.
-  // The next pass's codes are loaded while this pass computes.
-  uint32_t dr[kScanPasses][R];  // (distance << 16) | rank inside the bin
+  // special tokens (kForced with a mask): the caller's bitmap words of every
+  // pass, requested before the first wait on the key codes
+  uint32_t fw[kScanPasses];
+#pragma unroll
+  for (int pass = 0; pass < kScanPasses; ++pass) {
+    fw[pass] = 0u;
+    if (kForced && a.fmask && p0 + pass * kScanThreads < p1)
+      fw[pass] = a.fmask[(size_t)b * a.fmask_words + ((min(p0 + pass * kScanThreads + tid, p1 - 1)) >> 5)];
+  }
+
+  // selection keys (the distance; with kForced 0 for a special token and
+  // distance + 1 for the others); each ranked (key, head) takes the next rank
+  // in its key's bin.  The next pass's codes are loaded while this pass
+  // computes.
+  uint32_t dr[kScanPasses][R];  // (key << 16) | rank inside the bin
 #pragma unroll
   for (int pass = 0; pass < kScanPasses; ++pass) {
     const int base = p0 + pass * kScanThreads;
@@ -242,6 +274,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
         }
         // |a - b| summed over coordinates = popcount of the three thermometer
         // XORs (t1 = lo|hi, t2 = hi, t3 = lo&hi) over the 128 coordinates
+        const bool ranked = !kForced || (p >= m0 && p < m1);
+        const bool special = kForced && ((fw[pass] >> (p & 31)) & 1u);
         const uint32_t lo[4] = {klo.x, klo.y, klo.z, klo.w};
         const uint32_t hi[4] = {khi.x, khi.y, khi.z, khi.w};
         uint32_t t1[4], t3[4];
@@ -259,7 +293,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
             d += __builtin_popcount(hi[w] ^ qt[r][4 + w]);
             d += __builtin_popcount(t3[w] ^ qt[r][8 + w]);
           }
-          dr[pass][r] = (d << 16) | atomicAdd(&s_hist[r][d], 1u);
+          const uint32_t key = kForced ? (special ? 0u : d + 1u) : d;
+          if (ranked) dr[pass][r] = (key << 16) | atomicAdd(&s_hist[r][key], 1u);
           if (a.dist_out) a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + p] = (uint16_t)d;
         }
       }
@@ -269,9 +304,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   }
   __syncthreads();
 
-  // per head (wave r): bin offsets, dmin, localk, and the record
-  const int n_c = p1 - p0;
-  const int kk = min(min(a.budget, len), n_c);
+  // per head (wave r): bin offsets, dmin, localk, and the record.  A chunk
+  // with nothing to rank gets dmin = localk = kMaxKey, complete, n = 0.
+  const int n_c = max(m1 - m0, 0);
+  const int kk = min(k_mid, n_c);
   if (wave < R) {
     // (branch-free: selects instead of a search loop; cross-lane reads in
     // uniform code only -- a value read from lane lk must have been computed
@@ -279,7 +315,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     const int r = wave;
     uint32_t cnt[7], cum[7], loc = 0;
 #pragma unroll
-    for (int j = 0; j < 7; ++j) cnt[j] = s_hist[r][7 * lane + j];  // bins past 384 are zero
+    for (int j = 0; j < 7; ++j) cnt[j] = s_hist[r][7 * lane + j];  // bins past kMaxKey are zero
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       loc += cnt[j];
@@ -287,7 +323,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     }
     const uint32_t inc = wave_inclusive_scan_u32(loc);
     const uint32_t base = inc - loc;
-    const int lmin = __builtin_ffsll((long long)__ballot(loc > 0)) - 1;            // n_c >= 1
+    const int lmin = __builtin_ffsll((long long)__ballot(loc > 0)) - 1;            // -1 if n_c == 0
     const int lk = __builtin_ffsll((long long)__ballot(inc >= (uint32_t)kk)) - 1;  // total n_c >= kk
     int fj = 7, kj = 7;  // this lane's first non-empty bin and first bin reaching kk
 #pragma unroll
@@ -301,8 +337,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       lim_l = j == kj ? base + cum[j] : lim_l;
       s_hist[r][7 * lane + j] = base + cum[j] - cnt[j];  // exclusive offset of the bin
     }
-    const int dmin = 7 * lmin + __builtin_amdgcn_readlane(fj, lmin);
-    const int localk = 7 * lk + __builtin_amdgcn_readlane(kj, lk);
+    const int dmin = n_c > 0 ? 7 * lmin + __builtin_amdgcn_readlane(fj, max(lmin, 0)) : kMaxKey;
+    // (kk == 0 finds bin 0: localk is then taken as dmin, which keeps the record
+    // well formed; nothing of the chunk is selected)
+    const int localk = max(7 * lk + __builtin_amdgcn_readlane(kj, lk), dmin);
     const uint32_t limit = (uint32_t)__builtin_amdgcn_readlane((int)lim_l, lk);
     uint16_t* rec = s_rec[r];
     if (lane == 0) {
@@ -331,7 +369,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 #pragma unroll
   for (int pass = 0; pass < kScanPasses; ++pass) {
     const int pp = p0 + pass * kScanThreads + tid;
-    if (p0 + pass * kScanThreads < p1 && pp < p1) {
+    if (p0 + pass * kScanThreads < p1 && pp < p1 && (!kForced || (pp >= m0 && pp < m1))) {
 #pragma unroll
       for (int r = 0; r < R; ++r) dr[pass][r] = s_hist[r][dr[pass][r] >> 16] + (dr[pass][r] & 0xFFFFu);
     }
@@ -339,7 +377,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 #pragma unroll
   for (int pass = 0; pass < kScanPasses; ++pass) {
     const int pp = p0 + pass * kScanThreads + tid;
-    if (p0 + pass * kScanThreads < p1 && pp < p1) {
+    if (p0 + pass * kScanThreads < p1 && pp < p1 && (!kForced || (pp >= m0 && pp < m1))) {
 #pragma unroll
       for (int r = 0; r < R; ++r) s_sorted[r * a.chunk + dr[pass][r]] = (uint16_t)(pp - p0);
     }
@@ -382,6 +420,7 @@ struct SelAttArgs {
   float qscale;            // softmax scale * log2(e)
   int Hq, Hkv, R, cap, budget, chunk, nch, rec_win, pre_slots, splits, rows_per_split, bitmap_words;
   int early_prefetch;  // speculative prefetch of the likely rows right after the record loads
+  int sink, recent;    // always-kept sinks and recent window
 };
 
 constexpr int kSAThreads = 512;
@@ -417,11 +456,11 @@ __device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t* 
 }
 
 // A record header as read, clamped so that no content of the workspace can
-// lead the block out of bounds: dmin <= localk <= 384, complete 0 or 1, n at
+// lead the block out of bounds: dmin <= localk <= kMaxKey, complete 0 or 1, n at
 // most the chunk's length.
 __device__ __forceinline__ uint2 sanitize_hdr(uint32_t x, uint32_t y, int n_true) {
-  const uint32_t dm = min(x & 0xFFFFu, 384u);
-  const uint32_t lk = min(max(x >> 16, dm), 384u);
+  const uint32_t dm = min(x & 0xFFFFu, (uint32_t)kMaxKey);
+  const uint32_t lk = min(max(x >> 16, dm), (uint32_t)kMaxKey);
   const uint32_t n = min(y >> 16, (uint32_t)n_true);
   return make_uint2(dm | (lk << 16), ((y & 0xFFFFu) ? 1u : 0u) | (n << 16));
 }
@@ -522,6 +561,25 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   const uint16_t* grec = a.rec + (size_t)bh * a.nch * kRecStride;
   const uint16_t* gsorted = a.sorted + (size_t)bh * a.nch * a.chunk;
   const int k_eff = min(a.budget, len);
+  // Final ranks (ascending positions): the sinks [0, s_b), then the k_mid
+  // ranked positions, then the recent window; the ranking below works on
+  // ranks of the middle (the scan left sinks and window out of it).
+  const int s_b = min(a.sink, len), r_b = min(a.recent, len - s_b);
+  const int k_mid = k_eff - s_b - r_b;
+  const int lo_rank = split * a.rows_per_split;
+  const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
+  const int mlo = lo_rank - s_b, mhi = hi_rank - s_b;  // this split's window of middle ranks
+  const uint16_t* Kg = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
+  const uint16_t* Vg = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
+  // the split's always-kept row of this thread (-1: none): known from kv_len
+  // alone, so its K/V lines are requested with the first record loads (into
+  // pe, which the speculative prefetch below then leaves to this row)
+  int forced_pos = -1;
+  if (a.sink > 0 || a.recent > 0) {
+    const int i = lo_rank + tid, j = i - s_b;
+    if (i < hi_rank && (j < 0 || j >= k_mid)) forced_pos = j < 0 ? i : len - r_b + (j - k_mid);
+  }
+  uint32_t pe[4] = {0u, 0u, 0u, 0u};
   const int nch_b = (len + a.chunk - 1) >> __builtin_ctz(a.chunk);  // chunk is a power of two
   {
     // 16-byte words per chunk: record window and sorted prefix (powers of two)
@@ -542,6 +600,13 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
         const int cc = i >> per_log2, j = i & (per - 1);
         t[u] = *reinterpret_cast<const uint4*>(grec + (size_t)cc * kRecStride + 8 * j);
+      }
+      if (i0 == 0 && forced_pos >= 0) {  // (issued after the records: their waits do not include these)
+        const size_t row = (size_t)forced_pos * kHeadDim;
+        pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
+        pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
+        pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
+        pe[3] = *reinterpret_cast<const uint32_t*>(Vg + row + 64);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -565,17 +630,12 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // The exact rows are prefetched again after E; the words are read only at
   // the block's end, so nothing waits for these loads.  Only where the rows
   // stay in L2 until used (a few heads, one block each: plan.h).
-  const int lo_rank = split * a.rows_per_split;
-  const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
-  const uint16_t* Kg = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
-  const uint16_t* Vg = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
-  uint32_t pe[4] = {0u, 0u, 0u, 0u};
-  if (a.early_prefetch && k_eff > 0) {
+  if (a.early_prefetch && k_mid > 0 && max(mlo, 0) < min(mhi, k_mid)) {
     int ulog = 0;  // U = 1 << ulog
-    while ((1 << ulog) < a.pre_slots && (nch_b << ulog) < k_eff) ++ulog;
-    const int cs0 = (int)((int64_t)lo_rank * nch_b / k_eff);
-    const int cs1 = min(nch_b, (int)(((int64_t)hi_rank * nch_b + k_eff - 1) / k_eff) + 1);
-    if (tid < ((cs1 - cs0) << ulog)) {
+    while ((1 << ulog) < a.pre_slots && (nch_b << ulog) < k_mid) ++ulog;
+    const int cs0 = (int)((int64_t)max(mlo, 0) * nch_b / k_mid);
+    const int cs1 = min(nch_b, (int)(((int64_t)min(mhi, k_mid) * nch_b + k_mid - 1) / k_mid) + 1);
+    if (tid < ((cs1 - cs0) << ulog) && forced_pos < 0) {
       const int cc = cs0 + (tid >> ulog), j = tid & ((1 << ulog) - 1);
       const int lp = min((int)s_pre[(size_t)cc * a.pre_slots + j], min(a.chunk, len - cc * a.chunk) - 1);
       const size_t row = (size_t)(cc * a.chunk + lp) * kHeadDim;
@@ -669,13 +729,13 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
       if constexpr (kTwo) acc1 += cu[min(max(d1 - dm, -1), wd)];
     }
   };
-  int T = 385;
+  int T = kMaxKey + 1;
   uint32_t g_before = 0;  // G'(T - 1)
   {
-    int base = lo - 1;   // G'(lo - 1) = 0 < k_eff
+    int base = lo - 1;   // G'(lo - 1) = 0 (< k_mid unless k_mid = 0: then T = lo - 1)
     uint32_t carry = 0;  // G'(base - 1)
 #pragma unroll 1
-    for (int round = 0; base <= 384; ++round) {
+    for (int round = 0; base <= kMaxKey; ++round) {
       const bool two = hi - base >= 64;
       const int d0 = base + lane, d1 = d0 + 64;
       uint32_t acc0 = 0, acc1 = 0;
@@ -701,8 +761,8 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         g0 += s_part[w][0][lane];
         g1 += s_part[w][1][lane];
       }
-      const uint64_t r0 = __ballot(g0 >= (uint32_t)k_eff);
-      const uint64_t r1 = two ? __ballot(g1 >= (uint32_t)k_eff) : 0ull;
+      const uint64_t r0 = __ballot(g0 >= (uint32_t)k_mid);
+      const uint64_t r1 = two ? __ballot(g1 >= (uint32_t)k_mid) : 0ull;
       const uint32_t g0_last = (uint32_t)__builtin_amdgcn_readlane((int)g0, 63);
       if (r0 | r1) {  // (wave-uniform)
         const int jj = r0 ? 0 : 1;
@@ -714,10 +774,10 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
       }
       carry = two ? (uint32_t)__builtin_amdgcn_readlane((int)g1, 63) : g0_last;
       base += two ? 128 : 64;
-      g_before = carry;  // (kept if no candidate up to 384 reaches k_eff: contradictory records)
+      g_before = carry;  // (kept if no candidate up to kMaxKey reaches k_mid: contradictory records)
     }
   }
-  const uint32_t quota = (uint32_t)k_eff - min(g_before, (uint32_t)k_eff);
+  const uint32_t quota = (uint32_t)k_mid - min(g_before, (uint32_t)k_mid);
 
   // ---- E. per chunk (every wave, lane l: chunks l and 64 + l): lt =
   // positions below T (slots [0, lt) of its sorted prefix) and m = lt + its
@@ -762,7 +822,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     const int cc = 64 * gi + lane;
     const uint4 c = ci[gi];
     const uint32_t kept = c.y + min(c.x - c.y, quota > c.w ? quota - c.w : 0u);  // lt + kept ties
-    const bool mine = cc < nch_b && kept > 0u && (int)c.z < hi_rank && (int)(c.z + kept) > lo_rank;
+    const bool mine = cc < nch_b && kept > 0u && (int)c.z < mhi && (int)(c.z + kept) > mlo;
     const uint64_t mb = __ballot(mine);
     if (mb) {
       c_lo = min(c_lo, 64 * gi + __builtin_ctzll(mb));
@@ -786,8 +846,8 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     // ---- F. every chunk's m entries in one group of S >= m lanes, sorted by
     // position (key = 2 * position + [at T]); a tie is kept while its rank
     // among all ties stays below the quota; ranks by ballot.
-    const SortedEmit e{{ci[0], ci[1]}, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, len, quota, lo_rank, hi_rank,
-                       c_lo, c_hi, s_list, a.sel_idx ? a.sel_idx + (size_t)bh * a.budget : nullptr};
+    const SortedEmit e{{ci[0], ci[1]}, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, len, quota, mlo, mhi,
+                       c_lo, c_hi, s_list, a.sel_idx ? a.sel_idx + (size_t)bh * a.budget + s_b : nullptr};
     if (max_m <= 1) emit_sorted<1>(e);
     else if (max_m <= 2) emit_sorted<2>(e);
     else if (max_m <= 4) emit_sorted<4>(e);
@@ -840,7 +900,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     block_scan2(nk, nt, s_wsum, kb, tb, ktot, ttot);
     uint32_t tie_left = tb >= quota ? 0u : min(nt, quota - tb);  // this thread's kept ties
     uint32_t r = kb + min(tb, quota);
-    if ((int)r < hi_rank && (int)(r + nk + tie_left) > lo_rank) {
+    if ((int)r < mhi && (int)(r + nk + tie_left) > mlo) {
       for (int w = w0; w < w1; ++w) {
         uint32_t tw = s_tie[w];
         uint32_t ties_kept = 0;
@@ -854,15 +914,27 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         while (bits) {
           const int bit = __builtin_ctz(bits);
           bits &= bits - 1;
-          if ((int)r >= lo_rank && (int)r < hi_rank) {
+          if ((int)r >= mlo && (int)r < mhi) {
             const int pp = 32 * w + bit;
-            s_list[r - lo_rank] = pp;
-            if (a.sel_idx) a.sel_idx[(size_t)bh * a.budget + r] = pp;
+            s_list[r - mlo] = pp;
+            if (a.sel_idx) a.sel_idx[(size_t)bh * a.budget + s_b + r] = pp;
           }
           ++r;
         }
       }
     }
+  }
+  // the always-kept rows of this split: sinks first, the window last
+  if (forced_pos >= 0) {
+    s_list[tid] = forced_pos;
+    if (a.sel_idx) a.sel_idx[(size_t)bh * a.budget + lo_rank + tid] = forced_pos;
+  }
+  for (int i = lo_rank + kSAThreads + tid; i < hi_rank; i += kSAThreads) {  // (splits over 512 rows)
+    const int j = i - s_b;
+    if (j >= 0 && j < k_mid) continue;
+    const int pp = j < 0 ? i : len - r_b + (j - k_mid);
+    s_list[i - lo_rank] = pp;
+    if (a.sel_idx) a.sel_idx[(size_t)bh * a.budget + i] = pp;
   }
   if (a.sel_idx && split == 0) {
     for (int i = k_eff + tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
@@ -1057,34 +1129,41 @@ static void launch_k(int i, Kernel kernel, dim3 grid, dim3 block, uint32_t shmem
     hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
 }
 
-template <int R>
+template <int R, bool kForced>
 static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
   const uint32_t shmem = (uint32_t)(R * p.chunk * sizeof(uint16_t));  // sorted slots, staged
   if (shmem > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<R>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<R, kForced>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  launch_k(0, scan_kernel<R>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), shmem, s, sa);
+  launch_k(0, scan_kernel<R, kForced>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), shmem, s, sa);
   return hipSuccess;
 }
 
+template <int R>
+static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, bool forced, hipStream_t s) {
+  return forced ? launch_scan<R, true>(p, sa, s) : launch_scan<R, false>(p, sa, s);
+}
+
 hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* codes,
-                         bool append, const int32_t* kv_len, float scale, float* out, int32_t* sel_idx,
-                         uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s) {
+                         bool append, const Forced& f, const int32_t* kv_len, float scale, float* out,
+                         int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s) {
   uint16_t* ws_sorted = reinterpret_cast<uint16_t*>(ws + p.off_sorted);
   uint16_t* ws_rec = reinterpret_cast<uint16_t*>(ws + p.off_rec);
   float* ws_part = reinterpret_cast<float*>(ws + p.off_part);
   uint32_t* counters = reinterpret_cast<uint32_t*>(ws + p.off_count);
 
+  const bool forced = f.sink > 0 || f.recent > 0 || f.mask != nullptr;
   ScanArgs sa{q,       k,     codes,   kv_len, ws_sorted, ws_rec,   dist,          q_codes,
-              counters, p.Hq, p.Hkv, p.cap, p.chunk,   p.nch,    p.budget, append ? 1 : 0};
+              counters, f.mask, p.Hq, p.Hkv, p.cap, p.chunk,   p.nch,    p.budget, append ? 1 : 0,
+              f.sink, f.recent, f.mask_words};
   hipError_t es = hipErrorInvalidValue;
   switch (p.R) {
-    case 1: es = launch_scan<1>(p, sa, s); break;
-    case 2: es = launch_scan<2>(p, sa, s); break;
-    case 4: es = launch_scan<4>(p, sa, s); break;
-    case 8: es = launch_scan<8>(p, sa, s); break;
+    case 1: es = launch_scan<1>(p, sa, forced, s); break;
+    case 2: es = launch_scan<2>(p, sa, forced, s); break;
+    case 4: es = launch_scan<4>(p, sa, forced, s); break;
+    case 8: es = launch_scan<8>(p, sa, forced, s); break;
   }
   if (es != hipSuccess) return es;
   // In timing mode the select/attend kernel waits for the scan on the host, so
@@ -1096,7 +1175,8 @@ hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, co
   }
   SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
                 scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch, p.rec_win,
-                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words, p.early_prefetch ? 1 : 0};
+                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words, p.early_prefetch ? 1 : 0,
+                f.sink, f.recent};
   if (p.lds_select > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_attend_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_select);

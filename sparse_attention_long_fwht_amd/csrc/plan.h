@@ -9,7 +9,10 @@ namespace adamas {
 
 constexpr int kHeadDim = 128;
 constexpr int kCodeBytes = 32;
-constexpr int kBins = 385;        // distances 0..384 (128 coordinates x largest code gap 3)
+constexpr int kMaxDist = 384;     // distances 0..384 (128 coordinates x largest code gap 3)
+// Selection keys: the distance, or -- when positions are forced -- 0 for a
+// forced position and distance + 1 for the others: 0..385.
+constexpr int kMaxKey = kMaxDist + 1;
 // Sparse path: chunks of the scan (one block per (b, kv head, chunk)).
 constexpr int kScanMinChunk = 512;   // = threads of the scan block: one key per thread per pass
 constexpr int kScanMaxChunk = 4096;  // at most eight passes per block
@@ -18,7 +21,9 @@ constexpr int64_t kScanBlocks = 256;   // scan blocks wanted at most: one per co
 constexpr int64_t kMaxCapacity = 524288;  // positions per (b, kv head)
 constexpr int kSelMaxChunks = 128;  // chunks per (b, kv head) at most: kMaxCapacity / kScanMaxChunk
 constexpr int kRecHead = 5;          // record words before cum(dmin): dmin, localk, complete, n, zero
-constexpr int kRecStride = 392;      // u16 per (head, chunk) record: kRecHead + up to 385 counts, padded
+constexpr int kRecStride = 392;      // u16 per (head, chunk) record: kRecHead + up to 386 counts, padded
+static_assert(kRecHead + kMaxKey + 1 <= kRecStride - 1, "the record's last word is padding");
+static_assert(kRecStride % 8 == 0, "records are copied in 16-byte words");
 // Dense baseline: chunks of the split-K attention.
 constexpr int kMaxChunks = 128;      // dense chunks per (b, kv head)
 constexpr int kPartFloats = 132;     // m, l, 2 pad, o[128]
@@ -148,12 +153,20 @@ ProfileEvents& profile_events();  // this thread's setting
 hipError_t launch_encode_keys(int B, int Hkv, int cap, const uint16_t* k, const int32_t* start,
                               const int32_t* end, uint8_t* codes, hipStream_t s);
 
+// Forced positions of a decode step: p < sink, p >= kv_len[b] - recent, or bit
+// p % 32 of mask[b * mask_words + p / 32] (mask may be null).  All zero: none.
+struct Forced {
+  int sink, recent;
+  const uint32_t* mask;
+  int mask_words;
+};
+
 // `append`: first encode the key at position kv_len[b]-1 of every (b, kv head)
 // into `codes` (the scan block holding that position does it); otherwise codes
 // are only read.
 hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* codes,
-                         bool append, const int32_t* kv_len, float scale, float* out, int32_t* sel_idx,
-                         uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s);
+                         bool append, const Forced& f, const int32_t* kv_len, float scale, float* out,
+                         int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s);
 
 hipError_t launch_dense(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const int32_t* kv_len, float scale, float* out, char* ws, hipStream_t s);

@@ -50,8 +50,11 @@ class DeviceCase:
         if encode:
             A.encode_keys(self.k, self.kv_len, self.codes)
 
-    def decode(self, budget=None, want_debug=True):
+    def decode(self, budget=None, want_debug=True, sink=None, recent=None, mask=None, append=False):
+        """One decode step through the C ABI; sink / recent / mask (a host uint32
+        [B][words] bitmap) select the forced-position entry point."""
         A, torch, wl = self.A, self.torch, self.wl
+        mask_dev = None if mask is None else to_dev(np.ascontiguousarray(mask, np.uint32).view(np.int32), torch)
         budget = wl.budget if budget is None else budget
         out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device="cuda")
         sel = torch.full((wl.B, wl.Hq, budget), -7, dtype=torch.int32, device="cuda")
@@ -60,7 +63,7 @@ class DeviceCase:
         ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, budget))
         ws.fill_(0xFF)  # poison: any read of scratch not written by this call shows up
         A.decode_step(self.q, self.k, self.v, self.codes, self.kv_len, budget, wl.scale, out, ws, sel_idx=sel,
-                      dist=dist, q_codes=qc)
+                      dist=dist, q_codes=qc, sink=sink, recent=recent, mask=mask_dev, append=append)
         torch.cuda.synchronize()
         return (from_dev(out), from_dev(sel), None if dist is None else from_dev(dist, np.uint16),
                 None if qc is None else from_dev(qc))

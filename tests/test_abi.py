@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("adamas_encode_keys", "adamas_decode_step", "adamas_append_decode_step", "dense_decode_attention",
+    for n in ("adamas_encode_keys", "adamas_decode_step", "adamas_append_decode_step", "adamas_forced_decode_step",
+              "dense_decode_attention",
               "adamas_decode_workspace_size",
               "dense_decode_workspace_size", "adamas_status_string", "adamas_abi_version"):
         assert n in names
@@ -98,6 +99,30 @@ def test_decode_rejects_invalid_arguments(A):
     assert call_decode(A, good, ws_bytes=need - 1) == A.ERR_WORKSPACE
     assert call_decode(A, good, ws=None) == A.ERR_WORKSPACE
     assert call_decode(A, good, ws=FAKE + 128) == A.ERR_WORKSPACE  # not 256-byte aligned
+
+
+def call_forced(A, f, append=0, budget=8, d=None):
+    lib = A.raw_library()
+    d = d or A.dims(1, 32, 8, 32768)
+    fp = ctypes.byref(f) if f is not None else None
+    return lib.adamas_forced_decode_step(ctypes.byref(d), fp, append, FAKE, FAKE, FAKE, FAKE, FAKE, budget,
+                                         ctypes.c_float(0.088), FAKE, None, None, None, None, 0, None)
+
+
+def test_forced_decode_rejects_invalid_arguments(A):
+    """Checked before anything else runs (the workspace here is missing, so an
+    accepted forced set reaches ERR_WORKSPACE and no launch)."""
+    F = A.Forced
+    assert call_forced(A, F(2, 6, None, 0)) == A.ERR_WORKSPACE  # valid: fails only on the workspace
+    assert call_forced(A, F(4, 4, None, 0)) == A.ERR_WORKSPACE  # sink + recent == budget is allowed
+    assert call_forced(A, None) == A.ERR_INVALID_ARGUMENT
+    assert call_forced(A, F(0, 0, None, 0), append=2) == A.ERR_INVALID_ARGUMENT
+    assert call_forced(A, F(-1, 0, None, 0)) == A.ERR_INVALID_ARGUMENT
+    assert call_forced(A, F(0, -1, None, 0)) == A.ERR_INVALID_ARGUMENT
+    assert call_forced(A, F(5, 4, None, 0)) == A.ERR_INVALID_ARGUMENT  # more than the budget
+    assert call_forced(A, F(0, 0, FAKE, 1023)) == A.ERR_INVALID_ARGUMENT  # 1023 * 32 < 32768 positions
+    assert call_forced(A, F(0, 0, FAKE, 1024)) == A.ERR_WORKSPACE
+    assert call_forced(A, F(0, 0, FAKE + 2, 1024)) == A.ERR_INVALID_ARGUMENT  # misaligned mask
 
 
 def test_encode_and_dense_reject_invalid_arguments(A):

@@ -26,7 +26,8 @@ def env():
     return A, torch, oracle
 
 
-def check_decode(case, oracle, budget=None, threads=8, check_dist=True):
+def check_decode(case, oracle, budget=None, threads=8, check_dist=True, **forced):
+    """forced: sink / recent / mask (host uint32 [B][words]) for both sides."""
     wl = case.wl
     budget = wl.budget if budget is None else budget
     codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
@@ -35,8 +36,8 @@ def check_decode(case, oracle, budget=None, threads=8, check_dist=True):
         L = int(wl.kv_len[b])
         assert np.array_equal(codes_gpu[b, :, :L], codes_ref[b, :, :L]), "key codes differ (b=%d)" % b
     out_r, sel_r, dist_r, qc_r = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, budget, wl.scale,
-                                                    threads=threads, want_dist=check_dist)
-    out, sel, dist, qc = case.decode(budget, want_debug=True)
+                                                    threads=threads, want_dist=check_dist, **forced)
+    out, sel, dist, qc = case.decode(budget, want_debug=True, **forced)
     assert np.array_equal(qc, qc_r), "query codes differ"
     if check_dist:
         for b in range(wl.B):
