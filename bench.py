@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-e2e", action="store_true",
+                    help="skip the end-to-end decode of the 32-layer Llama-3.1-8B-shaped stack (random weights)")
+    ap.add_argument("--e2e-steps", type=int, default=16, help="timed tokens per end-to-end variant")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline: step latency over contexts 4K..128K x budgets 64..1024 on the "
                          "32/8-head layer (one JSON line per context), with the dense baseline")
@@ -303,6 +306,14 @@ def main():
             log("[bench] %s: %s" % (name, extra[name]))
             torch.cuda.empty_cache()
 
+    if not args.no_extra and not args.no_e2e:
+        extra["e2e_llama31_8b_shaped_b1"] = e2e(torch, dev, log, [args.context], budget, args.e2e_steps)
+        torch.cuda.empty_cache()
+        lens16 = W.batched_lengths(np.random.default_rng(args.seed))
+        extra["e2e_llama31_8b_shaped_b16_ragged16k-32k"] = e2e(torch, dev, log, [int(x) for x in lens16], 256,
+                                                               args.e2e_steps)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, budget, args.cpu_seconds, log)
@@ -496,6 +507,58 @@ def timed_graph_steps(torch, fn, cases, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (reps * len(cases))
+
+
+def e2e(torch, dev, log, lengths, budget, steps):
+    """Per-token latency of a 32-layer Llama-3.1-8B-shaped decode (random bf16
+    weights; torch GEMMs and the fused elementwise kernels for the dense parts)
+    with Adamas attention, with the last 3 layers dense (blog section 3.2), and
+    with dense attention everywhere; each step is one HIP graph replay (blog
+    section 5.1: graph capture at small batch), plus the Adamas step run
+    eagerly.  Sequence b holds lengths[b] positions when each variant starts;
+    every timed token appends one."""
+    import time
+    from sparse_attention_long_fwht_amd.llama_decode import LLAMA31_8B, LlamaShapedDecoder
+    t0 = time.time()
+    batch, context = len(lengths), max(lengths)
+    m = LlamaShapedDecoder(LLAMA31_8B, batch, context + 4 * steps + 64, attention="adamas", budget=budget)
+    m.fill_cache(lengths)
+    torch.cuda.synchronize()
+    log("[bench] e2e model and caches (batch %d, up to %d positions) ready (%.1f s)"
+        % (batch, context, time.time() - t0))
+    start = (m.tokens.clone(), m.kv_len.clone())
+
+    def timed(fn, n):
+        m.tokens.copy_(start[0])
+        m.kv_len.copy_(start[1])
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    res = {"model": "llama3.1-8b-shaped, 32 layers, random weights", "batch": batch, "max_context": context,
+           "positions": int(sum(lengths)), "budget": budget}
+    for name, mode, dense_last in (("adamas", "adamas", 0), ("adamas_last3_dense", "adamas", 3),
+                                   ("dense", "dense", 0)):
+        m.use(mode, dense_last)
+        g = m.capture(1)
+        res[name + "_ms_per_token"] = round(timed(g.replay, steps), 4)
+        del g
+        log("[bench] e2e %s: %.3f ms/token" % (name, res[name + "_ms_per_token"]))
+    m.use("adamas", 0)
+    res["adamas_eager_ms_per_token"] = round(timed(m.step, steps), 4)
+    res["speedup_vs_dense"] = round(res["dense_ms_per_token"] / res["adamas_ms_per_token"], 3)
+    res["speedup_vs_dense_last3_dense"] = round(res["dense_ms_per_token"] / res["adamas_last3_dense_ms_per_token"], 3)
+    res["graph_gain_vs_eager"] = round(1 - res["adamas_ms_per_token"] / res["adamas_eager_ms_per_token"], 3)
+    log("[bench] e2e: %s" % res)
+    del m
+    return res
 
 
 def upload(np, torch, dev, a):

@@ -12,6 +12,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libadamas.so")
 SOURCES = [os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "decode.hip")]
+# the decoder stack's fused elementwise kernels (include/llama_glue.h), a library of their own
+GLUE_LIB = os.path.join(PKG, "libllama_glue.so")
+GLUE_SOURCES = [os.path.join(CSRC, "llama_glue.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -24,8 +27,14 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+    _build_one(LIB, SOURCES, verbose)
+    _build_one(GLUE_LIB, GLUE_SOURCES, verbose)
+    return LIB
+
+
+def _build_one(lib, sources, verbose):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,8 +46,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + msg)
     if msg.strip() and verbose:
         print(msg)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -10,6 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "adamas.h")
+GLUE_HEADER = os.path.join(ROOT, "include", "llama_glue.h")
 
 
 @pytest.fixture(scope="module")
@@ -18,8 +19,8 @@ def A():
     return A
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
     return sorted(set(names))
@@ -136,6 +137,25 @@ def test_encode_and_dense_reject_invalid_arguments(A):
                                       None) == A.ERR_WORKSPACE
     assert lib.dense_decode_attention(ctypes.byref(d), FAKE, None, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE,
                                       1 << 30, None) == A.ERR_INVALID_ARGUMENT
+
+
+def test_glue_library_exports_and_rejects():
+    """libllama_glue.so exports what include/llama_glue.h declares; invalid
+    arguments return 1 before any launch."""
+    from sparse_attention_long_fwht_amd import llama_glue as G
+    lib = G.raw_library()
+    assert sorted(G.EXPORTED_SYMBOLS) == declared_functions(GLUE_HEADER)
+    for n in declared_functions(GLUE_HEADER):
+        assert hasattr(lib, n), n
+    f = ctypes.c_float(1e-5)
+    assert lib.llama_add_rmsnorm(None, None, None, FAKE, FAKE, 1, 4096, f, None) == 1
+    assert lib.llama_add_rmsnorm(FAKE, None, None, FAKE, FAKE, 1, 4100, f, None) == 1   # hidden % 8
+    assert lib.llama_add_rmsnorm(FAKE, None, None, FAKE, FAKE, 1, 32768, f, None) == 2  # too wide
+    assert lib.llama_add_rmsnorm(FAKE + 2, None, None, FAKE, FAKE, 1, 4096, f, None) == 1  # misaligned
+    assert lib.llama_rope_append(FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 32, 8, 100, None) == 1
+    assert lib.llama_rope_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 8, 100, None) == 1
+    assert lib.llama_silu_mul(FAKE, FAKE, 1, 100, None) == 1  # ffn % 8
+    assert lib.llama_silu_mul(None, FAKE, 1, 128, None) == 1
 
 
 def test_package_has_no_cpu_fallback():

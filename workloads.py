@@ -146,9 +146,14 @@ def llama(seed: int = 0, cap: int = 32768, budget: int = 128, B: int = 1, Hq: in
     return Workload(nm, q, k, v, kv_len, budget, planted, seed)
 
 
+def batched_lengths(rng: np.random.Generator, B: int = 16, cap: int = 32768, lo: int = 16384) -> np.ndarray:
+    """The batched recipe's lengths: uniform integers in [lo, cap], drawn first."""
+    return rng.integers(lo, cap, size=B, endpoint=True).astype(np.int32)
+
+
 def batched(seed: int = 0, B: int = 16, cap: int = 32768, budget: int = 256, lo: int = 16384) -> Workload:
     rng = np.random.default_rng(seed)
-    kv_len = rng.integers(lo, cap, size=B, endpoint=True).astype(np.int32)
+    kv_len = batched_lengths(rng, B, cap, lo)
     return llama(seed, cap=cap, budget=budget, B=B, kv_len=kv_len, rng=rng,
                  name="batched_b%d_n%d_k%d" % (B, cap, budget))
 
