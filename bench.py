@@ -290,6 +290,29 @@ def main():
             extra["step_us_forced_sink4_recent64"] = round(ms_f * 1e3, 3)
             log("[bench] forced (4 sinks, 64 recent): %.2f us" % (ms_f * 1e3))
             del g_f
+        # paged caches: the same data in shuffled pages of 16 and 64 positions
+        # (16 rotating copies, one block table shared by all)
+        for page in (16, 64):
+            mp = cap // page
+            perm = torch.randperm(B * mp, device=dev).view(B, mp).to(torch.int32)
+
+            def to_pages(t):  # [B][Hkv][cap][D] -> pool [B*mp][Hkv][page][D], logical page (b, j) at perm[b][j]
+                src = t.view(B, Hkv, mp, page, t.shape[-1]).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, page, -1)
+                pool = torch.empty(src.shape, dtype=src.dtype, device=src.device)
+                pool[perm.view(-1).long()] = src
+                return pool
+
+            pages = A.Pages(perm, page, capacity=cap)
+            pcopies = [(c[0], to_pages(c[1]), to_pages(c[2]), to_pages(c[3])) for c in copies[:16]]
+
+            def paged_step(c):
+                q, kp, vp, cp = c
+                A.decode_step(q, kp, vp, cp, kv_len, budget, wl.scale, out, ws, append=True, pages=pages)
+            g_p = graph_of(paged_step, pcopies)
+            ms_p, _ = time_graph(g_p, 16, args.steps, args.warmup)
+            extra["step_us_paged_page%d" % page] = round(ms_p * 1e3, 3)
+            log("[bench] paged (page %d): %.2f us" % (page, ms_p * 1e3))
+            del g_p, pcopies
         # full-cache key encode (prefill) pass, cold rotation
         g_enc = graph_of(lambda c: A.encode_keys(c[1], kv_len, c[3]), copies[:16])
         ms_enc, _ = time_graph(g_enc, 16, 64, 16)

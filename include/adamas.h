@@ -207,14 +207,65 @@ adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const 
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * Paged caches.  The pages are silent on cache layout; serving systems keep K/V
+ * in fixed-size pages handed out from pools (the paper builds on FlashInfer, a
+ * paged-KV attention engine, per the mlsanity.com citation map), and the key
+ * codes of the blog's section 3.1 cache can share the same pages.  Position p of
+ * sequence b lives on page block_table[b * max_pages + p / page_size] at slot
+ * p % page_size:
+ *   K, V pools    bf16  [num_pages][num_kv_heads][page_size][128]
+ *   codes pool    uint8 [num_pages][num_kv_heads][page_size][32]
+ *   block_table   int32 [batch][max_pages], device; page ids in [0, num_pages)
+ *                 (a precondition like kv_len: ids outside are clamped, never
+ *                 dereferenced out of the pools)
+ *   page_size     a power of two (1 .. 2^20)
+ *   max_pages     max_pages * page_size >= capacity (the dims' capacity is the
+ *                 longest a sequence may grow)
+ * Pages may be shared between sequences only where their contents are equal
+ * (a common prefix); an append writes the page of position kv_len[b]-1.
+ */
+typedef struct adamas_pages {
+  const int32_t* block_table;
+  int32_t max_pages;
+  int32_t page_size;
+  int32_t num_pages;
+} adamas_pages;
+
+/* adamas_encode_keys on paged pools: encodes positions [start[b], end[b]) of
+ * every sequence from k_pool into codes_pool.  Errors as adamas_encode_keys,
+ * plus INVALID_ARGUMENT for a NULL or inconsistent `pages`. */
+adamas_status adamas_paged_encode_keys(const adamas_dims* d, const adamas_pages* pages, const void* k_pool,
+                                       const int32_t* start, const int32_t* end, uint8_t* codes_pool,
+                                       void* stream);
+
+/* The decode step on paged pools: what adamas_forced_decode_step computes
+ * (forced may be NULL: no forced positions; append 0 or 1), reading K, V and
+ * codes through the block table.  dist and sel_idx stay indexed by position.
+ * Workspace: adamas_decode_workspace_size(d, budget).  Errors as
+ * adamas_forced_decode_step, plus INVALID_ARGUMENT for a NULL or inconsistent
+ * `pages`. */
+adamas_status adamas_paged_decode_step(const adamas_dims* d, const adamas_pages* pages, const adamas_forced* forced,
+                                       int32_t append, const void* q, const void* k_pool, const void* v_pool,
+                                       uint8_t* codes_pool, const int32_t* kv_len, int32_t budget, float scale,
+                                       float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* dense_decode_attention on paged pools (workspace: dense_decode_workspace_size). */
+adamas_status dense_paged_decode_attention(const adamas_dims* d, const adamas_pages* pages, const void* q,
+                                           const void* k_pool, const void* v_pool, const int32_t* kv_len,
+                                           float scale, float* out, void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
+/*
  * Profiling aid, not needed for correct use.  Enables (n_events > 0) or disables
  * (events == NULL or n_events == 0) per-kernel timing for calls made later on the
  * CALLING THREAD: launch i of a call (counting from 0) is bracketed by the HIP
  * events events[2*i] (start) and events[2*i+1] (stop), recorded on the call's
  * stream by the kernel dispatch itself, for every i with 2*i+1 < n_events.
- * Launch order: adamas_encode_keys -> 0 encode; adamas_decode_step,
- * adamas_append_decode_step and adamas_forced_decode_step -> 0 scan, 1
- * select+attend; dense_decode_attention ->
+ * Launch order: adamas_encode_keys, adamas_paged_encode_keys -> 0 encode;
+ * adamas_decode_step, adamas_append_decode_step, adamas_forced_decode_step and
+ * adamas_paged_decode_step -> 0 scan, 1 select+attend; dense_decode_attention
+ * and dense_paged_decode_attention ->
  * 0 attend, 1 combine.  While timing is on, a call waits (on the host) for each
  * of its kernels before launching the next, so that every event pair brackets
  * one kernel and not the dispatch gap after the previous one.

@@ -41,8 +41,31 @@ class Forced(ctypes.Structure):
                 ("mask_words", ctypes.c_int32)]
 
 
+class _PagesC(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+
+class Pages:
+    """A paged cache description: block_table int32 [B][max_pages] (device),
+    positions per page (a power of two), and the longest a sequence may grow
+    (default max_pages * page_size).  The K/V pools passed with it are
+    [num_pages][Hkv][page_size][128], the codes pool [num_pages][Hkv][page_size][32]."""
+
+    def __init__(self, block_table, page_size, capacity=None):
+        if block_table.dim() != 2 or block_table.element_size() != 4:
+            raise ValueError("block_table must be int32 [batch][max_pages]")
+        self.table = block_table
+        self.page_size = int(page_size)
+        self.capacity = int(capacity) if capacity is not None else block_table.shape[1] * self.page_size
+
+    def c(self, num_pages):
+        return _PagesC(_ptr(self.table, "block_table", 4), self.table.shape[1], self.page_size, int(num_pages))
+
+
 _vp = ctypes.c_void_p
 _dims_p = ctypes.POINTER(Dims)
+_pages_p = ctypes.POINTER(_PagesC)
 _lib.adamas_encode_keys.argtypes = [_dims_p, _vp, _vp, _vp, _vp, _vp]
 _lib.adamas_encode_keys.restype = ctypes.c_int
 _lib.adamas_decode_workspace_size.argtypes = [_dims_p, ctypes.c_int32]
@@ -56,6 +79,15 @@ _lib.adamas_forced_decode_step.argtypes = [_dims_p, ctypes.POINTER(Forced), ctyp
                                            ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                            _vp]
 _lib.adamas_forced_decode_step.restype = ctypes.c_int
+_lib.adamas_paged_encode_keys.argtypes = [_dims_p, _pages_p, _vp, _vp, _vp, _vp, _vp]
+_lib.adamas_paged_encode_keys.restype = ctypes.c_int
+_lib.adamas_paged_decode_step.argtypes = [_dims_p, _pages_p, ctypes.POINTER(Forced), ctypes.c_int32, _vp, _vp, _vp,
+                                          _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
+                                          ctypes.c_size_t, _vp]
+_lib.adamas_paged_decode_step.restype = ctypes.c_int
+_lib.dense_paged_decode_attention.argtypes = [_dims_p, _pages_p, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
+                                              ctypes.c_size_t, _vp]
+_lib.dense_paged_decode_attention.restype = ctypes.c_int
 _lib.dense_decode_workspace_size.argtypes = [_dims_p]
 _lib.dense_decode_workspace_size.restype = ctypes.c_size_t
 _lib.dense_decode_attention.argtypes = [_dims_p, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
@@ -69,8 +101,10 @@ _lib.adamas_abi_version.argtypes = []
 _lib.adamas_abi_version.restype = ctypes.c_int32
 
 EXPORTED_SYMBOLS = ("adamas_encode_keys", "adamas_decode_workspace_size", "adamas_decode_step",
-                    "adamas_append_decode_step", "adamas_forced_decode_step", "dense_decode_workspace_size",
-                    "dense_decode_attention", "adamas_profile_events", "adamas_status_string", "adamas_abi_version")
+                    "adamas_append_decode_step", "adamas_forced_decode_step", "adamas_paged_encode_keys",
+                    "adamas_paged_decode_step", "dense_decode_workspace_size", "dense_decode_attention",
+                    "dense_paged_decode_attention", "adamas_profile_events", "adamas_status_string",
+                    "adamas_abi_version")
 
 
 class AdamasError(RuntimeError):
@@ -118,13 +152,24 @@ def _check(status, where):
         raise AdamasError(status, where)
 
 
-def encode_keys(k, end, codes, start=None, stream=None, num_q_heads=None):
-    """Encode keys at positions [start[b], end[b]) of k [B][Hkv][cap][128] into codes [B][Hkv][cap][32]."""
-    B, Hkv, cap, hd = k.shape
-    d = dims(B, num_q_heads or Hkv, Hkv, cap, hd)
-    st = _lib.adamas_encode_keys(ctypes.byref(d), _ptr(k, "k", 2), _ptr(start, "start", 4, optional=True),
-                                 _ptr(end, "end", 4), _ptr(codes, "codes", 1), _stream(stream))
-    _check(st, "adamas_encode_keys")
+def encode_keys(k, end, codes, start=None, stream=None, num_q_heads=None, pages=None):
+    """Encode keys at positions [start[b], end[b]) of k [B][Hkv][cap][128] into codes [B][Hkv][cap][32]
+    (with `pages`: of the pools k [num_pages][Hkv][page][128] into codes [num_pages][Hkv][page][32])."""
+    if pages is None:
+        B, Hkv, cap, hd = k.shape
+        d = dims(B, num_q_heads or Hkv, Hkv, cap, hd)
+        st = _lib.adamas_encode_keys(ctypes.byref(d), _ptr(k, "k", 2), _ptr(start, "start", 4, optional=True),
+                                     _ptr(end, "end", 4), _ptr(codes, "codes", 1), _stream(stream))
+        _check(st, "adamas_encode_keys")
+        return
+    num_pages, Hkv, _, hd = k.shape
+    B = pages.table.shape[0]
+    d = dims(B, num_q_heads or Hkv, Hkv, pages.capacity, hd)
+    pc = pages.c(num_pages)
+    st = _lib.adamas_paged_encode_keys(ctypes.byref(d), ctypes.byref(pc), _ptr(k, "k", 2),
+                                       _ptr(start, "start", 4, optional=True), _ptr(end, "end", 4),
+                                       _ptr(codes, "codes", 1), _stream(stream))
+    _check(st, "adamas_paged_encode_keys")
 
 
 def decode_workspace_size(B, Hq, Hkv, cap, budget, head_dim=HEAD_DIM) -> int:
@@ -141,42 +186,61 @@ def alloc_workspace(nbytes, device=None):
 
 
 def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=None, dist=None, q_codes=None,
-                stream=None, append=False, sink=None, recent=None, mask=None):
+                stream=None, append=False, sink=None, recent=None, mask=None, pages=None):
     """One Adamas decode step; writes out [B][Hq][128] fp32 (and the optional outputs).
 
     append=True calls adamas_append_decode_step: the key at kv_len[b]-1 is
     encoded into `codes` first (no separate encode launch).  Any of sink /
     recent / mask (int32 [B][words] device bitmap, bit p % 32 of word p / 32)
-    calls adamas_forced_decode_step with those forced positions."""
+    calls adamas_forced_decode_step with those forced positions.  `pages`
+    (a Pages) calls adamas_paged_decode_step: k, v and codes are then pools."""
     B, Hq, hd = q.shape
-    _, Hkv, cap, _ = k.shape
+    n0, Hkv, cap, _ = k.shape
+    if pages is not None:
+        cap = pages.capacity
     d = dims(B, Hq, Hkv, cap, hd)
     tail = (_ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2), _ptr(codes, "codes", 1), _ptr(kv_len, "kv_len", 4),
             int(budget), float(scale), _ptr(out, "out", 4), _ptr(sel_idx, "sel_idx", 4, optional=True),
             _ptr(dist, "dist", 2, optional=True), _ptr(q_codes, "q_codes", 1, optional=True),
             _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
-    if sink is None and recent is None and mask is None:
+    forced = not (sink is None and recent is None and mask is None)
+    if not forced and pages is None:
         fn = _lib.adamas_append_decode_step if append else _lib.adamas_decode_step
         _check(fn(ctypes.byref(d), *tail), "adamas_append_decode_step" if append else "adamas_decode_step")
         return
-    if mask is not None and mask.dim() != 2:
-        raise ValueError("mask must be [batch][words]")
-    f = Forced(int(sink or 0), int(recent or 0), _ptr(mask, "mask", 4, optional=True),
-               0 if mask is None else int(mask.shape[1]))
-    st = _lib.adamas_forced_decode_step(ctypes.byref(d), ctypes.byref(f), 1 if append else 0, *tail)
-    _check(st, "adamas_forced_decode_step")
+    f = None
+    if forced:
+        if mask is not None and mask.dim() != 2:
+            raise ValueError("mask must be [batch][words]")
+        f = Forced(int(sink or 0), int(recent or 0), _ptr(mask, "mask", 4, optional=True),
+                   0 if mask is None else int(mask.shape[1]))
+    if pages is None:
+        st = _lib.adamas_forced_decode_step(ctypes.byref(d), ctypes.byref(f), 1 if append else 0, *tail)
+        _check(st, "adamas_forced_decode_step")
+        return
+    pc = pages.c(n0)
+    st = _lib.adamas_paged_decode_step(ctypes.byref(d), ctypes.byref(pc), ctypes.byref(f) if f is not None else None,
+                                       1 if append else 0, *tail)
+    _check(st, "adamas_paged_decode_step")
 
 
-def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None):
-    """Dense decode attention over every position < kv_len[b]; writes out [B][Hq][128] fp32."""
+def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None, pages=None):
+    """Dense decode attention over every position < kv_len[b]; writes out [B][Hq][128] fp32
+    (with `pages`: k and v are pools, see Pages)."""
     B, Hq, hd = q.shape
-    _, Hkv, cap, _ = k.shape
+    n0, Hkv, cap, _ = k.shape
+    if pages is not None:
+        cap = pages.capacity
     d = dims(B, Hq, Hkv, cap, hd)
-    st = _lib.dense_decode_attention(ctypes.byref(d), _ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2),
-                                     _ptr(kv_len, "kv_len", 4), float(scale), _ptr(out, "out", 4),
-                                     _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                                     _stream(stream))
-    _check(st, "dense_decode_attention")
+    tail = (_ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2), _ptr(kv_len, "kv_len", 4), float(scale),
+            _ptr(out, "out", 4), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    if pages is None:
+        _check(_lib.dense_decode_attention(ctypes.byref(d), *tail), "dense_decode_attention")
+        return
+    pc = pages.c(n0)
+    _check(_lib.dense_paged_decode_attention(ctypes.byref(d), ctypes.byref(pc), *tail),
+           "dense_paged_decode_attention")
 
 
 def profile_events(events):

@@ -37,6 +37,23 @@ adamas_status check_dims(const adamas_dims* d, bool need_q) {
   return ADAMAS_OK;
 }
 
+adamas::KvLayout contiguous_layout(const adamas_dims* d) {
+  return adamas::KvLayout{nullptr, 0, 0, 0, d->num_kv_heads, d->capacity};
+}
+
+// Checks a page description against the dims (after check_dims) and builds the layout.
+adamas_status paged_layout(const adamas_dims* d, const adamas_pages* pg, adamas::KvLayout* kv) {
+  if (!pg || !pg->block_table || !aligned(pg->block_table, 4)) return ADAMAS_ERR_INVALID_ARGUMENT;
+  const int32_t ps = pg->page_size;
+  if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1)) != 0 || pg->max_pages < 1 || pg->num_pages < 1)
+    return ADAMAS_ERR_INVALID_ARGUMENT;
+  if ((int64_t)pg->max_pages * ps < d->capacity) return ADAMAS_ERR_INVALID_ARGUMENT;
+  if ((int64_t)d->batch * pg->max_pages > ((int64_t)1 << 31)) return ADAMAS_ERR_UNSUPPORTED;
+  *kv = adamas::KvLayout{pg->block_table, pg->max_pages, __builtin_ctz((unsigned)ps), pg->num_pages,
+                         d->num_kv_heads, d->capacity};
+  return ADAMAS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,17 +80,38 @@ adamas_status adamas_profile_events(void* const* events, int32_t n_events) {
   return ADAMAS_OK;
 }
 
-adamas_status adamas_encode_keys(const adamas_dims* d, const void* k, const int32_t* start, const int32_t* end,
-                                 uint8_t* codes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+adamas_status encode_common(const adamas_dims* d, const adamas_pages* pages, const void* k, const int32_t* start,
+                            const int32_t* end, uint8_t* codes, void* stream) {
   adamas_status st = check_dims(d, false);
   if (st != ADAMAS_OK) return st;
   if (!k || !end || !codes) return ADAMAS_ERR_INVALID_ARGUMENT;
   if (!aligned(k, 16) || !aligned(codes, 16) || !aligned(end, 4) || (start && !aligned(start, 4)))
     return ADAMAS_ERR_INVALID_ARGUMENT;
-  hipError_t e = adamas::launch_encode_keys(d->batch, d->num_kv_heads, d->capacity,
-                                            static_cast<const uint16_t*>(k), start, end, codes,
+  adamas::KvLayout kv = contiguous_layout(d);
+  if (pages && (st = paged_layout(d, pages, &kv)) != ADAMAS_OK) return st;
+  hipError_t e = adamas::launch_encode_keys(d->batch, kv, static_cast<const uint16_t*>(k), start, end, codes,
                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+adamas_status adamas_encode_keys(const adamas_dims* d, const void* k, const int32_t* start, const int32_t* end,
+                                 uint8_t* codes, void* stream) {
+  return encode_common(d, nullptr, k, start, end, codes, stream);
+}
+
+adamas_status adamas_paged_encode_keys(const adamas_dims* d, const adamas_pages* pages, const void* k_pool,
+                                       const int32_t* start, const int32_t* end, uint8_t* codes_pool,
+                                       void* stream) {
+  if (!pages) return ADAMAS_ERR_INVALID_ARGUMENT;
+  return encode_common(d, pages, k_pool, start, end, codes_pool, stream);
 }
 
 size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget) {
@@ -86,13 +124,16 @@ size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget) {
 
 namespace {
 
-adamas_status decode_common(const adamas_dims* d, const void* q, const void* k, const void* v, uint8_t* codes,
-                            bool append, const adamas_forced* forced, const int32_t* kv_len, int32_t budget,
-                            float scale, float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+adamas_status decode_common(const adamas_dims* d, const adamas_pages* pages, const void* q, const void* k,
+                            const void* v, uint8_t* codes, bool append, const adamas_forced* forced,
+                            const int32_t* kv_len, int32_t budget, float scale, float* out, int32_t* sel_idx,
+                            uint16_t* dist, uint8_t* q_codes, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   adamas_status st = check_dims(d, true);
   if (st != ADAMAS_OK) return st;
   if (!q || !k || !v || !codes || !kv_len || !out || budget < 1) return ADAMAS_ERR_INVALID_ARGUMENT;
+  adamas::KvLayout kv = contiguous_layout(d);
+  if (pages && (st = paged_layout(d, pages, &kv)) != ADAMAS_OK) return st;
   adamas::Forced f{0, 0, nullptr, 0};
   if (forced) {
     if (forced->sink < 0 || forced->recent < 0 || (int64_t)forced->sink + forced->recent > budget)
@@ -108,7 +149,7 @@ adamas_status decode_common(const adamas_dims* d, const void* q, const void* k, 
   const Plan p = adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false);
   if (!p.supported) return ADAMAS_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return ADAMAS_ERR_WORKSPACE;
-  hipError_t e = adamas::launch_decode(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  hipError_t e = adamas::launch_decode(p, kv, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                        static_cast<const uint16_t*>(v), codes, append, f, kv_len, scale, out, sel_idx,
                                        dist, q_codes, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
@@ -123,16 +164,16 @@ adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void
                                  float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   // codes are only read on this path
-  return decode_common(d, q, k, v, const_cast<uint8_t*>(codes), false, nullptr, kv_len, budget, scale, out, sel_idx,
-                       dist, q_codes, workspace, workspace_bytes, stream);
+  return decode_common(d, nullptr, q, k, v, const_cast<uint8_t*>(codes), false, nullptr, kv_len, budget, scale, out,
+                       sel_idx, dist, q_codes, workspace, workspace_bytes, stream);
 }
 
 adamas_status adamas_append_decode_step(const adamas_dims* d, const void* q, const void* k, const void* v,
                                         uint8_t* codes, const int32_t* kv_len, int32_t budget, float scale,
                                         float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(d, q, k, v, codes, true, nullptr, kv_len, budget, scale, out, sel_idx, dist, q_codes,
-                       workspace, workspace_bytes, stream);
+  return decode_common(d, nullptr, q, k, v, codes, true, nullptr, kv_len, budget, scale, out, sel_idx, dist,
+                       q_codes, workspace, workspace_bytes, stream);
 }
 
 adamas_status adamas_forced_decode_step(const adamas_dims* d, const adamas_forced* forced, int32_t append,
@@ -141,8 +182,18 @@ adamas_status adamas_forced_decode_step(const adamas_dims* d, const adamas_force
                                         int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, void* workspace,
                                         size_t workspace_bytes, void* stream) {
   if (!forced || (append != 0 && append != 1)) return ADAMAS_ERR_INVALID_ARGUMENT;
-  return decode_common(d, q, k, v, codes, append != 0, forced, kv_len, budget, scale, out, sel_idx, dist, q_codes,
-                       workspace, workspace_bytes, stream);
+  return decode_common(d, nullptr, q, k, v, codes, append != 0, forced, kv_len, budget, scale, out, sel_idx, dist,
+                       q_codes, workspace, workspace_bytes, stream);
+}
+
+adamas_status adamas_paged_decode_step(const adamas_dims* d, const adamas_pages* pages, const adamas_forced* forced,
+                                       int32_t append, const void* q, const void* k_pool, const void* v_pool,
+                                       uint8_t* codes_pool, const int32_t* kv_len, int32_t budget, float scale,
+                                       float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pages || (append != 0 && append != 1)) return ADAMAS_ERR_INVALID_ARGUMENT;
+  return decode_common(d, pages, q, k_pool, v_pool, codes_pool, append != 0, forced, kv_len, budget, scale, out,
+                       sel_idx, dist, q_codes, workspace, workspace_bytes, stream);
 }
 
 size_t dense_decode_workspace_size(const adamas_dims* d) {
@@ -150,20 +201,44 @@ size_t dense_decode_workspace_size(const adamas_dims* d) {
   return adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, 1, true).total;
 }
 
-adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const void* k, const void* v,
-                                     const int32_t* kv_len, float scale, float* out, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+adamas_status dense_common(const adamas_dims* d, const adamas_pages* pages, const void* q, const void* k,
+                           const void* v, const int32_t* kv_len, float scale, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   adamas_status st = check_dims(d, true);
   if (st != ADAMAS_OK) return st;
+  adamas::KvLayout kv = contiguous_layout(d);
+  if (pages && (st = paged_layout(d, pages, &kv)) != ADAMAS_OK) return st;
   if (!q || !k || !v || !kv_len || !out) return ADAMAS_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(kv_len, 4) || !aligned(out, 4))
     return ADAMAS_ERR_INVALID_ARGUMENT;
   const Plan p = adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, 1, true);
   if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return ADAMAS_ERR_WORKSPACE;
-  hipError_t e = adamas::launch_dense(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  hipError_t e = adamas::launch_dense(p, kv, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                       static_cast<const uint16_t*>(v), kv_len, scale, out,
                                       static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                     const int32_t* kv_len, float scale, float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return dense_common(d, nullptr, q, k, v, kv_len, scale, out, workspace, workspace_bytes, stream);
+}
+
+adamas_status dense_paged_decode_attention(const adamas_dims* d, const adamas_pages* pages, const void* q,
+                                           const void* k_pool, const void* v_pool, const int32_t* kv_len,
+                                           float scale, float* out, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (!pages) return ADAMAS_ERR_INVALID_ARGUMENT;
+  return dense_common(d, pages, q, k_pool, v_pool, kv_len, scale, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

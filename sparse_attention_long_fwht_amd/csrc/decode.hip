@@ -142,6 +142,7 @@ struct ScanArgs {
   int Hq, Hkv, cap, chunk, nch, budget, append;
   int sink, recent;    // always-kept sinks and recent window (not ranked)
   int fmask_words;     // (sink, recent, fmask: scan_kernel<R, true> only)
+  KvLayout kv;         // where K rows and codes of a position live (scan_kernel<R, F, true>: paged)
 };
 
 // Blocks are dealt to the eight XCDs round-robin by linear block index.  When
@@ -151,7 +152,7 @@ constexpr int kXcds = 8;
 
 // kForced: sinks / recent window / special tokens in use (a separate
 // instantiation, so that the plain step pays nothing for them).
-template <int R, bool kForced>
+template <int R, bool kForced, bool kPaged>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int G = (int)gridDim.x / a.nch;  // (b, kv head) groups
   int bg, c;
@@ -178,10 +179,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const uint16_t q_lo = qrow[lane], q_hi = qrow[lane + 64];
   // first pass of key codes, addresses clamped to the capacity so that they
   // do not wait for kv_len
-  const uint4* cbase = reinterpret_cast<const uint4*>(a.codes + (size_t)bg * (size_t)a.cap * kCodeBytes);
+  const uint8_t* cbase = a.codes + (kPaged ? (size_t)0 : (size_t)bg * (size_t)a.cap * kCodeBytes);
+  auto code_src = [&](int pp) {
+    if constexpr (kPaged) return reinterpret_cast<const uint4*>(a.codes + kv_row<true>(a.kv, b, g, pp) * kCodeBytes);
+    else return reinterpret_cast<const uint4*>(cbase + (size_t)pp * kCodeBytes);
+  };
   int p = min(p0 + tid, a.cap - 1);
-  uint4 klo = cbase[(size_t)p * 2];
-  uint4 khi = cbase[(size_t)p * 2 + 1];
+  const uint4* c0 = code_src(p);
+  uint4 klo = c0[0];
+  uint4 khi = c0[1];
 
   __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins past kMaxKey stay 0)
   __shared__ uint32_t s_code[R + 1][8];      // query codes, then the appended key's
@@ -198,7 +204,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   for (int vi = wave; vi < nvec; vi += kScanThreads / 64) {
     uint32_t xlo = q_lo, xhi = q_hi;  // vi < R: vi == wave, the row loaded above
     if (vi >= R) {
-      const uint16_t* row = a.k + ((size_t)bg * a.cap + (size_t)(len - 1)) * kHeadDim;
+      const uint16_t* row = a.k + (kPaged ? kv_row<true>(a.kv, b, g, len - 1)
+                                          : (size_t)bg * a.cap + (size_t)(len - 1)) * kHeadDim;
       xlo = row[lane];
       xhi = row[lane + 64];
     }
@@ -213,7 +220,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
         if (c == 0 && a.q_codes)
           reinterpret_cast<uint32_t*>(a.q_codes + ((size_t)b * a.Hq + (size_t)(g * R + vi)) * kCodeBytes)[lane] = w;
       } else {
-        reinterpret_cast<uint32_t*>(a.codes + ((size_t)bg * a.cap + (size_t)(len - 1)) * kCodeBytes)[lane] = w;
+        reinterpret_cast<uint32_t*>(a.codes + (kPaged ? kv_row<true>(a.kv, b, g, len - 1)
+                                                      : (size_t)bg * a.cap + (size_t)(len - 1)) * kCodeBytes)[lane] = w;
       }
     }
   }
@@ -263,8 +271,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       uint4 nlo = klo, nhi = khi;
       if (pass + 1 < kScanPasses && base + kScanThreads < p1) {
         const int pn = min(base + kScanThreads + tid, p1 - 1);
-        nlo = cbase[(size_t)pn * 2];
-        nhi = cbase[(size_t)pn * 2 + 1];
+        const uint4* cn = code_src(pn);
+        nlo = cn[0];
+        nhi = cn[1];
       }
       p = base + tid;
       if (p < p1) {
@@ -421,6 +430,7 @@ struct SelAttArgs {
   int Hq, Hkv, R, cap, budget, chunk, nch, rec_win, pre_slots, splits, rows_per_split, bitmap_words;
   int early_prefetch;  // speculative prefetch of the likely rows right after the record loads
   int sink, recent;    // always-kept sinks and recent window
+  KvLayout kv;         // where K/V rows of a position live (select_attend_kernel<true>: paged)
 };
 
 constexpr int kSAThreads = 512;
@@ -518,6 +528,7 @@ __device__ __forceinline__ void emit_sorted(const SortedEmit& e) {
   }
 }
 
+template <bool kPaged>
 __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a) {
   const int bh = blockIdx.x;
   const int split = blockIdx.y;
@@ -569,8 +580,14 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   const int lo_rank = split * a.rows_per_split;
   const int hi_rank = min(lo_rank + a.rows_per_split, k_eff);
   const int mlo = lo_rank - s_b, mhi = hi_rank - s_b;  // this split's window of middle ranks
-  const uint16_t* Kg = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
-  const uint16_t* Vg = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
+  // K and V rows of a position of this head's kv head: Kg + kvoff(p), Vg + kvoff(p)
+  const size_t kv_base = kPaged ? (size_t)0 : ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
+  const uint16_t* Kg = a.k + kv_base;
+  const uint16_t* Vg = a.v + kv_base;
+  auto kvoff = [&](int pp) -> size_t {
+    if constexpr (kPaged) return kv_row<true>(a.kv, b, g, pp) * kHeadDim;
+    else return (size_t)pp * kHeadDim;
+  };
   // the split's always-kept row of this thread (-1: none): known from kv_len
   // alone, so its K/V lines are requested with the first record loads (into
   // pe, which the speculative prefetch below then leaves to this row)
@@ -602,7 +619,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         t[u] = *reinterpret_cast<const uint4*>(grec + (size_t)cc * kRecStride + 8 * j);
       }
       if (i0 == 0 && forced_pos >= 0) {  // (issued after the records: their waits do not include these)
-        const size_t row = (size_t)forced_pos * kHeadDim;
+        const size_t row = kvoff(forced_pos);
         pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
         pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
         pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
@@ -638,7 +655,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     if (tid < ((cs1 - cs0) << ulog) && forced_pos < 0) {
       const int cc = cs0 + (tid >> ulog), j = tid & ((1 << ulog) - 1);
       const int lp = min((int)s_pre[(size_t)cc * a.pre_slots + j], min(a.chunk, len - cc * a.chunk) - 1);
-      const size_t row = (size_t)(cc * a.chunk + lp) * kHeadDim;
+      const size_t row = kvoff(cc * a.chunk + lp);
       pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
       pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
       pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
@@ -833,7 +850,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
       const int j = wave + kSAWaves * jj;
       if (mine && j < (int)c.x && j < a.pre_slots) {
         const int lp = min((int)s_pre[(size_t)cc * a.pre_slots + j], min(a.chunk, len - cc * a.chunk) - 1);
-        const size_t row = (size_t)(cc * a.chunk + lp) * kHeadDim;
+        const size_t row = kvoff(cc * a.chunk + lp);
         pf[gi][jj][0] = *reinterpret_cast<const uint32_t*>(Kg + row);
         pf[gi][jj][1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
         pf[gi][jj][2] = *reinterpret_cast<const uint32_t*>(Vg + row);
@@ -958,14 +975,14 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     const int r0 = t0 + 16 * wave;
     const int ia = r0 + col;
     const int pa = min(max(s_list[ia < nrows ? ia : 0], 0), len - 1);  // (clamped: a position of the cache)
-    const uint16_t* kr = Kg + (size_t)pa * kHeadDim + 8 * kg;
+    const uint16_t* kr = Kg + kvoff(pa) + 8 * kg;
 #pragma unroll
     for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int iv = r0 + 4 * kg + i;
       const int pv = min(max(s_list[iv < nrows ? iv : 0], 0), len - 1);
-      vv[i] = *reinterpret_cast<const uint4*>(Vg + (size_t)pv * kHeadDim + 8 * col);
+      vv[i] = *reinterpret_cast<const uint4*>(Vg + kvoff(pv) + 8 * col);
     }
   };
   uint4 ka[4], vv[4];
@@ -1129,26 +1146,29 @@ static void launch_k(int i, Kernel kernel, dim3 grid, dim3 block, uint32_t shmem
     hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
 }
 
-template <int R, bool kForced>
+template <int R, bool kForced, bool kPaged>
 static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
   const uint32_t shmem = (uint32_t)(R * p.chunk * sizeof(uint16_t));  // sorted slots, staged
   if (shmem > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<R, kForced>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<R, kForced, kPaged>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  launch_k(0, scan_kernel<R, kForced>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), shmem, s, sa);
+  launch_k(0, scan_kernel<R, kForced, kPaged>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), shmem, s, sa);
   return hipSuccess;
 }
 
 template <int R>
 static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, bool forced, hipStream_t s) {
-  return forced ? launch_scan<R, true>(p, sa, s) : launch_scan<R, false>(p, sa, s);
+  if (sa.kv.table)
+    return forced ? launch_scan<R, true, true>(p, sa, s) : launch_scan<R, false, true>(p, sa, s);
+  return forced ? launch_scan<R, true, false>(p, sa, s) : launch_scan<R, false, false>(p, sa, s);
 }
 
-hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* codes,
-                         bool append, const Forced& f, const int32_t* kv_len, float scale, float* out,
-                         int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s) {
+hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, uint8_t* codes, bool append, const Forced& f, const int32_t* kv_len,
+                         float scale, float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, char* ws,
+                         hipStream_t s) {
   uint16_t* ws_sorted = reinterpret_cast<uint16_t*>(ws + p.off_sorted);
   uint16_t* ws_rec = reinterpret_cast<uint16_t*>(ws + p.off_rec);
   float* ws_part = reinterpret_cast<float*>(ws + p.off_part);
@@ -1157,7 +1177,7 @@ hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, co
   const bool forced = f.sink > 0 || f.recent > 0 || f.mask != nullptr;
   ScanArgs sa{q,       k,     codes,   kv_len, ws_sorted, ws_rec,   dist,          q_codes,
               counters, f.mask, p.Hq, p.Hkv, p.cap, p.chunk,   p.nch,    p.budget, append ? 1 : 0,
-              f.sink, f.recent, f.mask_words};
+              f.sink, f.recent, f.mask_words, kv};
   hipError_t es = hipErrorInvalidValue;
   switch (p.R) {
     case 1: es = launch_scan<1>(p, sa, forced, s); break;
@@ -1176,13 +1196,14 @@ hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, co
   SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
                 scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch, p.rec_win,
                 p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words, p.early_prefetch ? 1 : 0,
-                f.sink, f.recent};
+                f.sink, f.recent, kv};
+  const auto kernel = kv.table ? select_attend_kernel<true> : select_attend_kernel<false>;
   if (p.lds_select > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_attend_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_select);
     if (e != hipSuccess) return e;
   }
-  launch_k(1, select_attend_kernel, dim3(p.B * p.Hq, p.splits), dim3(kSAThreads), (uint32_t)p.lds_select, s, aa);
+  launch_k(1, kernel, dim3(p.B * p.Hq, p.splits), dim3(kSAThreads), (uint32_t)p.lds_select, s, aa);
   return hipGetLastError();
 }
 

@@ -28,23 +28,25 @@ namespace adamas {
 // --------------------------------------------------------------------------
 
 // grid (nblk, B*Hkv), 256 threads = 64 vectors per pass (a quad per vector).
+template <bool kPaged>
 __global__ __launch_bounds__(256) void encode_keys_kernel(const uint16_t* __restrict__ k,
                                                           const int32_t* __restrict__ start,
                                                           const int32_t* __restrict__ end,
-                                                          uint8_t* __restrict__ codes, int Hkv, int cap) {
+                                                          uint8_t* __restrict__ codes, KvLayout kv) {
   const int bg = blockIdx.y;
-  const int b = bg / Hkv;
+  const int b = bg / kv.Hkv;
+  const int g = bg - b * kv.Hkv;
   const int s = start ? start[b] : 0;
   const int e = end[b];
   const int quarter = threadIdx.x & 3;
   const int slot = threadIdx.x >> 2;  // 0..63
-  const size_t base = (size_t)bg * (size_t)cap;
   // The loop bound depends only on blockIdx, so every quad runs every pass.
   for (int p0 = s + (int)blockIdx.x * 64; p0 < e; p0 += (int)gridDim.x * 64) {
     const int p = p0 + slot;
     const bool valid = p < e;
     const int pl = valid ? p : e - 1;  // clamped rows keep the loads in bounds
-    const uint4* src = reinterpret_cast<const uint4*>(k + (base + (size_t)pl) * kHeadDim + quarter * 32);
+    const size_t row = kPaged ? kv_row<true>(kv, b, g, pl) : (size_t)bg * (size_t)kv.cap + (size_t)pl;
+    const uint4* src = reinterpret_cast<const uint4*>(k + row * kHeadDim + quarter * 32);
     uint4 w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = src[i];
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(const uint16_t* __rest
     uint32_t lo, hi;
     encode_quad(x, quarter, lo, hi);
     if (valid) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + (base + (size_t)p) * kCodeBytes);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * kCodeBytes);  // (valid: row of p)
       dst[quarter] = lo;
       dst[4 + quarter] = hi;
     }
@@ -72,6 +74,7 @@ struct AttendArgs {
   float* ws_part;       // [B][Hq][nch][kPartFloats]
   float qscale;         // softmax scale * log2(e)
   int Hq, Hkv, cap, chunk, nch;
+  KvLayout kv;
 };
 
 // Merge the per-chunk partials (m, l, o[128]) of R heads into out.  `part`
@@ -139,8 +142,8 @@ struct AttnSmem {
 //   q . K^T: MFMA 16x16x32 bf16, 16 rows x 16 columns (the R heads, rest zero)
 //            per wave, 64 rows per tile;
 //   P . V:   VALU, 16 lanes per row (8 dims each), 4 rows per instruction.
-template <int R>
-__device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, int bg, int c, int p0, int nrows,
+template <int R, bool kPaged>
+__device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, int c, int p0, int nrows,
                                             AttnSmem<R>& sm) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -165,8 +168,14 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
   for (int h = 0; h < R; ++h)
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
-  const uint16_t* Kg = a.k + (size_t)bg * (size_t)a.cap * kHeadDim;
-  const uint16_t* Vg = a.v + (size_t)bg * (size_t)a.cap * kHeadDim;
+  // K and V rows of position p: Kg + kvoff(p), Vg + kvoff(p)
+  const size_t kv_base = kPaged ? (size_t)0 : ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
+  const uint16_t* Kg = a.k + kv_base;
+  const uint16_t* Vg = a.v + kv_base;
+  auto kvoff = [&](int p) -> size_t {
+    if constexpr (kPaged) return kv_row<true>(a.kv, b, g, p) * kHeadDim;
+    else return (size_t)p * kHeadDim;
+  };
   __syncthreads();
 
   for (int t0 = 0; t0 < nrows; t0 += 64) {
@@ -176,14 +185,14 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
     {
       const int ia = t0 + 16 * w + col;
       const int pa = pos(ia < nrows ? ia : 0);
-      const uint16_t* kr = Kg + (size_t)pa * kHeadDim + 8 * kg;
+      const uint16_t* kr = Kg + kvoff(pa) + 8 * kg;
 #pragma unroll
       for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int iv = t0 + 16 * w + 4 * i + kg;
         const int pv = pos(iv < nrows ? iv : 0);
-        vv[i] = *reinterpret_cast<const uint4*>(Vg + (size_t)pv * kHeadDim + 8 * col);
+        vv[i] = *reinterpret_cast<const uint4*>(Vg + kvoff(pv) + 8 * col);
       }
     }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -273,7 +282,7 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
 // Dense decode attention: block (c, b*Hkv + g) attends the group's R queries
 // over positions [c*chunk, min((c+1)*chunk, kv_len[b])) and writes one partial
 // per head; combine_kernel merges the chunks.
-template <int R>
+template <int R, bool kPaged>
 __global__ __launch_bounds__(256) void dense_attend_kernel(AttendArgs a) {
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv;
@@ -285,7 +294,7 @@ __global__ __launch_bounds__(256) void dense_attend_kernel(AttendArgs a) {
   const int p0 = c * a.chunk;
   const int p1 = min(p0 + a.chunk, len);
   __shared__ AttnSmem<R> sm;
-  attend_rows<R>(a, b, g, bg, c, p0, p1 - p0, sm);
+  attend_rows<R, kPaged>(a, b, g, c, p0, p1 - p0, sm);
 }
 
 // Dense path: one block per (b, kv head) merges the chunk partials of its R heads.
@@ -318,22 +327,29 @@ static void launch_k(int i, Kernel kernel, dim3 grid, dim3 block, uint32_t shmem
     hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
 }
 
-hipError_t launch_encode_keys(int B, int Hkv, int cap, const uint16_t* k, const int32_t* start,
+hipError_t launch_encode_keys(int B, const KvLayout& kv, const uint16_t* k, const int32_t* start,
                               const int32_t* end, uint8_t* codes, hipStream_t s) {
-  const int bg = B * Hkv;
-  int nblk = (cap + 63) / 64;
+  const int bg = B * kv.Hkv;
+  int nblk = (kv.cap + 63) / 64;
   const int cap_blocks = 2048 / bg > 0 ? 2048 / bg : 1;
   if (nblk > cap_blocks) nblk = cap_blocks;
-  launch_k(0, encode_keys_kernel, dim3(nblk, bg), dim3(256), 0, s, k, start, end, codes, Hkv, cap);
+  if (kv.table)
+    launch_k(0, encode_keys_kernel<true>, dim3(nblk, bg), dim3(256), 0, s, k, start, end, codes, kv);
+  else
+    launch_k(0, encode_keys_kernel<false>, dim3(nblk, bg), dim3(256), 0, s, k, start, end, codes, kv);
   return hipGetLastError();
 }
 
 template <int R>
-static hipError_t launch_dense_r(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                 const int32_t* kv_len, float scale, float* out, char* ws, hipStream_t s) {
+static hipError_t launch_dense_r(const Plan& p, const KvLayout& kv, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const int32_t* kv_len, float scale, float* out, char* ws,
+                                 hipStream_t s) {
   float* ws_part = reinterpret_cast<float*>(ws + p.off_part);
-  AttendArgs aa{q, k, v, kv_len, ws_part, scale * 1.4426950408889634f, p.Hq, p.Hkv, p.cap, p.chunk, p.nch};
-  launch_k(0, dense_attend_kernel<R>, dim3(p.nch, p.B * p.Hkv), dim3(256), 0, s, aa);
+  AttendArgs aa{q, k, v, kv_len, ws_part, scale * 1.4426950408889634f, p.Hq, p.Hkv, p.cap, p.chunk, p.nch, kv};
+  if (kv.table)
+    launch_k(0, dense_attend_kernel<R, true>, dim3(p.nch, p.B * p.Hkv), dim3(256), 0, s, aa);
+  else
+    launch_k(0, dense_attend_kernel<R, false>, dim3(p.nch, p.B * p.Hkv), dim3(256), 0, s, aa);
   if (profile_events().n >= 4) {  // timing mode: see adamas_profile_events
     hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess) return e;
@@ -343,13 +359,14 @@ static hipError_t launch_dense_r(const Plan& p, const uint16_t* q, const uint16_
   return hipGetLastError();
 }
 
-hipError_t launch_dense(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        const int32_t* kv_len, float scale, float* out, char* ws, hipStream_t s) {
+hipError_t launch_dense(const Plan& p, const KvLayout& kv, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const int32_t* kv_len, float scale, float* out, char* ws,
+                        hipStream_t s) {
   switch (p.R) {
-    case 1: return launch_dense_r<1>(p, q, k, v, kv_len, scale, out, ws, s);
-    case 2: return launch_dense_r<2>(p, q, k, v, kv_len, scale, out, ws, s);
-    case 4: return launch_dense_r<4>(p, q, k, v, kv_len, scale, out, ws, s);
-    case 8: return launch_dense_r<8>(p, q, k, v, kv_len, scale, out, ws, s);
+    case 1: return launch_dense_r<1>(p, kv, q, k, v, kv_len, scale, out, ws, s);
+    case 2: return launch_dense_r<2>(p, kv, q, k, v, kv_len, scale, out, ws, s);
+    case 4: return launch_dense_r<4>(p, kv, q, k, v, kv_len, scale, out, ws, s);
+    case 8: return launch_dense_r<8>(p, kv, q, k, v, kv_len, scale, out, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

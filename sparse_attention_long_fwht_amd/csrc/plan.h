@@ -141,6 +141,26 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   return p;
 }
 
+// Where the K/V row and the key code of (b, kv head g, position p) live.
+// Contiguous caches: row (b * Hkv + g) * cap + p of [B][Hkv][cap].  Paged
+// caches: pools [num_pages][Hkv][page][...] and a block table [B][max_pages]
+// naming the page of each sequence's positions [j * page, (j + 1) * page);
+// the row is (page * Hkv + g) * page_size + p % page_size.  A K or V row starts
+// at row * 128 values, a code at row * 32 bytes.
+struct KvLayout {
+  const int32_t* table;  // paged only
+  int max_pages, page_log2, num_pages;
+  int Hkv, cap;
+};
+
+template <bool kPaged>
+__device__ __forceinline__ size_t kv_row(const KvLayout& L, int b, int g, int p) {
+  if (!kPaged) return ((size_t)b * L.Hkv + g) * (size_t)L.cap + (size_t)p;
+  // (page ids are a precondition; clamped to the pool all the same)
+  const int page = min(max(L.table[(size_t)b * L.max_pages + (p >> L.page_log2)], 0), L.num_pages - 1);
+  return ((((size_t)page * L.Hkv + g)) << L.page_log2) + (size_t)(p & ((1 << L.page_log2) - 1));
+}
+
 // Per-thread kernel-timing events (adamas_profile_events).
 constexpr int kMaxProfileEvents = 16;
 struct ProfileEvents {
@@ -149,8 +169,8 @@ struct ProfileEvents {
 };
 ProfileEvents& profile_events();  // this thread's setting
 
-// ---- launchers (kernels.hip) ----
-hipError_t launch_encode_keys(int B, int Hkv, int cap, const uint16_t* k, const int32_t* start,
+// ---- launchers (kernels.hip, decode.hip); kv.table == nullptr: contiguous caches ----
+hipError_t launch_encode_keys(int B, const KvLayout& kv, const uint16_t* k, const int32_t* start,
                               const int32_t* end, uint8_t* codes, hipStream_t s);
 
 // Forced positions of a decode step: p < sink, p >= kv_len[b] - recent, or bit
@@ -164,11 +184,13 @@ struct Forced {
 // `append`: first encode the key at position kv_len[b]-1 of every (b, kv head)
 // into `codes` (the scan block holding that position does it); otherwise codes
 // are only read.
-hipError_t launch_decode(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* codes,
-                         bool append, const Forced& f, const int32_t* kv_len, float scale, float* out,
-                         int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, char* ws, hipStream_t s);
+hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, uint8_t* codes, bool append, const Forced& f, const int32_t* kv_len,
+                         float scale, float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, char* ws,
+                         hipStream_t s);
 
-hipError_t launch_dense(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        const int32_t* kv_len, float scale, float* out, char* ws, hipStream_t s);
+hipError_t launch_dense(const Plan& p, const KvLayout& kv, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const int32_t* kv_len, float scale, float* out, char* ws,
+                        hipStream_t s);
 
 }  // namespace adamas

@@ -76,3 +76,27 @@ class DeviceCase:
         A.dense_decode_attention(self.q, self.k, self.v, self.kv_len, wl.scale, out, ws)
         torch.cuda.synchronize()
         return from_dev(out)
+
+
+def paginate(a, page, rng, spare=3, fill=0):
+    """Scatter a contiguous cache [B][H][cap][D] into a page pool [N][H][page][D]:
+    sequence b's logical page j goes to physical page table[b][j], a random
+    permutation over N = B * ceil(cap / page) + spare pages (the spare pages and
+    the tail of a last partial page hold `fill`).  Returns (pool, table)."""
+    B, H, cap, D = a.shape
+    mp = -(-cap // page)
+    n = B * mp + spare
+    table = rng.permutation(n)[:B * mp].reshape(B, mp).astype(np.int32)
+    padded = np.full((B, H, mp * page, D), fill, a.dtype)
+    padded[:, :, :cap] = a
+    pool = np.full((n, H, page, D), fill, a.dtype)
+    pool[table.reshape(-1)] = padded.reshape(B, H, mp, page, D).transpose(0, 2, 1, 3, 4).reshape(B * mp, H, page, D)
+    return pool, table
+
+
+def unpaginate(pool, table, cap):
+    """The contiguous view [B][H][cap][D] of a page pool through its table."""
+    B, mp = table.shape
+    n, H, page, D = pool.shape
+    out = pool[table.reshape(-1)].reshape(B, mp, H, page, D).transpose(0, 2, 1, 3, 4).reshape(B, H, mp * page, D)
+    return out[:, :, :cap]

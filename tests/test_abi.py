@@ -29,6 +29,7 @@ def declared_functions(header=HEADER):
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("adamas_encode_keys", "adamas_decode_step", "adamas_append_decode_step", "adamas_forced_decode_step",
+              "adamas_paged_encode_keys", "adamas_paged_decode_step", "dense_paged_decode_attention",
               "dense_decode_attention",
               "adamas_decode_workspace_size",
               "dense_decode_workspace_size", "adamas_status_string", "adamas_abi_version"):
@@ -124,6 +125,34 @@ def test_forced_decode_rejects_invalid_arguments(A):
     assert call_forced(A, F(0, 0, FAKE, 1023)) == A.ERR_INVALID_ARGUMENT  # 1023 * 32 < 32768 positions
     assert call_forced(A, F(0, 0, FAKE, 1024)) == A.ERR_WORKSPACE
     assert call_forced(A, F(0, 0, FAKE + 2, 1024)) == A.ERR_INVALID_ARGUMENT  # misaligned mask
+
+
+def test_paged_entry_points_reject_invalid_pages(A):
+    """Page descriptions are checked before anything runs (a valid one reaches
+    ERR_WORKSPACE here, since no workspace is given)."""
+    lib = A.raw_library()
+    d = A.dims(2, 32, 8, 32768)
+
+    def dec(pages):
+        pp = ctypes.byref(pages) if pages is not None else None
+        return lib.adamas_paged_decode_step(ctypes.byref(d), pp, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 128,
+                                            ctypes.c_float(0.088), FAKE, None, None, None, None, 0, None)
+
+    P = A._PagesC
+    assert dec(P(FAKE, 512, 64, 1200)) == A.ERR_WORKSPACE    # 512 pages of 64 = 32768
+    assert dec(None) == A.ERR_INVALID_ARGUMENT
+    assert dec(P(None, 512, 64, 1200)) == A.ERR_INVALID_ARGUMENT
+    assert dec(P(FAKE, 511, 64, 1200)) == A.ERR_INVALID_ARGUMENT  # 511 * 64 < capacity
+    assert dec(P(FAKE, 700, 48, 1200)) == A.ERR_INVALID_ARGUMENT  # not a power of two
+    assert dec(P(FAKE, 512, 64, 0)) == A.ERR_INVALID_ARGUMENT     # empty pool
+    assert dec(P(FAKE + 2, 512, 64, 1200)) == A.ERR_INVALID_ARGUMENT  # misaligned table
+    assert lib.adamas_paged_encode_keys(ctypes.byref(d), None, FAKE, None, FAKE, FAKE, None) == A.ERR_INVALID_ARGUMENT
+    assert lib.adamas_paged_encode_keys(ctypes.byref(d), ctypes.byref(P(FAKE, 511, 64, 9)), FAKE, None, FAKE, FAKE,
+                                        None) == A.ERR_INVALID_ARGUMENT
+    assert lib.dense_paged_decode_attention(ctypes.byref(d), ctypes.byref(P(FAKE, 512, 64, 9)), FAKE, FAKE, FAKE,
+                                            FAKE, ctypes.c_float(1.0), FAKE, None, 0, None) == A.ERR_WORKSPACE
+    assert lib.dense_paged_decode_attention(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE,
+                                            FAKE, 1 << 30, None) == A.ERR_INVALID_ARGUMENT
 
 
 def test_encode_and_dense_reject_invalid_arguments(A):
