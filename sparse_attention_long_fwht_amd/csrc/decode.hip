@@ -558,8 +558,10 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 
   // ---- A. loads: kv_len, the query fragment, the first rec_win words of every
   // chunk record (headers also to s_hdr) and the first pre_slots sorted slots
-  // of every chunk.
-  const int len = min(a.kv_len[b], a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
+  // of every chunk.  kv_len is a scalar load; an empty asm statement that
+  // "redefines" it after the first record loads keeps every use of it -- and
+  // so the wait for it -- behind those loads.
+  int len_raw = a.kv_len[b];
   const int col = lane & 15;
   const int kg = lane >> 4;
   uint4 qf[4];
@@ -571,6 +573,25 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   }
   const uint16_t* grec = a.rec + (size_t)bh * a.nch * kRecStride;
   const uint16_t* gsorted = a.sorted + (size_t)bh * a.nch * a.chunk;
+  // 16-byte words per chunk: record window and sorted prefix (powers of two)
+  const int per_log2 = __builtin_ctz(a.rec_win) - 3, pper_log2 = __builtin_ctz(a.pre_slots) - 3;
+  const int per = 1 << per_log2, pper = 1 << pper_log2;
+  const int n16 = a.nch << per_log2;
+  const int p16 = a.nch << pper_log2;
+  auto pre_src = [&](int i) {
+    const int cc = i >> pper_log2, j = i & (pper - 1);
+    return reinterpret_cast<const uint4*>(gsorted + (size_t)cc * a.chunk + 8 * j);
+  };
+  auto rec_src = [&](int i) {
+    const int cc = i >> per_log2, j = i & (per - 1);
+    return reinterpret_cast<const uint4*>(grec + (size_t)cc * kRecStride + 8 * j);
+  };
+  const uint4 tp = *pre_src(min(tid, p16 - 1));  // first pass of the prefixes, issued with the records
+  uint4 t0[4];                                   // first pass of the records
+#pragma unroll
+  for (int u = 0; u < 4; ++u) t0[u] = *rec_src(min(u * kSAThreads + tid, n16 - 1));
+  asm volatile("" : "+s"(len_raw));
+  const int len = min(len_raw, a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
   const int k_eff = min(a.budget, len);
   // Final ranks (ascending positions): the sinks [0, s_b), then the k_mid
   // ranked positions, then the recent window; the ranking below works on
@@ -589,42 +610,24 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     else return (size_t)pp * kHeadDim;
   };
   // the split's always-kept row of this thread (-1: none): known from kv_len
-  // alone, so its K/V lines are requested with the first record loads (into
-  // pe, which the speculative prefetch below then leaves to this row)
+  // alone, so its K/V lines are requested right after the first record loads
+  // (into pe, which the speculative prefetch below then leaves to this row)
   int forced_pos = -1;
+  uint32_t pe[4] = {0u, 0u, 0u, 0u};
   if (a.sink > 0 || a.recent > 0) {
     const int i = lo_rank + tid, j = i - s_b;
     if (i < hi_rank && (j < 0 || j >= k_mid)) forced_pos = j < 0 ? i : len - r_b + (j - k_mid);
+    if (forced_pos >= 0) {
+      const size_t row = kvoff(forced_pos);
+      pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
+      pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
+      pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
+      pe[3] = *reinterpret_cast<const uint32_t*>(Vg + row + 64);
+    }
   }
-  uint32_t pe[4] = {0u, 0u, 0u, 0u};
   const int nch_b = (len + a.chunk - 1) >> __builtin_ctz(a.chunk);  // chunk is a power of two
   {
-    // 16-byte words per chunk: record window and sorted prefix (powers of two)
-    const int per_log2 = __builtin_ctz(a.rec_win) - 3, pper_log2 = __builtin_ctz(a.pre_slots) - 3;
-    const int per = 1 << per_log2, pper = 1 << pper_log2;
-    const int n16 = a.nch << per_log2;
-    const int p16 = a.nch << pper_log2;
-    auto pre_src = [&](int i) {
-      const int cc = i >> pper_log2, j = i & (pper - 1);
-      return reinterpret_cast<const uint4*>(gsorted + (size_t)cc * a.chunk + 8 * j);
-    };
-    const uint4 tp = *pre_src(min(tid, p16 - 1));  // first pass of the prefixes, issued with the records
-#pragma unroll 1
-    for (int i0 = 0; i0 < n16; i0 += 4 * kSAThreads) {
-      uint4 t[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
-        const int cc = i >> per_log2, j = i & (per - 1);
-        t[u] = *reinterpret_cast<const uint4*>(grec + (size_t)cc * kRecStride + 8 * j);
-      }
-      if (i0 == 0 && forced_pos >= 0) {  // (issued after the records: their waits do not include these)
-        const size_t row = kvoff(forced_pos);
-        pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
-        pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
-        pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
-        pe[3] = *reinterpret_cast<const uint32_t*>(Vg + row + 64);
-      }
+    auto store = [&](int i0, const uint4 (&t)[4]) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
@@ -632,6 +635,14 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
         const int cc = i >> per_log2;
         if ((i & (per - 1)) == 0 && cc < nch_b) s_hdr[cc] = sanitize_hdr(t[u].x, t[u].y, min(a.chunk, len - cc * a.chunk));
       }
+    };
+    store(0, t0);
+#pragma unroll 1
+    for (int i0 = 4 * kSAThreads; i0 < n16; i0 += 4 * kSAThreads) {  // (records of more than 2048 words)
+      uint4 t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t[u] = *rec_src(min(i0 + u * kSAThreads + tid, n16 - 1));
+      store(i0, t);
     }
     reinterpret_cast<uint4*>(s_pre)[min(tid, p16 - 1)] = tp;
 #pragma unroll 1
