@@ -236,17 +236,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int m0 = kForced ? max(p0, s_b) : p0, m1 = kForced ? min(p1, len - r_b) : p1;
   const int k_mid = min(a.budget, len) - s_b - r_b;  // >= 0: sink + recent <= budget
 
-  // thermometer words of the query codes: t1 = lo|hi, t2 = hi, t3 = lo&hi
-  uint32_t qt[R][12];
+  // the query codes' low and high planes (uniform)
+  uint32_t ql[R][4], qh[R][4];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = __builtin_amdgcn_readfirstlane(s_code[r][w]);
-      const uint32_t hi = __builtin_amdgcn_readfirstlane(s_code[r][4 + w]);
-      qt[r][w] = lo | hi;
-      qt[r][4 + w] = hi;
-      qt[r][8 + w] = lo & hi;
+      ql[r][w] = __builtin_amdgcn_readfirstlane(s_code[r][w]);
+      qh[r][w] = __builtin_amdgcn_readfirstlane(s_code[r][4 + w]);
     }
 
   // special tokens (kForced with a mask): the caller's bitmap words of every
@@ -281,27 +278,30 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
           klo = make_uint4(s_code[R][0], s_code[R][1], s_code[R][2], s_code[R][3]);
           khi = make_uint4(s_code[R][4], s_code[R][5], s_code[R][6], s_code[R][7]);
         }
-        // |a - b| summed over coordinates = popcount of the three thermometer
-        // XORs (t1 = lo|hi, t2 = hi, t3 = lo&hi) over the 128 coordinates
+        // |a - b| for 2-bit codes a = 2 ha + la, b = 2 hb + lb: its low bit is
+        // L = la ^ lb (the parity of a - b) and its high bit M = [|a - b| >= 2]
+        // = (ha ^ hb) & ~(L & (ha ^ la)) (the high bits differ and the low
+        // difference does not have the opposite sign: checked over all 16
+        // pairs), so the sum over the 128 coordinates is
+        // popcount(L) + 2 popcount(M), word by word over the bit planes.
         const bool ranked = !kForced || (p >= m0 && p < m1);
         const bool special = kForced && ((fw[pass] >> (p & 31)) & 1u);
         const uint32_t lo[4] = {klo.x, klo.y, klo.z, klo.w};
         const uint32_t hi[4] = {khi.x, khi.y, khi.z, khi.w};
-        uint32_t t1[4], t3[4];
+        uint32_t x[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          t1[w] = lo[w] | hi[w];
-          t3[w] = lo[w] & hi[w];
-        }
+        for (int w = 0; w < 4; ++w) x[w] = hi[w] ^ lo[w];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          uint32_t d = 0;
+          uint32_t cl = 0, cm = 0;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            d += __builtin_popcount(t1[w] ^ qt[r][w]);
-            d += __builtin_popcount(hi[w] ^ qt[r][4 + w]);
-            d += __builtin_popcount(t3[w] ^ qt[r][8 + w]);
+            const uint32_t L = lo[w] ^ ql[r][w];
+            const uint32_t M = (hi[w] ^ qh[r][w]) & ~(L & x[w]);
+            cl += __builtin_popcount(L);
+            cm += __builtin_popcount(M);
           }
+          const uint32_t d = cl + 2u * cm;
           const uint32_t key = kForced ? (special ? 0u : d + 1u) : d;
           if (ranked) dr[pass][r] = (key << 16) | atomicAdd(&s_hist[r][key], 1u);
           if (a.dist_out) a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + p] = (uint16_t)d;
