@@ -273,11 +273,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
         nhi = cn[1];
       }
       p = base + tid;
-      if (p < p1) {
-        if (app_here && p == len - 1) {  // the code this block just produced
+      // the code this block just produced replaces the stored one (a uniform
+      // test first: one block of a group holds position len - 1)
+      if (app_here && len - 1 - base < kScanThreads && len - 1 >= base) {
+        if (p == len - 1) {
           klo = make_uint4(s_code[R][0], s_code[R][1], s_code[R][2], s_code[R][3]);
           khi = make_uint4(s_code[R][4], s_code[R][5], s_code[R][6], s_code[R][7]);
         }
+      }
+      if (p < p1) {
         // |a - b| for 2-bit codes a = 2 ha + la, b = 2 hb + lb: its low bit is
         // L = la ^ lb (the parity of a - b) and its high bit M = [|a - b| >= 2]
         // = (ha ^ hb) & ~(L & (ha ^ la)) (the high bits differ and the low
@@ -304,7 +308,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
           const uint32_t d = cl + 2u * cm;
           const uint32_t key = kForced ? (special ? 0u : d + 1u) : d;
           if (ranked) dr[pass][r] = (key << 16) | atomicAdd(&s_hist[r][key], 1u);
-          if (a.dist_out) a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + p] = (uint16_t)d;
+          if (kForced && a.dist_out)
+            a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + p] = (uint16_t)d;
         }
       }
       klo = nlo;
@@ -312,6 +317,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     }
   }
   __syncthreads();
+  // debug distances of the plain step: the key is the distance
+  if (!kForced && a.dist_out) {
+#pragma unroll
+    for (int pass = 0; pass < kScanPasses; ++pass) {
+      const int pp = p0 + pass * kScanThreads + tid;
+      if (p0 + pass * kScanThreads < p1 && pp < p1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + pp] = (uint16_t)(dr[pass][r] >> 16);
+      }
+    }
+  }
 
   // per head (wave r): bin offsets, dmin, localk, and the record.  A chunk
   // with nothing to rank gets dmin = localk = kMaxKey, complete, n = 0.
