@@ -97,8 +97,8 @@ def main():
         return summarize_trace(*args.summarize_trace)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the Adamas decode step is built and timed on a single MI355X; "
-              "multi-GPU runs are not part of this build (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+        print("bench.py measures one GPU only: the Adamas decode step runs and is timed on a single MI355X; "
+              "runs over several GPUs are not supported (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
 

@@ -196,3 +196,13 @@ def test_package_has_no_cpu_fallback():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text, f
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says so,
+    before any GPU work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr
