@@ -125,7 +125,11 @@ __device__ __forceinline__ void encode_wave(uint32_t qlo_bits, uint32_t qhi_bits
 
 constexpr int kScanThreads = 512;  // one key per thread per pass
 constexpr int kHistBins = 7 * 64;  // bins as scanned by one wave: 7 per lane (up to kMaxKey + 1 used)
-static_assert(kHistBins > kMaxKey, "every selection key has a bin");
+// the last bin takes the keys a forced-position scan does not rank (sinks and
+// window): counted like the others so that no atomic sits behind a branch, then
+// left out of the records and the scatter
+constexpr int kSpareBin = kHistBins - 1;
+static_assert(kSpareBin > kMaxKey, "every selection key has a bin, and the spare bin is none of them");
 constexpr int kScanPasses = kScanMaxChunk / kScanThreads;
 
 struct ScanArgs {
@@ -306,8 +310,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
             cm += __builtin_popcount(M);
           }
           const uint32_t d = cl + 2u * cm;
-          const uint32_t key = kForced ? (special ? 0u : d + 1u) : d;
-          if (ranked) dr[pass][r] = (key << 16) | atomicAdd(&s_hist[r][key], 1u);
+          const uint32_t key = kForced ? (!ranked ? (uint32_t)kSpareBin : special ? 0u : d + 1u) : d;
+          dr[pass][r] = (key << 16) | atomicAdd(&s_hist[r][key], 1u);
           if (kForced && a.dist_out)
             a.dist_out[((size_t)b * a.Hq + (size_t)(g * R + r)) * (size_t)a.cap + p] = (uint16_t)d;
         }
@@ -341,7 +345,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     const int r = wave;
     uint32_t cnt[7], cum[7], loc = 0;
 #pragma unroll
-    for (int j = 0; j < 7; ++j) cnt[j] = s_hist[r][7 * lane + j];  // bins past kMaxKey are zero
+    for (int j = 0; j < 7; ++j) {
+      cnt[j] = s_hist[r][7 * lane + j];  // bins past kMaxKey are zero, but for the spare bin
+      if (kForced && 7 * lane + j == kSpareBin) cnt[j] = 0u;
+    }
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       loc += cnt[j];
