@@ -398,6 +398,37 @@ def test_decode_long512k_sampled_groups(env):
         assert_out_close(out[:, hs], o_r)
 
 
+def test_decode_long512k_largest_budget(env):
+    """The largest supported budget at the largest capacity (229376 of 524288
+    positions: 64 splits of 3584 rows per head); one KV group checked."""
+    A, torch, oracle = env
+    assert A.decode_workspace_size(1, 32, 8, 524288, 229376) > 0
+    assert A.decode_workspace_size(1, 32, 8, 524288, 229377) == 0
+    wl = W.llama(4, cap=524288, budget=229376, name="long512k_k224k")
+    case = DeviceCase(wl, A, torch)
+    out, sel, _, qc = case.decode(want_debug=False)
+    R = wl.Hq // wl.Hkv
+    g = 3
+    kg, vg = wl.k[:, g:g + 1], wl.v[:, g:g + 1]
+    codes_ref = oracle.encode_keys(kg, wl.kv_len)
+    assert np.array_equal(from_dev(case.codes)[:, g:g + 1], codes_ref)
+    o_r, s_r, _, _ = oracle.decode_step(wl.q[:, g * R:(g + 1) * R], kg, vg, codes_ref, wl.kv_len, wl.budget,
+                                        wl.scale, threads=16, want_dist=False)
+    hs = slice(g * R, (g + 1) * R)
+    assert np.array_equal(sel[:, hs], s_r)
+    assert_out_close(out[:, hs], o_r)
+
+
+def test_decode_many_heads(env):
+    """32768 query heads (batch 1024 x 32 / 8 heads, 96 positions each, ragged):
+    grids of 8192 scan and 32768 select blocks."""
+    A, torch, oracle = env
+    rng = np.random.default_rng(60)
+    lens = rng.integers(1, 97, 1024).astype(np.int32)
+    wl = W.llama(60, cap=96, budget=16, B=1024, kv_len=lens, n_planted=1)
+    check_decode(DeviceCase(wl, A, torch), oracle, budget=16, threads=16)
+
+
 # ---------------------------------------------------------------- dense baseline
 
 
