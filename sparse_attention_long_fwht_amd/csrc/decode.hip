@@ -116,12 +116,12 @@ __device__ __forceinline__ void encode_wave(uint32_t qlo_bits, uint32_t qhi_bits
 //                 positions at or below it (n_c = positions in the chunk);
 //   record        dmin, localk, complete (kk == n_c), n_c, a zero (cum(dmin - 1)),
 //                 then the cumulative count cum(d) for d = dmin .. localk.
-// (k = the ranked budget, k_eff less the always-kept positions; distances
-// mean selection keys.)  The k smallest distances overall never go past localk
-// of a chunk that is not complete (that chunk alone has kk = k positions at or
-// below localk),
-// and a complete chunk keeps all of its positions; so the records determine the
-// threshold and the sorted prefixes hold every selected position.
+// (k = the ranked budget, k_eff less the always-kept positions; "distance"
+// means the selection key, which differs from the distance only with forced
+// positions.)  The k smallest distances overall never go past localk of a chunk
+// that is not complete (that chunk alone has kk = k positions at or below
+// localk), and a complete chunk keeps all of its positions; so the records
+// determine the threshold and the sorted prefixes hold every selected position.
 
 constexpr int kScanThreads = 512;  // one key per thread per pass
 constexpr int kHistBins = 7 * 64;  // bins as scanned by one wave: 7 per lane (up to kMaxKey + 1 used)
@@ -135,14 +135,14 @@ constexpr int kScanPasses = kScanMaxChunk / kScanThreads;
 struct ScanArgs {
   const uint16_t* q;
   const uint16_t* k;   // read only when `append`
-  uint8_t* codes;      // written only when `append` (the appended key's code)
+  uint8_t* codes;      // read; written only when `append` (the appended key's code)
   const int32_t* kv_len;
   uint16_t* sorted;    // [B][Hq][nch][chunk]
   uint16_t* rec;       // [B][Hq][nch][kRecStride]
   uint16_t* dist_out;  // optional [B][Hq][cap]
   uint8_t* q_codes;    // optional [B][Hq][32]
   uint32_t* counters;  // [B][Hq], cleared here for select_attend_kernel
-  const uint32_t* fmask;  // optional [B][fmask_words] bitmap of forced positions
+  const uint32_t* fmask;  // optional [B][fmask_words] bitmap of special tokens (ranked first)
   int Hq, Hkv, cap, chunk, nch, budget, append;
   int sink, recent;    // always-kept sinks and recent window (not ranked)
   int fmask_words;     // (sink, recent, fmask: scan_kernel<R, true> only)
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   uint4 klo = c0[0];
   uint4 khi = c0[1];
 
-  __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins past kMaxKey stay 0)
+  __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins past kMaxKey stay 0 but for kSpareBin)
   __shared__ uint32_t s_code[R + 1][8];      // query codes, then the appended key's
   __shared__ uint32_t s_limit[R];                    // sorted slots kept per head
   __shared__ uint32_t s_recw[R];                     // 16-byte words of each head's record
@@ -260,10 +260,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       fw[pass] = a.fmask[(size_t)b * a.fmask_words + ((min(p0 + pass * kScanThreads + tid, p1 - 1)) >> 5)];
   }
 
-  // selection keys (the distance; with kForced 0 for a special token and
-  // distance + 1 for the others); each ranked (key, head) takes the next rank
-  // in its key's bin.  The next pass's codes are loaded while this pass
-  // computes.
+  // selection keys (the distance; with kForced 0 for a special token,
+  // distance + 1 for the other ranked keys and kSpareBin for the unranked);
+  // each (key, head) takes the next rank in its key's bin.  The next pass's
+  // codes are loaded while this pass computes.
   uint32_t dr[kScanPasses][R];  // (key << 16) | rank inside the bin
 #pragma unroll
   for (int pass = 0; pass < kScanPasses; ++pass) {
@@ -678,10 +678,11 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   // prefix hold its smallest distances, the positions most likely kept: long
   // before the selection is known, one word of each 128-byte line of their K
   // and V rows is loaded (thread (cc, j): slot j < U of chunk cc, U about
-  // k_eff / chunks, over the chunks this split's ranks most likely fall in).
-  // The exact rows are prefetched again after E; the words are read only at
-  // the block's end, so nothing waits for these loads.  Only where the rows
-  // stay in L2 until used (a few heads, one block each: plan.h).
+  // k_mid / chunks, over the chunks this split's ranks most likely fall in;
+  // a thread that already prefetched an always-kept row skips this).  The
+  // exact rows are prefetched again after E; the words are read only at the
+  // block's end, so nothing waits for these loads.  Only where the rows stay
+  // in L2 until used (a few heads, one block each: plan.h).
   if (a.early_prefetch && k_mid > 0 && max(mlo, 0) < min(mhi, k_mid)) {
     int ulog = 0;  // U = 1 << ulog
     while ((1 << ulog) < a.pre_slots && (nch_b << ulog) < k_mid) ++ulog;
