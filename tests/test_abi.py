@@ -206,3 +206,23 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_binding_rejects_host_and_misshapen_tensors(A):
+    """The binding checks its tensors before any library call: host tensors,
+    non-contiguous views and wrong element sizes raise ValueError (no GPU needed)."""
+    import torch
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16)
+    codes = torch.zeros((1, 2, 64, 32), dtype=torch.uint8)
+    kv_len = torch.full((1,), 64, dtype=torch.int32)
+    out = torch.zeros((1, 4, 128), dtype=torch.float32)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device tensor"):
+        A.decode_step(q, k, k, codes, kv_len, 8, 0.1, out, ws)
+    with pytest.raises(ValueError, match="device tensor"):
+        A.encode_keys(k, kv_len, codes)
+    with pytest.raises(ValueError, match="device tensor"):
+        A.dense_decode_attention(q, k, k, kv_len, 0.1, out, ws)
+    with pytest.raises(ValueError):
+        A.Pages(torch.zeros((1, 4), dtype=torch.int64), 16)  # block table must be int32 [B][pages]
