@@ -89,3 +89,55 @@ def test_profile_events_time_each_kernel_and_change_nothing():
         ms = ctypes.c_float()
         assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * i], evs[2 * i + 1]) == 0
         assert 0.0 < ms.value < 100.0
+
+
+def test_graph_replay_forced_and_paged():
+    """The paged step with forced positions and the fused append, captured once
+    and replayed with eager work in between: every replay equals the eager call."""
+    import torch
+    import sparse_attention_long_fwht_amd as A
+    from helpers import paginate, to_dev
+
+    wl = W.llama(44, cap=6000, budget=256, B=2, kv_len=np.array([6000, 3333], np.int32))
+    page = 64
+    kp, table = paginate(wl.k, page, np.random.default_rng(1))
+    vp, _ = paginate(wl.v, page, np.random.default_rng(1))
+    k, v, tab = to_dev(kp, torch), to_dev(vp, torch), to_dev(table, torch)
+    q, kv_len = to_dev(wl.q, torch), to_dev(wl.kv_len, torch)
+    pages = A.Pages(tab, page, capacity=wl.cap)
+    codes = torch.zeros((kp.shape[0], wl.Hkv, page, 32), dtype=torch.uint8, device="cuda")
+    A.encode_keys(k, kv_len, codes, pages=pages, num_q_heads=wl.Hq)
+    mask = torch.zeros((wl.B, (wl.cap + 31) // 32), dtype=torch.int32, device="cuda")
+    mask[:, 3] = 0x1010  # positions 100 and 108 of each sequence
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((wl.B, wl.Hq, wl.budget), dtype=torch.int32, device="cuda")
+    ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, wl.budget))
+
+    def step():
+        A.decode_step(q, k, v, codes, kv_len, wl.budget, wl.scale, out, ws, sel_idx=sel, append=True, sink=4,
+                      recent=32, mask=mask, pages=pages)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_sel = from_dev(out).copy(), from_dev(sel).copy()
+    assert np.all(np.isin([100, 108], ref_sel[0, 0])) and np.all(np.isin(np.arange(4), ref_sel[1, 3]))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-5)
+        torch.zeros(1 << 20, device="cuda").add_(1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(out), ref_out), "replay %d: out differs" % i
+        assert np.array_equal(from_dev(sel), ref_sel), "replay %d: sel_idx differs" % i
+

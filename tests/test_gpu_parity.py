@@ -439,6 +439,34 @@ def test_dense_tiny_and_ragged(env):
         assert_out_close(case.dense(), oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale))
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (8, 1), (16, 2)])
+def test_dense_group_sizes(env, Hq, Hkv):
+    A, torch, oracle = env
+    wl = W.llama(38, cap=3100, budget=1, B=2, Hq=Hq, Hkv=Hkv, kv_len=np.array([3100, 1], np.int32))
+    case = DeviceCase(wl, A, torch, encode=False)
+    assert_out_close(case.dense(), oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale))
+
+
+def test_encode_keys_arbitrary_ranges(env):
+    """Ranges [start[b], end[b]) anywhere in the cache (empty ones included):
+    exactly those rows are written, equal to the oracle's codes; the rest of
+    the poisoned code buffer is left as it was."""
+    A, torch, oracle = env
+    wl = W.llama(39, cap=4000, budget=8, B=4, Hq=8, Hkv=2)
+    start = np.array([0, 1234, 3999, 2000], np.int32)
+    end = np.array([4000, 1300, 3999, 3001], np.int32)
+    case = DeviceCase(wl, A, torch, encode=False)
+    case.codes.fill_(0xA5)
+    A.encode_keys(case.k, to_dev(end, torch), case.codes, start=to_dev(start, torch))
+    torch.cuda.synchronize()
+    got = from_dev(case.codes)
+    ref = oracle.encode_keys(wl.k, end, start=start)
+    for b in range(wl.B):
+        s, e = int(start[b]), int(end[b])
+        assert np.array_equal(got[b, :, s:e], ref[b, :, s:e])
+        assert np.all(got[b, :, :s] == 0xA5) and np.all(got[b, :, e:] == 0xA5)
+
+
 def test_dense_llama32k(env):
     A, torch, oracle = env
     wl = W.llama(0, cap=32768, budget=128)
