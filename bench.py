@@ -253,6 +253,8 @@ def main():
              "cache_copies": R}
 
     if not args.no_extra:
+        extra["selection_quality"] = selection_quality(torch, wl, q0, k0, v0, kv_len, sel, out, ws_dense, A)
+        log("[bench] selection quality (informational): %s" % extra["selection_quality"])
         # the same step as two library calls: adamas_encode_keys + adamas_decode_step
         g_unf = graph_of(step_unfused, copies)
         ms_unf, _ = time_graph(g_unf, R, args.steps, args.warmup)
@@ -530,6 +532,43 @@ def timed_graph_steps(torch, fn, cases, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (reps * len(cases))
+
+
+def selection_quality(torch, wl, q, k, v, kv_len, sel, out, ws_dense, A):
+    """Informational, never a pass/fail criterion (no page fixes a target on
+    synthetic data): how much of the exact attention the selection keeps, on the
+    headline workload.  Per query head: recall of the exact top-k by q.K (fp32
+    scores), recall of the planted positions the query was built from, the
+    softmax mass of the selected rows, and the output's relative L2 distance to
+    dense attention.  `sel` and `out` hold the Adamas step's selection and output
+    for (q, k, v) (bf16 bit patterns, any 2-byte dtype)."""
+    import numpy as np
+    B, Hq, budget = sel.shape
+    qb, kb = q.view(torch.bfloat16), k.view(torch.bfloat16)
+    grp = Hq // wl.Hkv
+    dense = torch.empty_like(out)
+    A.dense_decode_attention(q, k, v, kv_len, wl.scale, dense, ws_dense)
+    torch.cuda.synchronize()
+    rec, planted, mass, err = [], [], [], []
+    for b in range(B):
+        L = int(wl.kv_len[b])
+        for h in range(Hq):
+            kf = kb[b, h // grp, :L].float().contiguous()
+            s = (kf @ qb[b, h].float().contiguous()) * wl.scale
+            top = set(torch.topk(s, min(budget, L)).indices.cpu().tolist())
+            chosen = sel[b, h]
+            chosen = set(chosen[chosen >= 0].cpu().tolist())
+            rec.append(len(top & chosen) / max(1, len(top)))
+            pl = set(int(x) for x in wl.planted[b * Hq + h])
+            planted.append(len(pl & chosen) / max(1, len(pl)))
+            p = torch.softmax(s, 0)
+            mass.append(float(p[torch.tensor(sorted(chosen), device=p.device)].sum()))
+            d = dense[b, h]
+            err.append(float((out[b, h] - d).norm() / d.norm()))
+    return {"recall_vs_exact_qk_topk": round(float(np.mean(rec)), 4),
+            "planted_recall": round(float(np.mean(planted)), 4),
+            "softmax_mass_kept": round(float(np.mean(mass)), 4),
+            "out_rel_l2_vs_dense": round(float(np.mean(err)), 4)}
 
 
 def e2e(torch, dev, log, lengths, budget, steps):
