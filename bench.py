@@ -390,14 +390,15 @@ def read_traffic(kernel, algo_bytes):
     path = counters_path(kernel)
     if not os.path.exists(path):
         return None
-    fields = {}
+    recorded, hbm = None, None
     for line in open(path):
-        if ":" in line:
-            k, v = line.split(":", 1)
-            fields[k.strip()] = v.strip()
-    if fields.get("source sha256[:16]") != source_hash(kernel) or "hbm_bytes_per_launch" not in fields:
+        if line.startswith("source sha256[:16]:"):  # "<hash>  (files)"
+            recorded = line[len("source sha256[:16]:"):].split()[0]
+        elif line.startswith("hbm_bytes_per_launch:"):
+            hbm = int(float(line.split(":", 1)[1]))
+    if recorded != source_hash(kernel) or hbm is None:
         return None
-    return int(float(fields["hbm_bytes_per_launch"]))
+    return hbm
 
 
 def _csv_rows(d, suffix):

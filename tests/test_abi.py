@@ -226,3 +226,21 @@ def test_binding_rejects_host_and_misshapen_tensors(A):
         A.dense_decode_attention(q, k, k, kv_len, 0.1, out, ws)
     with pytest.raises(ValueError):
         A.Pages(torch.zeros((1, 4), dtype=torch.int64), 16)  # block table must be int32 [B][pages]
+
+
+def test_bench_reads_committed_counters():
+    """bench.py takes `traffic` from the committed counter summaries while they
+    match the kernel sources (a hash in the file), and None when they do not."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for kernel in ("scan", "select_attend"):
+        path = bench.counters_path(kernel)
+        assert os.path.exists(path), path
+        text = open(path).read()
+        got = bench.read_traffic(kernel, 0)
+        if bench.source_hash(kernel) in text:
+            assert got is not None and got > 0
+        else:
+            assert got is None
