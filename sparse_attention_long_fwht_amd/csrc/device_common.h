@@ -31,6 +31,12 @@ template <int CTRL>
 __device__ __forceinline__ float quad_swap(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+// The same permute with no "old" operand (every lane is written), so that the
+// compiler can fold it into the consuming add as a DPP source.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm_src(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -69,24 +75,28 @@ __device__ __forceinline__ void encode_quad(float (&x)[32], int quarter, uint32_
     }
   }
   // half-width 32: partner is lane ^ 1.  The lane holding x[j] (bit clear) forms
-  // own + partner; the lane holding x[j+32] forms partner - own.
+  // partner + own = x[j] + x[j+32] (addition commutes exactly); the lane holding
+  // x[j+32] forms partner + (-own) = x[j] - x[j+32] (negation is exact).  One
+  // add with the partner as a DPP source and the sign-flipped own value.
   {
-    const float sgn = (quarter & 1) ? -1.0f : 1.0f;
+    const uint32_t sgn = (quarter & 1) ? 0x80000000u : 0u;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = __builtin_fmaf(x[e], sgn, quad_swap<kQuadXor1>(x[e]));
+    for (int e = 0; e < 32; ++e)
+      x[e] = quad_perm_src<kQuadXor1>(x[e]) + __uint_as_float(__float_as_uint(x[e]) ^ sgn);
   }
   // half-width 64: partner is lane ^ 2
   {
-    const float sgn = (quarter & 2) ? -1.0f : 1.0f;
+    const uint32_t sgn = (quarter & 2) ? 0x80000000u : 0u;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = __builtin_fmaf(x[e], sgn, quad_swap<kQuadXor2>(x[e]));
+    for (int e = 0; e < 32; ++e)
+      x[e] = quad_perm_src<kQuadXor2>(x[e]) + __uint_as_float(__float_as_uint(x[e]) ^ sgn);
   }
   // m = max |y| over the 128 coordinates (exact), t = m / 2
   float m = 0.0f;
 #pragma unroll
   for (int e = 0; e < 32; ++e) m = fmaxf(m, fabsf(x[e]));
-  m = fmaxf(m, quad_swap<kQuadXor1>(m));
-  m = fmaxf(m, quad_swap<kQuadXor2>(m));
+  m = fmaxf(m, quad_perm_src<kQuadXor1>(m));
+  m = fmaxf(m, quad_perm_src<kQuadXor2>(m));
   const float t = 0.5f * m;
   // code = [y >= -t] + [y >= 0] + [y >= t]; low bit = XOR of the three tests,
   // high bit = [y >= 0].  Each test is the sign bit of an exactly-signed value:
@@ -98,7 +108,8 @@ __device__ __forceinline__ void encode_quad(float (&x)[32], int quarter, uint32_
   for (int e = 31; e >= 0; --e) {
     const float y = x[e] + 0.0f;
     const uint32_t sy = __float_as_uint(y);
-    const uint32_t sl = __float_as_uint(y + t) ^ sy ^ __float_as_uint(y - t);
+    // (one three-input XOR: truth table 0x96)
+    const uint32_t sl = __builtin_amdgcn_bitop3_b32(__float_as_uint(y + t), sy, __float_as_uint(y - t), 0x96);
     nlo = __builtin_amdgcn_alignbit(nlo, sl, 31);
     nhi = __builtin_amdgcn_alignbit(nhi, sy, 31);
   }
