@@ -139,6 +139,18 @@ def _ptr(t, name, itemsize=None, optional=False):
     return t.data_ptr()
 
 
+def _shape(t, name, shape, device=None):
+    """Raise unless t (if given) has exactly `shape` and lives on `device`: the
+    kernels index every buffer by the dims, so a short buffer would be written
+    past its end rather than rejected."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, [int(x) for x in shape], list(t.shape)))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, the other tensors on %s" % (name, t.device, device))
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -155,15 +167,27 @@ def _check(status, where):
 def encode_keys(k, end, codes, start=None, stream=None, num_q_heads=None, pages=None):
     """Encode keys at positions [start[b], end[b]) of k [B][Hkv][cap][128] into codes [B][Hkv][cap][32]
     (with `pages`: of the pools k [num_pages][Hkv][page][128] into codes [num_pages][Hkv][page][32])."""
+    if k.dim() != 4:
+        raise ValueError("k must be 4-D")
+    dev = k.device
     if pages is None:
         B, Hkv, cap, hd = k.shape
+        _shape(codes, "codes", (B, Hkv, cap, CODE_BYTES), dev)
+        _shape(end, "end", (B,), dev)
+        _shape(start, "start", (B,), dev)
         d = dims(B, num_q_heads or Hkv, Hkv, cap, hd)
         st = _lib.adamas_encode_keys(ctypes.byref(d), _ptr(k, "k", 2), _ptr(start, "start", 4, optional=True),
                                      _ptr(end, "end", 4), _ptr(codes, "codes", 1), _stream(stream))
         _check(st, "adamas_encode_keys")
         return
-    num_pages, Hkv, _, hd = k.shape
+    num_pages, Hkv, page, hd = k.shape
     B = pages.table.shape[0]
+    if page != pages.page_size:
+        raise ValueError("the k pool holds pages of %d positions, the page table %d" % (page, pages.page_size))
+    _shape(codes, "codes", (num_pages, Hkv, page, CODE_BYTES), dev)
+    _shape(end, "end", (B,), dev)
+    _shape(start, "start", (B,), dev)
+    _shape(pages.table, "block_table", pages.table.shape, dev)
     d = dims(B, num_q_heads or Hkv, Hkv, pages.capacity, hd)
     pc = pages.c(num_pages)
     st = _lib.adamas_paged_encode_keys(ctypes.byref(d), ctypes.byref(pc), _ptr(k, "k", 2),
@@ -185,6 +209,33 @@ def alloc_workspace(nbytes, device=None):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device or "cuda")
 
 
+def _check_shapes(q, k, v, codes, kv_len, out, pages):
+    """The shapes shared by the decode step and dense attention: q [B][Hq][hd],
+    k and v [B][Hkv][cap][hd] (with pages: pools [num_pages][Hkv][page][hd]),
+    codes k's leading dims by 32, kv_len [B], out [B][Hq][128].  Returns B, Hq,
+    Hkv and the capacity."""
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [batch][q heads][head_dim] and k 4-D")
+    B, Hq, hd = q.shape
+    n0, Hkv, rows, _ = k.shape
+    dev = q.device
+    _shape(k, "k", (n0, Hkv, rows, hd), dev)
+    _shape(v, "v", k.shape, dev)
+    _shape(codes, "codes", (n0, Hkv, rows, CODE_BYTES), dev)
+    _shape(kv_len, "kv_len", (B,), dev)
+    _shape(out, "out", (B, Hq, HEAD_DIM), dev)
+    if pages is None:
+        if n0 != B:
+            raise ValueError("k has %d sequences, q %d" % (n0, B))
+        return B, Hq, Hkv, rows
+    if rows != pages.page_size:
+        raise ValueError("the k pool holds pages of %d positions, the page table %d" % (rows, pages.page_size))
+    if pages.table.shape[0] != B:
+        raise ValueError("the page table has %d rows, q %d sequences" % (pages.table.shape[0], B))
+    _shape(pages.table, "block_table", pages.table.shape, dev)
+    return B, Hq, Hkv, pages.capacity
+
+
 def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=None, dist=None, q_codes=None,
                 stream=None, append=False, sink=None, recent=None, mask=None, pages=None):
     """One Adamas decode step; writes out [B][Hq][128] fp32 (and the optional outputs).
@@ -194,10 +245,15 @@ def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=N
     recent / mask (int32 [B][words] device bitmap, bit p % 32 of word p / 32)
     calls adamas_forced_decode_step with those forced positions.  `pages`
     (a Pages) calls adamas_paged_decode_step: k, v and codes are then pools."""
-    B, Hq, hd = q.shape
-    n0, Hkv, cap, _ = k.shape
-    if pages is not None:
-        cap = pages.capacity
+    B, Hq, Hkv, cap = _check_shapes(q, k, v, codes, kv_len, out, pages)
+    hd = q.shape[2]
+    _shape(sel_idx, "sel_idx", (B, Hq, int(budget)), q.device)
+    _shape(dist, "dist", (B, Hq, cap), q.device)
+    _shape(q_codes, "q_codes", (B, Hq, CODE_BYTES), q.device)
+    if mask is not None:
+        if mask.dim() != 2:
+            raise ValueError("mask must be [batch][words]")
+        _shape(mask, "mask", (B, mask.shape[1]), q.device)
     d = dims(B, Hq, Hkv, cap, hd)
     tail = (_ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2), _ptr(codes, "codes", 1), _ptr(kv_len, "kv_len", 4),
             int(budget), float(scale), _ptr(out, "out", 4), _ptr(sel_idx, "sel_idx", 4, optional=True),
@@ -210,15 +266,13 @@ def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=N
         return
     f = None
     if forced:
-        if mask is not None and mask.dim() != 2:
-            raise ValueError("mask must be [batch][words]")
         f = Forced(int(sink or 0), int(recent or 0), _ptr(mask, "mask", 4, optional=True),
                    0 if mask is None else int(mask.shape[1]))
     if pages is None:
         st = _lib.adamas_forced_decode_step(ctypes.byref(d), ctypes.byref(f), 1 if append else 0, *tail)
         _check(st, "adamas_forced_decode_step")
         return
-    pc = pages.c(n0)
+    pc = pages.c(k.shape[0])
     st = _lib.adamas_paged_decode_step(ctypes.byref(d), ctypes.byref(pc), ctypes.byref(f) if f is not None else None,
                                        1 if append else 0, *tail)
     _check(st, "adamas_paged_decode_step")
@@ -227,18 +281,15 @@ def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=N
 def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None, pages=None):
     """Dense decode attention over every position < kv_len[b]; writes out [B][Hq][128] fp32
     (with `pages`: k and v are pools, see Pages)."""
-    B, Hq, hd = q.shape
-    n0, Hkv, cap, _ = k.shape
-    if pages is not None:
-        cap = pages.capacity
-    d = dims(B, Hq, Hkv, cap, hd)
+    B, Hq, Hkv, cap = _check_shapes(q, k, v, None, kv_len, out, pages)
+    d = dims(B, Hq, Hkv, cap, q.shape[2])
     tail = (_ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2), _ptr(kv_len, "kv_len", 4), float(scale),
             _ptr(out, "out", 4), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
             _stream(stream))
     if pages is None:
         _check(_lib.dense_decode_attention(ctypes.byref(d), *tail), "dense_decode_attention")
         return
-    pc = pages.c(n0)
+    pc = pages.c(k.shape[0])
     _check(_lib.dense_paged_decode_attention(ctypes.byref(d), ctypes.byref(pc), *tail),
            "dense_paged_decode_attention")
 

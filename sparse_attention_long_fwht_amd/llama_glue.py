@@ -31,6 +31,13 @@ def _p(t):
     return t.data_ptr()
 
 
+def _shape(t, name, shape):
+    """The kernels index by the dims they are given: a buffer of another shape
+    is rejected rather than read or written past its end."""
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, [int(x) for x in shape], list(t.shape)))
+
+
 def _s():
     return torch.cuda.current_stream().cuda_stream
 
@@ -43,19 +50,31 @@ def _check(rc, name):
 def add_rmsnorm(x, delta, x_out, w, h, eps):
     """x_out = x + delta (delta may be None; x_out may be x or None); h = rmsnorm(x_out) * w."""
     rows, hidden = x.shape
+    _shape(delta, "delta", x.shape)
+    _shape(x_out, "x_out", x.shape)
+    _shape(w, "w", (hidden,))
+    _shape(h, "h", x.shape)
     _check(_lib.llama_add_rmsnorm(_p(x), _p(delta), _p(x_out), _p(w), _p(h), rows, hidden, float(eps), _s()),
            "llama_add_rmsnorm")
 
 
 def rope_append(qkv, pos, inv_freq, q_out, k_cache, v_cache):
     """Rotary q/k of the new token at pos[b], q to q_out, k/v rows into the caches."""
-    B, Hkv, cap, _ = k_cache.shape
+    B, Hkv, cap, hd = k_cache.shape
+    Hq = q_out.shape[1]
+    _shape(k_cache, "k_cache", (B, Hkv, cap, 128))
+    _shape(v_cache, "v_cache", k_cache.shape)
+    _shape(q_out, "q_out", (B, Hq, 128))
+    _shape(qkv, "qkv", (B, (Hq + 2 * Hkv) * 128))
+    _shape(pos, "pos", (B,))
+    _shape(inv_freq, "inv_freq", (64,))
     _check(_lib.llama_rope_append(_p(qkv), _p(pos), _p(inv_freq), _p(q_out), _p(k_cache), _p(v_cache), B,
-                                  q_out.shape[1], Hkv, cap, _s()), "llama_rope_append")
+                                  Hq, Hkv, cap, _s()), "llama_rope_append")
 
 
 def silu_mul(gu, out):
     rows, ffn = out.shape
+    _shape(gu, "gu", (rows, 2 * ffn))
     _check(_lib.llama_silu_mul(_p(gu), _p(out), rows, ffn, _s()), "llama_silu_mul")
 
 

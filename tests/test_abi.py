@@ -185,6 +185,17 @@ def test_glue_library_exports_and_rejects():
     assert lib.llama_rope_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 8, 100, None) == 1
     assert lib.llama_silu_mul(FAKE, FAKE, 1, 100, None) == 1  # ffn % 8
     assert lib.llama_silu_mul(None, FAKE, 1, 128, None) == 1
+    # the binding rejects buffers that do not match the dims before any call
+    import torch
+    x = torch.zeros((2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="gu must have shape"):
+        G.silu_mul(torch.zeros((2, 64), dtype=torch.bfloat16), x)
+    with pytest.raises(ValueError, match="w must have shape"):
+        G.add_rmsnorm(x, None, x, torch.zeros(32, dtype=torch.bfloat16), x, 1e-5)
+    kc = torch.zeros((2, 1, 16, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="qkv must have shape"):
+        G.rope_append(torch.zeros((2, 128), dtype=torch.bfloat16), torch.zeros(2, dtype=torch.int32),
+                      torch.zeros(64), torch.zeros((2, 2, 128), dtype=torch.bfloat16), kc, kc)
 
 
 def test_package_has_no_cpu_fallback():
@@ -210,7 +221,8 @@ def test_bench_refuses_several_gpus():
 
 def test_binding_rejects_host_and_misshapen_tensors(A):
     """The binding checks its tensors before any library call: host tensors,
-    non-contiguous views and wrong element sizes raise ValueError (no GPU needed)."""
+    non-contiguous views, wrong element sizes and buffers whose shapes do not
+    match the dims raise ValueError (no GPU needed)."""
     import torch
     q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
     k = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16)
@@ -226,6 +238,35 @@ def test_binding_rejects_host_and_misshapen_tensors(A):
         A.dense_decode_attention(q, k, k, kv_len, 0.1, out, ws)
     with pytest.raises(ValueError):
         A.Pages(torch.zeros((1, 4), dtype=torch.int64), 16)  # block table must be int32 [B][pages]
+    # buffers that do not match the dims are rejected before any pointer is taken
+    # (the kernels would index past their ends)
+    with pytest.raises(ValueError, match="out must have shape"):
+        A.decode_step(q, k, k, codes, kv_len, 8, 0.1, torch.zeros((1, 2, 128)), ws)
+    with pytest.raises(ValueError, match="sel_idx must have shape"):
+        A.decode_step(q, k, k, codes, kv_len, 8, 0.1, out, ws, sel_idx=torch.zeros((1, 4, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="dist must have shape"):
+        A.decode_step(q, k, k, codes, kv_len, 8, 0.1, out, ws, dist=torch.zeros((1, 4, 32), dtype=torch.int16))
+    with pytest.raises(ValueError, match="q_codes must have shape"):
+        A.decode_step(q, k, k, codes, kv_len, 8, 0.1, out, ws, q_codes=torch.zeros((1, 4, 16), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="codes must have shape"):
+        A.decode_step(q, k, k, codes[:, :, :32], kv_len, 8, 0.1, out, ws)
+    with pytest.raises(ValueError, match="v must have shape"):
+        A.decode_step(q, k, k[:, :1], codes, kv_len, 8, 0.1, out, ws)
+    with pytest.raises(ValueError, match="kv_len must have shape"):
+        A.dense_decode_attention(q, k, k, torch.zeros((2,), dtype=torch.int32), 0.1, out, ws)
+    with pytest.raises(ValueError, match="sequences"):
+        A.decode_step(q, torch.zeros((2, 2, 64, 128), dtype=torch.bfloat16), torch.zeros((2, 2, 64, 128)),
+                      torch.zeros((2, 2, 64, 32), dtype=torch.uint8), kv_len, 8, 0.1, out, ws)
+    with pytest.raises(ValueError, match="codes must have shape"):
+        A.encode_keys(k, kv_len, codes[:, :1])
+    with pytest.raises(ValueError, match="mask must have shape"):
+        A.decode_step(q, k, k, codes, kv_len, 8, 0.1, out, ws, mask=torch.zeros((2, 2), dtype=torch.int32))
+    table = torch.zeros((1, 4), dtype=torch.int32)
+    with pytest.raises(ValueError, match="pages of 64 positions"):
+        A.decode_step(q, k, k, codes, kv_len, 8, 0.1, out, ws, pages=A.Pages(table, 16))
+    with pytest.raises(ValueError, match="page table has 1 rows"):
+        A.decode_step(torch.zeros((2, 4, 128), dtype=torch.bfloat16), k, k, codes, torch.zeros(2, dtype=torch.int32),
+                      8, 0.1, torch.zeros((2, 4, 128)), ws, pages=A.Pages(table, 64))
 
 
 def test_bench_reads_committed_counters():
