@@ -152,8 +152,8 @@ def attention_rows(q, k_head, v_head, pos, scale):
     kh = _c(k_head, np.uint16)
     vh = _c(v_head, np.uint16)
     p = _c(pos, np.int32)
-    assert q.shape == (128,) and kh.shape[-1] == 128 and vh.shape == kh.shape and p.size >= 1
-    assert p.min() >= 0 and p.max() < kh.shape[0]
+    assert q.shape == (128,) and kh.shape[-1] == 128 and vh.shape == kh.shape
+    assert p.size == 0 or (p.min() >= 0 and p.max() < kh.shape[0])  # (no rows: the zero vector)
     out = np.empty(128, np.float32)
     lib().oracle_attention_rows(_ptr(q, _u16p), _ptr(kh, _u16p), _ptr(vh, _u16p), _ptr(p, _i32p),
                                 int(p.size), float(scale), _ptr(out, _f32p))

@@ -251,10 +251,16 @@ int oracle_topk_forced(const uint16_t* dist, const uint8_t* force, int32_t len, 
  * ([v2-abs]: the selected positions gather the original K/V for sparse
  * attention).  s_p = scale * sum_i q_i K[p][i]; o = sum_p softmax(s)_p V[p].
  * Inputs are the original bf16 values; all arithmetic is fp64; out is rounded
- * to fp32 once at the end.  n must be >= 1.
+ * to fp32 once at the end.  n == 0 (a sequence with no cached position) gives
+ * the zero vector: the pages never attend over an empty set, and the empty sum
+ * of weighted values is the reading taken (an idle slot of a batch).
  */
 void oracle_attention_rows(const uint16_t* q, const uint16_t* kh, const uint16_t* vh,
                            const int32_t* pos, int32_t n, double scale, float* out) {
+  if (n <= 0) {
+    for (int i = 0; i < HD; ++i) out[i] = 0.0f;
+    return;
+  }
   double* s = (double*)malloc(sizeof(double) * (size_t)n);
   double qd[HD];
   for (int i = 0; i < HD; ++i) qd[i] = (double)oracle_bf16_to_f32(q[i]);
@@ -322,7 +328,9 @@ int oracle_encode_keys(int32_t B, int32_t Hkv, int32_t cap, const uint16_t* k,
  *      fit); preferred are the positions whose bit p % 32 of
  *      mask[b * mask_words + p / 32] is set (mask may be NULL)
  *   4. exact fp64 softmax attention over the selected original K/V rows -> out
- * g = h / (Hq / Hkv).  threads > 1 runs independent (b, h) pairs in parallel
+ * g = h / (Hq / Hkv).  0 <= kv_len[b] <= cap; a sequence with kv_len[b] = 0
+ * selects nothing (sel_idx all -1) and gets the zero vector (see
+ * oracle_attention_rows).  threads > 1 runs independent (b, h) pairs in parallel
  * (no change to any arithmetic).  Returns 0, or 1 on invalid arguments
  * (including sink < 0, recent < 0, sink + recent > budget, or a mask with
  * fewer than ceil(cap / 32) words per batch entry).
@@ -337,7 +345,7 @@ int oracle_decode_step_forced(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
   if (sink < 0 || recent < 0 || (int64_t)sink + recent > budget) return 1;
   if (mask && (int64_t)mask_words * 32 < cap) return 1;
   for (int32_t b = 0; b < B; ++b)
-    if (kv_len[b] < 1 || kv_len[b] > cap) return 1;
+    if (kv_len[b] < 0 || kv_len[b] > cap) return 1;
   const int32_t group = Hq / Hkv;
   const int32_t pairs = B * Hq;
   (void)threads;
@@ -347,15 +355,16 @@ int oracle_decode_step_forced(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
   for (int32_t bh = 0; bh < pairs; ++bh) {
     const int32_t b = bh / Hq, h = bh % Hq, g = h / group;
     const int32_t len = kv_len[b];
+    const size_t nalloc = (size_t)(len > 0 ? len : 1);
     uint8_t qc[CODE_BYTES];
     oracle_encode_vector(q + (size_t)bh * HD, qc);
     if (q_codes) memcpy(q_codes + (size_t)bh * CODE_BYTES, qc, CODE_BYTES);
     const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)cap;
-    uint16_t* d = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)len);
+    uint16_t* d = (uint16_t*)malloc(sizeof(uint16_t) * nalloc);
     for (int32_t p = 0; p < len; ++p)
       d[p] = (uint16_t)oracle_distance(qc, codes + (kvbase + (size_t)p) * CODE_BYTES);
     if (dist) memcpy(dist + (size_t)bh * cap, d, sizeof(uint16_t) * (size_t)len);
-    uint8_t* f = (uint8_t*)malloc((size_t)len);
+    uint8_t* f = (uint8_t*)malloc(nalloc);
     for (int32_t p = 0; p < len; ++p) {
       const int in_mask = mask ? (int)((mask[(size_t)b * mask_words + (size_t)(p / 32)] >> (p % 32)) & 1u) : 0;
       f[p] = (uint8_t)((p < sink || p >= len - recent) ? 2 : (in_mask ? 1 : 0));
@@ -384,14 +393,15 @@ int oracle_decode_step(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap,
 
 /*
  * Dense decode attention, the comparison baseline: the attention of step 4 over
- * every position p < kv_len[b].  Returns 0, or 1 on invalid arguments.
+ * every position p < kv_len[b] (the zero vector where kv_len[b] = 0).  Returns 0,
+ * or 1 on invalid arguments.
  */
 int oracle_dense_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap, const uint16_t* q,
                            const uint16_t* k, const uint16_t* v, const int32_t* kv_len,
                            float scale, float* out, int32_t threads) {
   if (bad_dims(B, Hq, Hkv, cap)) return 1;
   for (int32_t b = 0; b < B; ++b)
-    if (kv_len[b] < 1 || kv_len[b] > cap) return 1;
+    if (kv_len[b] < 0 || kv_len[b] > cap) return 1;
   const int32_t group = Hq / Hkv;
   const int32_t pairs = B * Hq;
   (void)threads;
@@ -402,7 +412,7 @@ int oracle_dense_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap, cons
     const int32_t b = bh / Hq, h = bh % Hq, g = h / group;
     const int32_t len = kv_len[b];
     const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)cap;
-    int32_t* all = (int32_t*)malloc(sizeof(int32_t) * (size_t)len);
+    int32_t* all = (int32_t*)malloc(sizeof(int32_t) * (size_t)(len > 0 ? len : 1));
     for (int32_t p = 0; p < len; ++p) all[p] = p;
     oracle_attention_rows(q + (size_t)bh * HD, k + kvbase * HD, v + kvbase * HD, all, len,
                           (double)scale, out + (size_t)bh * HD);

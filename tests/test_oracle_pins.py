@@ -570,6 +570,27 @@ def test_decode_batch_is_independent(oracle_mod):
         assert np.array_equal(d1[0], dist[b]) and np.array_equal(q1[0], qc[b])
 
 
+def test_decode_empty_sequence(oracle_mod):
+    """A sequence with no cached position (an idle batch slot) selects nothing
+    and gets the zero vector, by the empty-sum reading; the other entries are
+    what they are alone, with and without forced positions, and dense attention
+    agrees."""
+    wl = small_case()
+    codes = oracle_mod.encode_keys(wl.k, wl.kv_len)
+    lens = wl.kv_len.copy()
+    lens[0] = 0
+    for kw in ({}, dict(sink=2, recent=3)):
+        out, sel, dist, _ = oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, lens, wl.budget, wl.scale, **kw)
+        assert np.all(out[0] == 0.0) and np.all(sel[0] == -1) and np.all(dist[0] == 0)
+        o1, s1, d1, _ = oracle_mod.decode_step(wl.q[1:], wl.k[1:], wl.v[1:], codes[1:], lens[1:], wl.budget,
+                                               wl.scale, **kw)
+        assert np.array_equal(o1, out[1:]) and np.array_equal(s1, sel[1:]) and np.array_equal(d1, dist[1:])
+    dense = oracle_mod.dense_attention(wl.q, wl.k, wl.v, lens, wl.scale)
+    assert np.all(dense[0] == 0.0)
+    assert np.array_equal(dense[1:], oracle_mod.dense_attention(wl.q[1:], wl.k[1:], wl.v[1:], lens[1:], wl.scale))
+    assert np.all(oracle_mod.attention_rows(wl.q[0, 0], wl.k[0, 0], wl.v[0, 0], np.zeros(0, np.int32), 0.1) == 0.0)
+
+
 def test_decode_rederived_in_numpy(oracle_mod):
     """Independent numpy path for the step after encoding: unpackbits distances,
     lexsort top-k, fp64 softmax attention."""
@@ -617,7 +638,9 @@ def test_invalid_arguments_rejected(oracle_mod):
     wl = small_case()
     codes = oracle_mod.encode_keys(wl.k, wl.kv_len)
     with pytest.raises(ValueError):
-        oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, np.array([0, 5], np.int32), 8, 0.1)
+        oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, np.array([-1, 5], np.int32), 8, 0.1)
+    with pytest.raises(ValueError):
+        oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, np.array([wl.cap + 1, 5], np.int32), 8, 0.1)
     with pytest.raises(ValueError):
         oracle_mod.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, 0, 0.1)
     with pytest.raises(ValueError):
