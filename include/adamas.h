@@ -110,7 +110,10 @@ size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget);
  *   q          bf16 [batch][num_q_heads][128]
  *   k, v       bf16 [batch][num_kv_heads][capacity][128] (the original cache)
  *   codes      uint8 [batch][num_kv_heads][capacity][32], valid for p < kv_len[b]
- *   kv_len     int32 [batch] device array; precondition 1 <= kv_len[b] <= capacity
+ *   kv_len     int32 [batch] device array; precondition 0 <= kv_len[b] <= capacity.
+ *              kv_len[b] = 0 (an idle slot of the batch): nothing is selected
+ *              (sel_idx row all -1) and out[b][h] = 0, the empty sum (the pages
+ *              never attend over an empty set; this is the reading taken)
  *   budget     token budget k >= 1 (may exceed kv_len[b]: then every position is kept)
  *   scale      softmax scale
  *   out        fp32 [batch][num_q_heads][128] (output)
@@ -142,7 +145,8 @@ adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void
  * (The first kernel of the step encodes the key in the block that scans its
  * position, so the append costs no separate launch.)  Same arguments, layouts,
  * workspace size and errors as adamas_decode_step; `codes` is written at
- * positions kv_len[b]-1 only.  Precondition: K[b][g][kv_len[b]-1] holds the new key.
+ * positions kv_len[b]-1 only (nothing where kv_len[b] = 0).  Precondition:
+ * K[b][g][kv_len[b]-1] holds the new key.
  */
 adamas_status adamas_append_decode_step(const adamas_dims* d, const void* q, const void* k,
                                         const void* v, uint8_t* codes, const int32_t* kv_len,
@@ -199,8 +203,8 @@ size_t dense_decode_workspace_size(const adamas_dims* d);
 /*
  * Dense decode attention, the comparison baseline the pages measure Adamas
  * against: out[b][h] = softmax attention of q[b][h] over every position
- * p < kv_len[b] of KV head g = h / (Hq/Hkv).  Same layouts, preconditions and
- * errors as adamas_decode_step.
+ * p < kv_len[b] of KV head g = h / (Hq/Hkv) (0 where kv_len[b] = 0).  Same
+ * layouts, preconditions and errors as adamas_decode_step.
  */
 adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const void* k, const void* v,
                                      const int32_t* kv_len, float scale, float* out, void* workspace,

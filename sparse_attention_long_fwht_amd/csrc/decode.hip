@@ -616,6 +616,14 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   for (int u = 0; u < 4; ++u) t0[u] = *rec_src(min(u * kSAThreads + tid, n16 - 1));
   asm volatile("" : "+s"(len_raw));
   const int len = min(len_raw, a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
+  if (len <= 0) {  // no cached position: nothing selected, attention over the empty set is the zero vector
+    if (split == 0) {
+      if (tid < kHeadDim) a.out[(size_t)bh * kHeadDim + tid] = 0.f;
+      if (a.sel_idx)
+        for (int i = tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
+    }
+    return;
+  }
   const int k_eff = min(a.budget, len);
   // Final ranks (ascending positions): the sinks [0, s_b), then the k_mid
   // ranked positions, then the recent window; the ranking below works on

@@ -288,8 +288,8 @@ __global__ __launch_bounds__(256) void dense_attend_kernel(AttendArgs a) {
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
   const int c = blockIdx.x;
-  const int len = a.kv_len[b];
-  const int nch_b = (len + a.chunk - 1) / a.chunk;
+  const int len = min(a.kv_len[b], a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
+  const int nch_b = (max(len, 0) + a.chunk - 1) / a.chunk;
   if (c >= nch_b) return;
   const int p0 = c * a.chunk;
   const int p1 = min(p0 + a.chunk, len);
@@ -307,8 +307,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int bg = blockIdx.x;
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
-  const int nch_b = (kv_len[b] + chunk - 1) / chunk;
+  // (clamped like the attend kernel's: the nch chunks cover the capacity)
+  const int nch_b = (max(min(kv_len[b], nch * chunk), 0) + chunk - 1) / chunk;
   const size_t bh0 = (size_t)b * Hq + (size_t)(g * R);
+  if (nch_b == 0) {  // no cached position: attention over the empty set is the zero vector
+    for (int i = threadIdx.x; i < R * kHeadDim; i += 256) out[bh0 * kHeadDim + i] = 0.f;
+    return;
+  }
   combine_group<R>(part + bh0 * nch * kPartFloats, nch, nch_b, out + bh0 * kHeadDim, s_w, s_l);
 }
 

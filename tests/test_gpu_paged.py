@@ -119,6 +119,20 @@ def test_paged_decode_ragged(env, page, budget):
     assert np.array_equal(sel, sel_c) and np.array_equal(out, out_c)
 
 
+def test_paged_empty_sequences(env):
+    """Idle slots (kv_len 0) in a paged batch: nothing selected, out 0, dense too."""
+    import dataclasses
+    A, torch, oracle = env
+    wl = W.llama(53, cap=3000, budget=64, B=4, Hq=8, Hkv=2, kv_len=np.array([3000, 1, 1537, 1], np.int32))
+    wl = dataclasses.replace(wl, kv_len=np.array([3000, 0, 1537, 0], np.int32))
+    case = PagedCase(wl, A, torch, 16, seed=9)
+    out, sel = check_paged(case, oracle, 64)
+    assert np.all(out[[1, 3]] == 0.0) and np.all(sel[[1, 3]] == -1)
+    dense = case.dense()
+    assert np.all(dense[[1, 3]] == 0.0)
+    assert_out_close(dense, oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale, threads=8))
+
+
 def test_paged_dense(env):
     A, torch, oracle = env
     wl = ragged(52, 64)

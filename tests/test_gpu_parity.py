@@ -8,6 +8,8 @@ edge cases (kv_len 1, budget 1, budget >= kv_len, heavy ties, boundary values of
 the bucketing), and the full configurations: tiny (1K), Llama-shaped 32K with
 budgets 128 and 1024, the batched ragged 16 x [16K, 32K] case and 512K.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -322,7 +324,7 @@ def check_append_decode(A, torch, oracle, wl, budget=None):
     key kv_len-1 and then match the oracle step on the complete codes."""
     budget = wl.budget if budget is None else budget
     case = DeviceCase(wl, A, torch, encode=False)
-    end_prev = to_dev(wl.kv_len - 1, torch)
+    end_prev = to_dev(np.maximum(wl.kv_len - 1, 0), torch)  # (an empty sequence has nothing to append)
     A.encode_keys(case.k, end_prev, case.codes)  # positions [0, len-1)
     out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device="cuda")
     sel = torch.empty((wl.B, wl.Hq, budget), dtype=torch.int32, device="cuda")
@@ -351,6 +353,40 @@ def test_append_decode_ragged(env):
     check_append_decode(A, torch, oracle, wl)
     wl = W.llama(42, cap=5000, budget=64, B=2, Hq=8, Hkv=1, kv_len=np.array([4097, 512], np.int32))
     check_append_decode(A, torch, oracle, wl)
+
+
+def with_empty_slots(seed, budget):
+    """Idle batch slots (kv_len 0) between a full, a ragged and a length-1
+    sequence (the workload is drawn with length 1 there, then emptied)."""
+    wl = W.llama(seed, cap=3000, budget=budget, B=5, Hq=8, Hkv=2, kv_len=np.array([3000, 1, 1537, 1, 1], np.int32))
+    return dataclasses.replace(wl, kv_len=np.array([3000, 0, 1537, 0, 1], np.int32))
+
+
+@pytest.mark.parametrize("variant", ["plain", "forced", "append", "dense"])
+def test_empty_sequences(env, variant):
+    """An empty sequence selects nothing (sel_idx all -1) and gets out exactly 0;
+    the other entries match the oracle as usual."""
+    A, torch, oracle = env
+    wl = with_empty_slots(43, 96)
+    if variant == "dense":
+        out = DeviceCase(wl, A, torch, encode=False).dense()
+        assert np.all(out[[1, 3]] == 0.0)
+        assert_out_close(out, oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale))
+    elif variant == "append":
+        check_append_decode(A, torch, oracle, wl)
+    else:
+        case = DeviceCase(wl, A, torch)
+        kw = dict(sink=4, recent=16) if variant == "forced" else {}
+        check_decode(case, oracle, **kw)
+        out, sel, _, _ = case.decode(wl.budget, want_debug=False, **kw)
+        assert np.all(out[[1, 3]] == 0.0) and np.all(sel[[1, 3]] == -1)
+
+
+def test_empty_sequences_several_splits(env):
+    """The same with a budget that spreads a head over several blocks."""
+    A, torch, oracle = env
+    wl = with_empty_slots(44, 1024)
+    check_decode(DeviceCase(wl, A, torch), oracle, budget=1024)
 
 
 def test_append_decode_llama32k(env):
