@@ -34,6 +34,11 @@ if ROOT not in sys.path:
 
 METRIC = "decode-step sparse-attn latency (us) and achieved HBM GB/s vs peak, 32K ctx"
 HBM_PEAK_GBS = 8000.0
+# The secondary workloads: name -> (workload maker, rotating cache copies).
+OTHER_WORKLOADS = {
+    "batched16_ragged16k-32k_b256": (lambda W, seed: W.batched(seed), 3),
+    "long512k_b1024": (lambda W, seed: W.llama(seed, cap=524288, budget=1024, name="long512k"), 2),
+}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -61,6 +66,13 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: write the counter summary of the dominant kernel under profiles/ from the CSV "
                          "output of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of PMC_COMMAND")
+    ap.add_argument("--only-workload", choices=sorted(OTHER_WORKLOADS),
+                    help="instead of the headline: only this secondary workload's step and dense baseline, one "
+                         "JSON line (the program SQ_COMMAND profiles)")
+    ap.add_argument("--summarize-sq", nargs=3, metavar=("WORKLOAD", "DIR_A", "DIR_B"),
+                    help="no GPU: write the SQ counter summary (occupancy, VALU, LDS bank conflicts per kernel) "
+                         "under profiles/ from the CSV output of the two SQ_COMMAND passes on WORKLOAD "
+                         "(llama32k_b128 or a secondary workload's name)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
                     help="no GPU: write the kernel-trace summary under profiles/ from the CSV output of "
                          "TRACE_COMMAND and the JSON line of a plain bench.py run on the same box and sources")
@@ -95,6 +107,8 @@ def main():
         return summarize_counters(*args.summarize_counters)
     if args.summarize_trace:
         return summarize_trace(*args.summarize_trace)
+    if args.summarize_sq:
+        return summarize_sq(*args.summarize_sq)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the Adamas decode step runs and is timed on a single MI355X; "
@@ -115,6 +129,11 @@ def main():
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     if args.sweep:
         return sweep(A, W, np, torch, dev, log)
+    if args.only_workload:
+        make, ncopy = OTHER_WORKLOADS[args.only_workload]
+        r = other_workload(A, np, torch, dev, make(W, args.seed), ncopy)
+        print(json.dumps(dict(r, workload=args.only_workload)), flush=True)
+        return
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
@@ -325,9 +344,8 @@ def main():
         del copies, g_cold, g_warm, g_dense, g_enc
         torch.cuda.empty_cache()
         # the batched and long-context workloads
-        for name, wl_x, ncopy in (("batched16_ragged16k-32k_b256", W.batched(args.seed), 3),
-                                  ("long512k_b1024", W.llama(args.seed, cap=524288, budget=1024, name="long512k"), 2)):
-            extra[name] = other_workload(A, np, torch, dev, wl_x, ncopy)
+        for name, (make, ncopy) in OTHER_WORKLOADS.items():
+            extra[name] = other_workload(A, np, torch, dev, make(W, args.seed), ncopy)
             log("[bench] %s: %s" % (name, extra[name]))
             torch.cuda.empty_cache()
 
@@ -475,6 +493,91 @@ def summarize_counters(fetch_dir, write_dir):
             fh.write("\n".join(text) + "\n")
         lines.append("%s: %.0f bytes/launch" % (kernel, hbm))
     print("\n".join(lines))
+
+
+# Two SQ counter passes per workload (each within one pass's limits: at most
+# 8 SQ and 2 GRBM counters); GRBM_GUI_ACTIVE in both, for the normalisation.
+SQ_PASSES = {
+    "a": "SQ_WAVES,SQ_WAVE_CYCLES,SQ_BUSY_CU_CYCLES,SQ_ACTIVE_INST_VALU,GRBM_GUI_ACTIVE",
+    "b": "SQ_INSTS_VALU,SQ_INSTS_LDS,SQ_LDS_BANK_CONFLICT,SQ_LDS_IDX_ACTIVE,GRBM_GUI_ACTIVE",
+}
+SQ_ARGS = {WORKLOAD_TAG: "--steps 8 --warmup 2 --copies 4 --no-extra --no-cpu"}
+SQ_ARGS.update({name: "--only-workload " + name for name in OTHER_WORKLOADS})
+SQ_COMMAND = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc {counters} "
+              "--output-format csv -d gpurun_out/sq_{workload}_{p} -o pmc -- python3 bench.py {args}")
+CU_NUM = 256
+
+
+def summarize_sq(workload, dir_a, dir_b):
+    """Per-kernel SQ counter summary of the step's kernels (and the dense
+    baseline's) on one workload, with rocprofv3's own derived metrics."""
+    import csv
+    import glob
+    if workload not in SQ_ARGS:
+        raise SystemExit("unknown workload %r (one of %s)" % (workload, sorted(SQ_ARGS)))
+    per = {}    # (kernel, pass, dispatch) -> {counter: value}
+    wpb = {}    # kernel -> waves per block
+    dur = {}    # kernel -> [us per dispatch, under the profiler]
+    for p, d in (("a", dir_a), ("b", dir_b)):
+        files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+        if not files:
+            raise SystemExit("no counter_collection.csv under " + d)
+        for f in files:
+            for r in csv.DictReader(open(f, newline="")):
+                name = r["Kernel_Name"]
+                if "adamas::" not in name:
+                    continue
+                k = name.split("(")[0].replace("void adamas::", "")
+                c, v = r["Counter_Name"], float(r["Counter_Value"])
+                acc = per.setdefault((k, p, r["Dispatch_Id"]), {})
+                # GRBM_GUI_ACTIVE: the busy cycles of the device (the largest
+                # instance); SQ counters: summed over shader engines and XCDs
+                acc[c] = max(acc.get(c, 0.0), v) if c == "GRBM_GUI_ACTIVE" else acc.get(c, 0.0) + v
+                wpb[k] = int(r["Workgroup_Size"]) // 64
+                if p == "a" and c == "SQ_WAVES":
+                    dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def mean(k, p, c):
+        vals = [a[c] for (kk, pp, _), a in per.items() if kk == k and pp == p and c in a]
+        return sum(vals) / len(vals) if vals else float("nan"), len(vals)
+
+    cmd = {p: SQ_COMMAND.format(counters=SQ_PASSES[p], workload=workload, p=p, args=SQ_ARGS[workload])
+           for p in SQ_PASSES}
+    text = ["rocprofv3 SQ counters per kernel, workload %s (the step's kernels and the dense baseline's)" % workload,
+            "", "command (pass a): " + cmd["a"], "command (pass b): " + cmd["b"], "",
+            "Under --pmc every dispatch runs alone and GRBM_GUI_ACTIVE also counts the profiler's own time around",
+            "it, so nothing below is normalised by it.  SQ_WAVE_CYCLES, SQ_BUSY_CU_CYCLES and SQ_ACTIVE_INST_VALU",
+            "are quad-cycles summed over SIMDs; per kernel, means over its dispatches:",
+            "  us      = End - Start timestamp of the dispatch under the profiler",
+            "  w/SIMD  = SQ_WAVE_CYCLES / SQ_BUSY_CU_CYCLES: waves resident per SIMD while its CU has work (of 8)",
+            "  VALU/cy = SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES: wave-cycles on VALU instructions per busy SIMD",
+            "            cycle (the issue share of the SIMD when at most one wave's VALU instruction is in flight)",
+            "  VALU/w, LDS/w = SQ_INSTS_VALU, SQ_INSTS_LDS per wave",
+            "  cf/LDS  = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS: bank-conflict stall cycles per LDS instruction",
+            "  cf/act  = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE: share of LDS-busy cycles lost to bank conflicts",
+            "",
+            "%-32s %5s %7s %5s %8s %7s %7s %9s %7s %7s %7s" % (
+                "kernel", "disp", "waves", "w/blk", "us", "w/SIMD", "VALU/cy", "VALU/w", "LDS/w", "cf/LDS",
+                "cf/act")]
+    for k in sorted({kk for kk, _, _ in per}):
+        waves, n = mean(k, "a", "SQ_WAVES")
+        wcyc, _ = mean(k, "a", "SQ_WAVE_CYCLES")
+        busy, _ = mean(k, "a", "SQ_BUSY_CU_CYCLES")
+        valu_act, _ = mean(k, "a", "SQ_ACTIVE_INST_VALU")
+        valu, _ = mean(k, "b", "SQ_INSTS_VALU")
+        lds, _ = mean(k, "b", "SQ_INSTS_LDS")
+        conf, _ = mean(k, "b", "SQ_LDS_BANK_CONFLICT")
+        lact, _ = mean(k, "b", "SQ_LDS_IDX_ACTIVE")
+        us = sum(dur[k]) / len(dur[k])
+        text.append("%-32s %5d %7.0f %5d %8.2f %7.2f %7.3f %9.1f %7.1f %7.2f %7.3f" % (
+            k[:32], n, waves, wpb[k], us, wcyc / busy, valu_act / busy, valu / waves, lds / waves,
+            conf / lds if lds else 0.0, conf / lact if lact else 0.0))
+    text += ["", "source sha256[:16]: %s  (%s)" % (source_hash("scan"), ", ".join(KERNEL_SOURCES["scan"]))]
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    path = os.path.join(PROFILE_DIR, "sq_counters_%s.txt" % workload)
+    with open(path, "w") as fh:
+        fh.write("\n".join(text) + "\n")
+    print(path)
 
 
 def summarize_trace(trace_dir, bench_json):

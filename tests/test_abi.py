@@ -285,3 +285,42 @@ def test_bench_reads_committed_counters():
             assert got is not None and got > 0
         else:
             assert got is None
+
+
+def test_bench_summarizes_sq_counters(tmp_path, monkeypatch):
+    """The SQ counter summary reads rocprofv3's counter CSV (two passes), sums
+    the SQ counters over their dimensions, and derives the ratios it states."""
+    import csv
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod_sq", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    cols = ["Dispatch_Id", "Kernel_Name", "Workgroup_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
+            "End_Timestamp"]
+    passes = {"a": {"SQ_WAVES": 64, "SQ_WAVE_CYCLES": 800, "SQ_BUSY_CU_CYCLES": 400, "SQ_ACTIVE_INST_VALU": 100,
+                    "GRBM_GUI_ACTIVE": 9},
+              "b": {"SQ_INSTS_VALU": 6400, "SQ_INSTS_LDS": 640, "SQ_LDS_BANK_CONFLICT": 320,
+                    "SQ_LDS_IDX_ACTIVE": 1280, "GRBM_GUI_ACTIVE": 9}}
+    dirs = []
+    for p, counters in passes.items():
+        d = tmp_path / p
+        d.mkdir()
+        with open(d / "pmc_counter_collection.csv", "w", newline="") as fh:
+            w = csv.writer(fh)
+            w.writerow(cols)
+            for disp in (1, 2):
+                for c, v in counters.items():
+                    for half in (0.5, 0.5):  # two shader engines: summed
+                        w.writerow([disp, "void adamas::scan_kernel<4, false, false>(adamas::ScanArgs)", 512, c,
+                                    v * half if c != "GRBM_GUI_ACTIVE" else v, 1000, 8000])
+                w.writerow([disp, "__amd_rocclr_copyBuffer", 512, "SQ_WAVES", 1, 0, 1])
+        dirs.append(str(d))
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path / "out"))
+    bench.summarize_sq("llama32k_b128", *dirs)
+    text = open(tmp_path / "out" / "sq_counters_llama32k_b128.txt").read()
+    row = [line for line in text.splitlines() if line.startswith("scan_kernel<4, false, false>")]
+    assert len(row) == 1 and "copyBuffer" not in text
+    f = row[0].split()[-10:]
+    # dispatches, waves, waves/block, us, w/SIMD, VALU/cy, VALU/w, LDS/w, cf/LDS, cf/act
+    assert f == ["2", "64", "8", "7.00", "2.00", "0.250", "100.0", "10.0", "0.50", "0.250"], f
+    assert "--only-workload" not in text and "--pmc SQ_WAVES" in text
