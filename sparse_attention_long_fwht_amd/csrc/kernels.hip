@@ -36,8 +36,9 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(const uint16_t* __rest
   const int bg = blockIdx.y;
   const int b = bg / kv.Hkv;
   const int g = bg - b * kv.Hkv;
-  const int s = start ? start[b] : 0;
-  const int e = end[b];
+  // (0 <= start <= end <= capacity is a precondition; clamped all the same)
+  const int s = max(start ? start[b] : 0, 0);
+  const int e = min(end[b], kv.cap);
   const int quarter = threadIdx.x & 3;
   const int slot = threadIdx.x >> 2;  // 0..63
   // The loop bound depends only on blockIdx, so every quad runs every pass.

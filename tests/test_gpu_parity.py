@@ -355,6 +355,19 @@ def test_append_decode_ragged(env):
     check_append_decode(A, torch, oracle, wl)
 
 
+@pytest.mark.parametrize("cap", [1, 5, 63, 64, 65, 511, 513])
+def test_decode_capacities_below_a_chunk(env, cap):
+    """Caches smaller than (or just past) one scan chunk and one encode pass,
+    full and partly filled, with budgets below, at and above the length."""
+    A, torch, oracle = env
+    lens = np.array([cap, max(1, cap // 2), 1], np.int32)
+    for budget in sorted({1, max(1, cap // 3), cap, cap + 7}):
+        wl = W.llama(60 + cap, cap=cap, budget=budget, B=3, Hq=8, Hkv=2, kv_len=lens)
+        check_decode(DeviceCase(wl, A, torch), oracle)
+        out = DeviceCase(wl, A, torch, encode=False).dense()
+        assert_out_close(out, oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale))
+
+
 def with_empty_slots(seed, budget):
     """Idle batch slots (kv_len 0) between a full, a ragged and a length-1
     sequence (the workload is drawn with length 1 there, then emptied)."""
