@@ -38,7 +38,11 @@
  *     memory is the caller's `workspace`.
  *   - Arguments the host can check are validated before any HIP call; on failure
  *     the call returns a status and enqueues nothing.  Values that live in
- *     device memory (kv_len, start, end) are preconditions and are not checked.
+ *     device memory (kv_len, start, end) cannot be checked by the host: the
+ *     kernels clamp them to [0, capacity], so no value makes a kernel read or
+ *     write outside the buffers the dims describe, but results for values
+ *     outside the stated preconditions are unspecified (kv_len = 0 is inside
+ *     them: an empty sequence).
  *   - A failed launch returns ADAMAS_ERR_HIP.  The library keeps no mutable
  *     global state (the opt-in profiling setting below is per thread); calls on
  *     different streams with different workspaces may run concurrently.  Two
