@@ -118,7 +118,8 @@ size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget);
  *              kv_len[b] = 0 (an idle slot of the batch): nothing is selected
  *              (sel_idx row all -1) and out[b][h] = 0, the empty sum (the pages
  *              never attend over an empty set; this is the reading taken)
- *   budget     token budget k >= 1 (may exceed kv_len[b]: then every position is kept)
+ *   budget     token budget k >= 1, any positive int32 (may exceed kv_len[b]: then every
+ *              position is kept; past the capacity it plans like budget = capacity)
  *   scale      softmax scale
  *   out        fp32 [batch][num_q_heads][128] (output)
  *   sel_idx    optional (NULL = not written): int32 [batch][num_q_heads][budget];

@@ -620,7 +620,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     if (split == 0) {
       if (tid < kHeadDim) a.out[(size_t)bh * kHeadDim + tid] = 0.f;
       if (a.sel_idx)
-        for (int i = tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
+        for (int64_t i = tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
     }
     return;
   }
@@ -998,7 +998,8 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     if (a.sel_idx) a.sel_idx[(size_t)bh * a.budget + i] = pp;
   }
   if (a.sel_idx && split == 0) {
-    for (int i = k_eff + tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
+    // (a 64-bit index: budget may be any positive int32)
+    for (int64_t i = k_eff + tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
   }
   const int nrows = max(0, hi_rank - lo_rank);
   __syncthreads();

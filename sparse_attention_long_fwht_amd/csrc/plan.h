@@ -79,6 +79,10 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   p.R = Hq / Hkv;
   p.cap = cap;
   p.budget = budget;
+  // No step selects more than min(budget, capacity) rows: the launch shape is
+  // planned for that (budget itself is only the stride of sel_idx), which also
+  // keeps the arithmetic below far from overflow for any int32 budget.
+  const int kb = budget < cap ? budget : cap;
   const size_t bhq = (size_t)B * Hq;
   size_t off = 0;
   if (dense) {
@@ -106,9 +110,9 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   // about twice the mean number of selected positions per chunk: a power of
   // two, 16..64 (halved below, down to 8, when LDS is short)
   p.pre_slots = 16;
-  while (p.pre_slots < 64 && p.pre_slots < 2 * budget / p.nch) p.pre_slots <<= 1;
-  p.rows_per_split = choose_rows_per_split(budget, B * Hq);
-  p.splits = (budget + p.rows_per_split - 1) / p.rows_per_split;
+  while (p.pre_slots < 64 && p.pre_slots < 2 * kb / p.nch) p.pre_slots <<= 1;
+  p.rows_per_split = choose_rows_per_split(kb, B * Hq);
+  p.splits = (kb + p.rows_per_split - 1) / p.rows_per_split;
   p.bitmap_words = ((cap + 31) / 32 + 3) / 4 * 4;  // keeps the record area 16-byte aligned
   // The speculative prefetch pays where the selection is latency-bound: a few
   // heads, one block each, whose rows stay in L2 until the gather.  With many

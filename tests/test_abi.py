@@ -324,3 +324,17 @@ def test_bench_summarizes_sq_counters(tmp_path, monkeypatch):
     # dispatches, waves, waves/block, us, w/SIMD, VALU/cy, VALU/w, LDS/w, cf/LDS, cf/act
     assert f == ["2", "64", "8", "7.00", "2.00", "0.250", "100.0", "10.0", "0.50", "0.250"], f
     assert "--only-workload" not in text and "--pmc SQ_WAVES" in text
+
+
+def test_workspace_for_any_int32_budget(A):
+    """A budget past the capacity plans like budget = capacity (no step selects
+    more rows), so every positive int32 budget gives a sane size and no
+    arithmetic overflows; budgets the select kernel cannot hold give 0."""
+    for B, Hq, Hkv, cap in ((1, 32, 8, 32768), (3, 8, 2, 3000), (1, 4, 1, 1)):
+        at_cap = A.decode_workspace_size(B, Hq, Hkv, cap, cap)
+        assert 0 < at_cap < (1 << 32)
+        for budget in (cap + 1, 1 << 20, 1 << 30, 2 ** 31 - 1):
+            assert A.decode_workspace_size(B, Hq, Hkv, cap, budget) == at_cap, (cap, budget)
+    assert A.decode_workspace_size(1, 32, 8, 524288, 229376) > 0
+    for budget in (229377, 1 << 30, 2 ** 31 - 1):
+        assert A.decode_workspace_size(1, 32, 8, 524288, budget) == 0

@@ -368,6 +368,26 @@ def test_decode_capacities_below_a_chunk(env, cap):
         assert_out_close(out, oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale))
 
 
+def test_decode_largest_int32_budget(env):
+    """Any positive int32 budget: past the capacity the step plans and selects
+    exactly as at budget = capacity (every position kept), bit for bit."""
+    A, torch, oracle = env
+    wl = W.llama(70, cap=3000, budget=3000, B=2, Hq=8, Hkv=2, kv_len=np.array([3000, 1537], np.int32))
+    case = DeviceCase(wl, A, torch)
+    outs = []
+    for budget in (3000, 2 ** 31 - 1):
+        out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device="cuda")
+        ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, budget))
+        A.decode_step(case.q, case.k, case.v, case.codes, case.kv_len, budget, wl.scale, out, ws)
+        torch.cuda.synchronize()
+        outs.append(from_dev(out))
+    assert np.array_equal(outs[0], outs[1])
+    codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
+    out_r, _, _, _ = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, 3000, wl.scale, threads=8,
+                                        want_dist=False)
+    assert_out_close(outs[1], out_r)
+
+
 def with_empty_slots(seed, budget):
     """Idle batch slots (kv_len 0) between a full, a ragged and a length-1
     sequence (the workload is drawn with length 1 there, then emptied)."""
