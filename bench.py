@@ -692,11 +692,10 @@ def e2e(torch, dev, log, lengths, budget, steps):
     torch.cuda.synchronize()
     log("[bench] e2e model and caches (batch %d, up to %d positions) ready (%.1f s)"
         % (batch, context, time.time() - t0))
-    start = (m.tokens.clone(), m.kv_len.clone())
+    start = m.state()
 
     def timed(fn, n):
-        m.tokens.copy_(start[0])
-        m.kv_len.copy_(start[1])
+        m.restore(start)
         for _ in range(2):
             fn()
         torch.cuda.synchronize()

@@ -45,7 +45,8 @@ int32_t llama_add_rmsnorm(const void* x, const void* delta, void* x_out, const v
  *   y[i] = x[i] cos a - x[i+64] sin a,  y[i+64] = x[i+64] cos a + x[i] sin a.
  * Writes q_out bf16 [batch][q_heads][128], and row pos[b] of k_cache (rotated)
  * and v_cache (copied), both bf16 [batch][kv_heads][capacity][128].
- *   pos       int32 [batch] device; precondition 0 <= pos[b] < capacity
+ *   pos       int32 [batch] device; precondition 0 <= pos[b] < capacity (a
+ *             position outside [0, capacity) writes q_out but no cache row)
  *   inv_freq  fp32 [64] device
  */
 int32_t llama_rope_append(const void* qkv, const int32_t* pos, const float* inv_freq, void* q_out, void* k_cache,

@@ -21,12 +21,14 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 
 
 def lib():
-    """Load liboracle.so, compiling it first if it is absent."""
+    """Load liboracle.so, compiling it first if it is absent (or the library
+    that ADAMAS_ORACLE_LIB names, e.g. the sanitizer build)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("ADAMAS_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         i32 = ctypes.c_int32
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
@@ -46,7 +48,7 @@ def lib():
         L.oracle_topk.restype = i32
         L.oracle_attention_rows.argtypes = [_u16p, _u16p, _u16p, _i32p, i32, ctypes.c_double, _f32p]
         L.oracle_attention_rows.restype = None
-        L.oracle_encode_keys.argtypes = [i32, i32, i32, _u16p, _i32p, _i32p, _u8p]
+        L.oracle_encode_keys.argtypes = [i32, i32, i32, _u16p, _i32p, _i32p, _u8p, i32]
         L.oracle_encode_keys.restype = ctypes.c_int
         L.oracle_decode_step.argtypes = [i32, i32, i32, i32, _u16p, _u16p, _u16p, _u8p, _i32p, i32,
                                          ctypes.c_float, _f32p, _i32p, _u16p, _u8p, i32]
@@ -160,11 +162,12 @@ def attention_rows(q, k_head, v_head, pos, scale):
     return out
 
 
-def encode_keys(k, end, start=None, codes=None):
+def encode_keys(k, end, start=None, codes=None, threads=1):
     """Encode positions [start[b], end[b]) of k (uint16 [B][Hkv][cap][128]).
 
     Returns the codes array (uint8 [B][Hkv][cap][32]); rows outside the ranges
-    keep their previous contents (zeros for a fresh array).
+    keep their previous contents (zeros for a fresh array).  threads > 1 encodes
+    independent rows in parallel (same arithmetic per row).
     """
     k = _c(k, np.uint16)
     B, Hkv, cap, d = k.shape
@@ -175,7 +178,7 @@ def encode_keys(k, end, start=None, codes=None):
         codes = np.zeros((B, Hkv, cap, 32), np.uint8)
     assert codes.shape == (B, Hkv, cap, 32) and codes.dtype == np.uint8 and codes.flags["C_CONTIGUOUS"]
     rc = lib().oracle_encode_keys(B, Hkv, cap, _ptr(k, _u16p), _ptr(start, _i32p), _ptr(end, _i32p),
-                                  _ptr(codes, _u8p))
+                                  _ptr(codes, _u8p), int(threads))
     if rc != 0:
         raise ValueError("oracle_encode_keys: invalid arguments")
     return codes

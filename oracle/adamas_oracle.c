@@ -295,24 +295,28 @@ static int bad_dims(int32_t B, int32_t Hq, int32_t Hkv, int32_t cap) {
  * at positions [start[b], end[b]) (start may be NULL = 0).  The same routine
  * serves the prefill pass and the one-key append (start = len-1, end = len);
  * because thresholds are per vector, a key's code never depends on other keys.
+ * threads > 1 encodes independent key rows in parallel (no change to any
+ * arithmetic: each row is encoded by oracle_encode_vector alone).
  * Returns 0, or 1 on invalid arguments.
  */
 int oracle_encode_keys(int32_t B, int32_t Hkv, int32_t cap, const uint16_t* k,
-                       const int32_t* start, const int32_t* end, uint8_t* codes) {
+                       const int32_t* start, const int32_t* end, uint8_t* codes, int32_t threads) {
   if (bad_dims(B, Hkv, Hkv, cap)) return 1;
   for (int32_t b = 0; b < B; ++b) {
     int32_t s = start ? start[b] : 0;
     int32_t e = end[b];
     if (s < 0 || e > cap || s > e) return 1;
   }
-  for (int32_t b = 0; b < B; ++b) {
-    int32_t s = start ? start[b] : 0;
-    for (int32_t g = 0; g < Hkv; ++g) {
-      for (int32_t p = s; p < end[b]; ++p) {
-        size_t row = ((size_t)b * Hkv + g) * (size_t)cap + (size_t)p;
-        oracle_encode_vector(k + row * HD, codes + row * CODE_BYTES);
-      }
-    }
+  const int64_t rows = (int64_t)B * Hkv * cap;
+  (void)threads;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+#endif
+  for (int64_t row = 0; row < rows; ++row) {
+    const int32_t b = (int32_t)(row / ((int64_t)Hkv * cap));
+    const int32_t p = (int32_t)(row % cap);
+    const int32_t s = start ? start[b] : 0;
+    if (p >= s && p < end[b]) oracle_encode_vector(k + (size_t)row * HD, codes + (size_t)row * CODE_BYTES);
   }
   return 0;
 }

@@ -114,14 +114,16 @@ __device__ __forceinline__ void encode_wave(uint32_t qlo_bits, uint32_t qhi_bits
 //                 distance), kept only for distances <= localk, where localk is
 //                 the smallest distance with at least kk = min(k, n_c)
 //                 positions at or below it (n_c = positions in the chunk);
-//   record        dmin, localk, complete (kk == n_c), n_c, a zero (cum(dmin - 1)),
-//                 then the cumulative count cum(d) for d = dmin .. localk.
+//   record        the cumulative count cum(d) of the chunk's positions at
+//                 distance <= d, for every d = 0 .. kMaxKey.
 // (k = the ranked budget, k_eff less the always-kept positions; "distance"
 // means the selection key, which differs from the distance only with forced
-// positions.)  The k smallest distances overall never go past localk of a chunk
-// that is not complete (that chunk alone has kk = k positions at or below
-// localk), and a complete chunk keeps all of its positions; so the records
-// determine the threshold and the sorted prefixes hold every selected position.
+// positions.)  Summed over the chunks, the records give the exact count of
+// positions at or below every distance, so the threshold T (the k-th smallest
+// distance) takes one sum; T never exceeds localk of a chunk with kk = k (that
+// chunk alone has k positions at or below localk), and a chunk with kk = n_c
+// keeps all of its positions in the sorted slots, so the sorted prefixes hold
+// every selected position.
 
 constexpr int kScanThreads = 512;  // one key per thread per pass
 constexpr int kHistBins = 7 * 64;  // bins as scanned by one wave: 7 per lane (up to kMaxKey + 1 used)
@@ -196,7 +198,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __shared__ uint32_t s_hist[R][kHistBins];  // counts, then exclusive offsets (bins past kMaxKey stay 0 but for kSpareBin)
   __shared__ uint32_t s_code[R + 1][8];      // query codes, then the appended key's
   __shared__ uint32_t s_limit[R];                    // sorted slots kept per head
-  __shared__ uint32_t s_recw[R];                     // 16-byte words of each head's record
   __shared__ __attribute__((aligned(16))) uint16_t s_rec[R][kRecStride];  // records, staged
   extern __shared__ __attribute__((aligned(16))) uint16_t s_sorted[];       // [R][chunk] sorted slots, staged
   for (int i = tid; i < R * kHistBins; i += kScanThreads) (&s_hist[0][0])[i] = 0u;
@@ -334,8 +335,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     }
   }
 
-  // per head (wave r): bin offsets, dmin, localk, and the record.  A chunk
-  // with nothing to rank gets dmin = localk = kMaxKey, complete, n = 0.
+  // per head (wave r): bin offsets, localk, the slots kept, and the record
+  // (cumulative counts; a chunk with nothing to rank has all of them 0).
   const int n_c = max(m1 - m0, 0);
   const int kk = min(k_mid, n_c);
   if (wave < R) {
@@ -356,41 +357,26 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     }
     const uint32_t inc = wave_inclusive_scan_u32(loc);
     const uint32_t base = inc - loc;
-    const int lmin = __builtin_ffsll((long long)__ballot(loc > 0)) - 1;            // -1 if n_c == 0
     const int lk = __builtin_ffsll((long long)__ballot(inc >= (uint32_t)kk)) - 1;  // total n_c >= kk
-    int fj = 7, kj = 7;  // this lane's first non-empty bin and first bin reaching kk
+    int kj = 7;  // this lane's first bin reaching kk
 #pragma unroll
-    for (int j = 6; j >= 0; --j) {
-      fj = cnt[j] > 0u ? j : fj;
-      kj = base + cum[j] >= (uint32_t)kk ? j : kj;
-    }
+    for (int j = 6; j >= 0; --j) kj = base + cum[j] >= (uint32_t)kk ? j : kj;
     uint32_t lim_l = 0;  // positions up to that bin
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       lim_l = j == kj ? base + cum[j] : lim_l;
       s_hist[r][7 * lane + j] = base + cum[j] - cnt[j];  // exclusive offset of the bin
     }
-    const int dmin = n_c > 0 ? 7 * lmin + __builtin_amdgcn_readlane(fj, max(lmin, 0)) : kMaxKey;
-    // (kk == 0 finds bin 0: localk is then taken as dmin, which keeps the record
-    // well formed; nothing of the chunk is selected)
-    const int localk = max(7 * lk + __builtin_amdgcn_readlane(kj, lk), dmin);
+    // slots kept: every position up to localk, the first key whose cumulative
+    // count reaches kk (kk == 0 finds key 0: a prefix nothing selects)
     const uint32_t limit = (uint32_t)__builtin_amdgcn_readlane((int)lim_l, lk);
-    uint16_t* rec = s_rec[r];
-    if (lane == 0) {
-      rec[0] = (uint16_t)dmin;
-      rec[1] = (uint16_t)localk;
-      rec[2] = (uint16_t)(kk == n_c ? 1 : 0);
-      rec[3] = (uint16_t)n_c;
-      rec[4] = 0;  // cum(dmin - 1)
-      s_limit[r] = limit;
-      s_recw[r] = (uint32_t)(kRecHead + localk - dmin + 1 + 7) / 8;
-    }
-    // cum(d) for d = dmin .. localk; the other bins write the last (padding)
-    // word of the record, which nothing reads
+    if (lane == 0) s_limit[r] = limit;
+    // cum(d) for every key d (bins past kMaxKey hold no ranked key: the
+    // padding words repeat the chunk's count)
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       const int d = 7 * lane + j;
-      rec[d >= dmin && d <= localk ? kRecHead + d - dmin : kRecStride - 1] = (uint16_t)(base + cum[j]);
+      if (d < kRecStride) s_rec[r][d] = (uint16_t)(base + cum[j]);
     }
   }
   __syncthreads();
@@ -420,7 +406,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   // copy records and sorted prefixes out in 16-byte words (the words past
   // a head's kept slots carry stale LDS values, which nothing reads)
   const size_t hc0 = (size_t)(b * a.Hq + g * R) * a.nch + c;  // (head g*R, chunk c)
-  if (wave < R && lane < (int)s_recw[wave]) {
+  if (wave < R && lane < kRecStride / 8) {
     const int r = wave;
     reinterpret_cast<uint4*>(a.rec + (hc0 + (size_t)r * a.nch) * kRecStride)[lane] =
         reinterpret_cast<const uint4*>(s_rec[r])[lane];
@@ -451,8 +437,7 @@ struct SelAttArgs {
   int32_t* sel_idx;        // optional [B][Hq][budget]
   float* out;              // [B][Hq][128]
   float qscale;            // softmax scale * log2(e)
-  int Hq, Hkv, R, cap, budget, chunk, nch, rec_win, pre_slots, splits, rows_per_split, bitmap_words;
-  int early_prefetch;  // speculative prefetch of the likely rows right after the record loads
+  int Hq, Hkv, R, cap, budget, chunk, nch, pre_slots, splits, rows_per_split, bitmap_words;
   int sink, recent;    // always-kept sinks and recent window
   KvLayout kv;         // where K/V rows of a position live (select_attend_kernel<true>: paged)
 };
@@ -487,16 +472,6 @@ __device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t* 
   before1 = b1 + inc1 - v1;
   total0 = t0;
   total1 = t1;
-}
-
-// A record header as read, clamped so that no content of the workspace can
-// lead the block out of bounds: dmin <= localk <= kMaxKey, complete 0 or 1, n at
-// most the chunk's length.
-__device__ __forceinline__ uint2 sanitize_hdr(uint32_t x, uint32_t y, int n_true) {
-  const uint32_t dm = min(x & 0xFFFFu, (uint32_t)kMaxKey);
-  const uint32_t lk = min(max(x >> 16, dm), (uint32_t)kMaxKey);
-  const uint32_t n = min(y >> 16, (uint32_t)n_true);
-  return make_uint2(dm | (lk << 16), ((y & 0xFFFFu) ? 1u : 0u) | (n << 16));
 }
 
 // Selection with every chunk's entries in one group of S >= m lanes (see
@@ -564,27 +539,24 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   const int wave = wave_id();
 
   // dynamic LDS: [list: rows_per_split ints][keep bitmap][sorted prefixes: nch x
-  // pre_slots u16][records: nch x rec_win u16 | tie bitmap]
+  // pre_slots u16][tie bitmap]
   extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // 16-byte aligned: uint4 accesses
   int* s_list = reinterpret_cast<int*>(s_dyn);
   uint32_t* s_keep = s_dyn + a.rows_per_split;
   uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_keep + a.bitmap_words);
-  uint32_t* s_aux = s_keep + a.bitmap_words + a.nch * a.pre_slots / 2;
-  uint16_t* s_rec = reinterpret_cast<uint16_t*>(s_aux);
-  uint32_t* s_tie = s_aux;
+  uint32_t* s_tie = s_keep + a.bitmap_words + a.nch * a.pre_slots / 2;
 
-  __shared__ uint2 s_hdr[kSelMaxChunks];  // per chunk: dmin | localk << 16, complete | n << 16
-  __shared__ uint32_t s_part[kSAWaves][2][64];  // per wave: its chunks' share of G' at 128 candidate distances
+  __shared__ uint32_t s_hit[kSAWaves][4];  // per wave: ballot of G >= k (2 words), G before its first hit, G at its last lane
   __shared__ uint32_t s_wsum[2 * kSAWaves];
   __shared__ float s_wm[kSAWaves], s_wl[kSAWaves];  // per wave: running max and sum
   __shared__ float s_red[kSAWaves][kHeadDim];
   __shared__ int s_last;
 
-  // ---- A. loads: kv_len, the query fragment, the first rec_win words of every
-  // chunk record (headers also to s_hdr) and the first pre_slots sorted slots
-  // of every chunk.  kv_len is a scalar load; an empty asm statement that
-  // "redefines" it after the first record loads keeps every use of it -- and
-  // so the wait for it -- behind those loads.
+  // ---- A. loads: kv_len, the query fragment, the first pre_slots sorted
+  // slots of every chunk and -- thread t for selection key t -- the first
+  // records' cumulative counts at key t.  kv_len is a scalar load; an empty
+  // asm statement that "redefines" it after those loads keeps every use of it
+  // -- and so the wait for it -- behind them.
   int len_raw = a.kv_len[b];
   const int col = lane & 15;
   const int kg = lane >> 4;
@@ -597,31 +569,29 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   }
   const uint16_t* grec = a.rec + (size_t)bh * a.nch * kRecStride;
   const uint16_t* gsorted = a.sorted + (size_t)bh * a.nch * a.chunk;
-  // 16-byte words per chunk: record window and sorted prefix (powers of two)
-  const int per_log2 = __builtin_ctz(a.rec_win) - 3, pper_log2 = __builtin_ctz(a.pre_slots) - 3;
-  const int per = 1 << per_log2, pper = 1 << pper_log2;
-  const int n16 = a.nch << per_log2;
+  // 16-byte words of sorted prefix per chunk (a power of two)
+  const int pper_log2 = __builtin_ctz(a.pre_slots) - 3;
+  const int pper = 1 << pper_log2;
   const int p16 = a.nch << pper_log2;
   auto pre_src = [&](int i) {
     const int cc = i >> pper_log2, j = i & (pper - 1);
     return reinterpret_cast<const uint4*>(gsorted + (size_t)cc * a.chunk + 8 * j);
   };
-  auto rec_src = [&](int i) {
-    const int cc = i >> per_log2, j = i & (per - 1);
-    return reinterpret_cast<const uint4*>(grec + (size_t)cc * kRecStride + 8 * j);
-  };
-  const uint4 tp = *pre_src(min(tid, p16 - 1));  // first pass of the prefixes, issued with the records
-  uint4 t0[4];                                   // first pass of the records
+  const uint4 tp = *pre_src(min(tid, p16 - 1));  // first pass of the prefixes
+  // G(t) = sum over the chunks of cum_c(t): thread t reads key t of every
+  // record (one 128-byte line per wave and chunk); the first 32 chunks here
+  constexpr int kGBatch = 32;
+  const uint16_t* gcol = grec + min(tid, kMaxKey);
+  uint32_t cv[kGBatch];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) t0[u] = *rec_src(min(u * kSAThreads + tid, n16 - 1));
+  for (int u = 0; u < kGBatch; ++u) cv[u] = gcol[(size_t)min(u, a.nch - 1) * kRecStride];
   asm volatile("" : "+s"(len_raw));
   const int len = min(len_raw, a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
   if (len <= 0) {  // no cached position: nothing selected, attention over the empty set is the zero vector
-    if (split == 0) {
-      if (tid < kHeadDim) a.out[(size_t)bh * kHeadDim + tid] = 0.f;
-      if (a.sel_idx)
-        for (int64_t i = tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
-    }
+    if (split == 0 && tid < kHeadDim) a.out[(size_t)bh * kHeadDim + tid] = 0.f;
+    if (a.sel_idx)
+      for (int64_t i = (int64_t)split * kSAThreads + tid; i < a.budget; i += (int64_t)a.splits * kSAThreads)
+        a.sel_idx[(size_t)bh * a.budget + i] = -1;
     return;
   }
   const int k_eff = min(a.budget, len);
@@ -641,204 +611,68 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     if constexpr (kPaged) return kv_row<true>(a.kv, b, g, pp) * kHeadDim;
     else return (size_t)pp * kHeadDim;
   };
-  // the split's always-kept row of this thread (-1: none): known from kv_len
-  // alone, so its K/V lines are requested right after the first record loads
-  // (into pe, which the speculative prefetch below then leaves to this row)
+  // the split's always-kept row of this thread (-1: none): known from kv_len alone
   int forced_pos = -1;
-  uint32_t pe[4] = {0u, 0u, 0u, 0u};
   if (a.sink > 0 || a.recent > 0) {
     const int i = lo_rank + tid, j = i - s_b;
     if (i < hi_rank && (j < 0 || j >= k_mid)) forced_pos = j < 0 ? i : len - r_b + (j - k_mid);
-    if (forced_pos >= 0) {
-      const size_t row = kvoff(forced_pos);
-      pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
-      pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
-      pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
-      pe[3] = *reinterpret_cast<const uint32_t*>(Vg + row + 64);
-    }
   }
   const int nch_b = (len + a.chunk - 1) >> __builtin_ctz(a.chunk);  // chunk is a power of two
+  reinterpret_cast<uint4*>(s_pre)[min(tid, p16 - 1)] = tp;
+#pragma unroll 1
+  for (int i = tid + kSAThreads; i < p16; i += kSAThreads) reinterpret_cast<uint4*>(s_pre)[i] = *pre_src(i);
+
+  // ---- B. threshold.  G(t) is the exact number of ranked positions at key
+  // <= t, non-decreasing, and G(kMaxKey) >= k_mid; the threshold T is the
+  // smallest key with G(T) >= k_mid, and quota = k_mid - G(T - 1) of the
+  // positions at key T are kept (the lowest ones).  Each wave ballots its 64
+  // keys; the first wave with a hit holds T.
+  uint32_t G = 0;
+#pragma unroll
+  for (int u = 0; u < kGBatch; ++u) G += u < nch_b ? cv[u] : 0u;
+#pragma unroll 1
+  for (int c0 = kGBatch; c0 < nch_b; c0 += kGBatch) {  // (more than 32 chunks)
+#pragma unroll
+    for (int u = 0; u < kGBatch; ++u) cv[u] = gcol[(size_t)min(c0 + u, nch_b - 1) * kRecStride];
+#pragma unroll
+    for (int u = 0; u < kGBatch; ++u) G += c0 + u < nch_b ? cv[u] : 0u;
+  }
   {
-    auto store = [&](int i0, const uint4 (&t)[4]) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = min(i0 + u * kSAThreads + tid, n16 - 1);
-        reinterpret_cast<uint4*>(s_rec)[i] = t[u];
-        const int cc = i >> per_log2;
-        if ((i & (per - 1)) == 0 && cc < nch_b) s_hdr[cc] = sanitize_hdr(t[u].x, t[u].y, min(a.chunk, len - cc * a.chunk));
-      }
-    };
-    store(0, t0);
-#pragma unroll 1
-    for (int i0 = 4 * kSAThreads; i0 < n16; i0 += 4 * kSAThreads) {  // (records of more than 2048 words)
-      uint4 t[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) t[u] = *rec_src(min(i0 + u * kSAThreads + tid, n16 - 1));
-      store(i0, t);
+    const uint64_t hit = __ballot(tid <= kMaxKey && G >= (uint32_t)k_mid);
+    const int first = hit ? __builtin_ctzll(hit) : 0;
+    const uint32_t g_prev = (uint32_t)__builtin_amdgcn_readlane((int)G, max(first - 1, 0));
+    const uint32_t g_last = (uint32_t)__builtin_amdgcn_readlane((int)G, 63);
+    if (lane == 0) {
+      s_hit[wave][0] = (uint32_t)hit;
+      s_hit[wave][1] = (uint32_t)(hit >> 32);
+      s_hit[wave][2] = first > 0 ? g_prev : 0u;
+      s_hit[wave][3] = g_last;
     }
-    reinterpret_cast<uint4*>(s_pre)[min(tid, p16 - 1)] = tp;
-#pragma unroll 1
-    for (int i = tid + kSAThreads; i < p16; i += kSAThreads) reinterpret_cast<uint4*>(s_pre)[i] = *pre_src(i);
   }
   __syncthreads();
-
-  // ---- early prefetch (speculative).  The first slots of a chunk's sorted
-  // prefix hold its smallest distances, the positions most likely kept: long
-  // before the selection is known, one word of each 128-byte line of their K
-  // and V rows is loaded (thread (cc, j): slot j < U of chunk cc, U about
-  // k_mid / chunks, over the chunks this split's ranks most likely fall in;
-  // a thread that already prefetched an always-kept row skips this).  The
-  // exact rows are prefetched again after E; the words are read only at the
-  // block's end, so nothing waits for these loads.  Only where the rows stay
-  // in L2 until used (a few heads, one block each: plan.h).
-  if (a.early_prefetch && k_mid > 0 && max(mlo, 0) < min(mhi, k_mid)) {
-    int ulog = 0;  // U = 1 << ulog
-    while ((1 << ulog) < a.pre_slots && (nch_b << ulog) < k_mid) ++ulog;
-    const int cs0 = (int)((int64_t)max(mlo, 0) * nch_b / k_mid);
-    const int cs1 = min(nch_b, (int)(((int64_t)min(mhi, k_mid) * nch_b + k_mid - 1) / k_mid) + 1);
-    if (tid < ((cs1 - cs0) << ulog) && forced_pos < 0) {
-      const int cc = cs0 + (tid >> ulog), j = tid & ((1 << ulog) - 1);
-      const int lp = min((int)s_pre[(size_t)cc * a.pre_slots + j], min(a.chunk, len - cc * a.chunk) - 1);
-      const size_t row = kvoff(cc * a.chunk + lp);
-      pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
-      pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
-      pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
-      pe[3] = *reinterpret_cast<const uint32_t*>(Vg + row + 64);
-    }
-  }
-
-  // Record word idx of chunk cc: from the LDS window, else from the global
-  // record (volatile: never merged with the LDS read into one generic load).
-  auto rec_word = [&](int cc, int idx) -> uint32_t {
-    uint32_t v = s_rec[(size_t)cc * a.rec_win + min(idx, a.rec_win - 1)];
-    if (idx >= a.rec_win) v = reinterpret_cast<const volatile uint16_t*>(grec)[(size_t)cc * kRecStride + idx];
-    return v;
-  };
-
-  // ---- B. threshold.  G'(d) = sum over chunks of cum(cc, min(d, localk)).
-  // Below D* (the least localk of the chunks that are not complete) G' is the
-  // exact count G of positions at distance <= d; from D* on it is >= k_eff
-  // (that chunk alone has k_eff positions at or below D*).  G' is
-  // non-decreasing, so the threshold T (the smallest d with G(d) >= k_eff) is
-  // where G' first reaches k_eff, and quota = k_eff - G(T-1) ties at T are
-  // kept.  T lies in [lo, hi]: lo = the least dmin, hi = min(D*, the largest
-  // localk).  Every wave reads the chunk headers (lane l: chunks l, 64 + l).
-  const bool two_groups = nch_b > 64;  // (wave-uniform) chunks 64.. exist
-  uint2 hd[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
-  uint32_t lo_n = 0, dstar_n = 0, lkmax = 0;  // (lo and D* as 511 - x: every reduction a maximum)
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    if (gi == 1 && !two_groups) break;
-    const int cc = 64 * gi + lane;
-    hd[gi] = s_hdr[min(cc, kSelMaxChunks - 1)];
-    if (cc >= nch_b) hd[gi] = make_uint2(0u, 0u);
-    const uint32_t dm = hd[gi].x & 0xFFFFu, lk = hd[gi].x >> 16;
-    if (cc < nch_b) lo_n = max(lo_n, 511u - dm);
-    if (cc < nch_b && !(hd[gi].y & 1u)) dstar_n = max(dstar_n, 511u - lk);
-    lkmax = max(lkmax, lk);
-  }
-  const int lo = 511 - (int)wave_max_u32(lo_n);
-  const int hi = min(511 - (int)wave_max_u32(dstar_n), (int)wave_max_u32(lkmax));
-
-  // G' at candidate distances d = base + lane (and base + 64 + lane): each
-  // wave sums over its chunks (w, w + 8, ...), then every wave adds the eight
-  // partial sums and finds the first candidate where G' reaches k_eff.  One
-  // round covers 64 or 128 distances, as hi - lo needs; more rounds only for
-  // contrived inputs.  Lane i holds the wave's chunk w + 8 i: dmin, localk -
-  // dmin (-1 past the wave's chunks: those read the zero word of a record)
-  // and the LDS byte address of its zero word.
-  const int per_wave = (nch_b - wave + kSAWaves - 1) / kSAWaves;  // chunks of this wave
-  int my_dm, my_wd;
-  {
-    const int cc = wave + kSAWaves * lane;
-    const uint2 h = s_hdr[min(cc, kSelMaxChunks - 1)];
-    my_dm = (int)(h.x & 0xFFFFu);
-    my_wd = (int)(h.x >> 16) - my_dm;
-  }
-  // every chunk of this wave within the LDS window (else: the global record)
-  const bool wave_fits = __ballot(lane < per_wave && kRecHead + my_wd >= a.rec_win) == 0ull;
-  // G' share of this wave's chunks at d0 (and d1), from the LDS window: chunk
-  // w + 8 i starts at LDS index (w + 8 i) * rec_win; cum(d) is word kRecHead +
-  // d - dmin, the zero word below it stands for d < dmin, the last count for d >
-  // localk.
-  auto sum_window = [&](auto two_c, int d0, int d1, uint32_t& acc0, uint32_t& acc1) {
-    constexpr bool kTwo = decltype(two_c)::value;
-    const uint16_t* c = s_rec + (size_t)wave * a.rec_win + kRecHead;
-    const size_t step = (size_t)kSAWaves * a.rec_win;
-    int i = 0;
+  int T = kMaxKey;
+  uint32_t g_before = (uint32_t)k_mid;  // (kept if no key reaches k_mid: contradictory records)
 #pragma unroll 1
-    for (; i + 4 <= per_wave; i += 4) {
-      uint32_t v0[4], v1[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int dm = __builtin_amdgcn_readlane(my_dm, i + u), wd = __builtin_amdgcn_readlane(my_wd, i + u);
-        const uint16_t* cu = c + (size_t)(i + u) * step;
-        v0[u] = cu[min(max(d0 - dm, -1), wd)];
-        if constexpr (kTwo) v1[u] = cu[min(max(d1 - dm, -1), wd)];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc0 += v0[u];
-        if constexpr (kTwo) acc1 += v1[u];
-      }
-    }
-#pragma unroll 1
-    for (; i < per_wave; ++i) {
-      const int dm = __builtin_amdgcn_readlane(my_dm, i), wd = __builtin_amdgcn_readlane(my_wd, i);
-      const uint16_t* cu = c + (size_t)i * step;
-      acc0 += cu[min(max(d0 - dm, -1), wd)];
-      if constexpr (kTwo) acc1 += cu[min(max(d1 - dm, -1), wd)];
-    }
-  };
-  int T = kMaxKey + 1;
-  uint32_t g_before = 0;  // G'(T - 1)
-  {
-    int base = lo - 1;   // G'(lo - 1) = 0 (< k_mid unless k_mid = 0: then T = lo - 1)
-    uint32_t carry = 0;  // G'(base - 1)
-#pragma unroll 1
-    for (int round = 0; base <= kMaxKey; ++round) {
-      const bool two = hi - base >= 64;
-      const int d0 = base + lane, d1 = d0 + 64;
-      uint32_t acc0 = 0, acc1 = 0;
-      if (wave_fits) {
-        if (two) sum_window(std::true_type{}, d0, d1, acc0, acc1);
-        else sum_window(std::false_type{}, d0, d1, acc0, acc1);
-      } else {
-#pragma unroll 1
-        for (int i = 0; i < per_wave; ++i) {
-          const int cc = wave + kSAWaves * i;
-          const int dm = __builtin_amdgcn_readlane(my_dm, i), wd = __builtin_amdgcn_readlane(my_wd, i);
-          acc0 += rec_word(cc, kRecHead + min(max(d0 - dm, -1), wd));
-          if (two) acc1 += rec_word(cc, kRecHead + min(max(d1 - dm, -1), wd));
-        }
-      }
-      if (round > 0) __syncthreads();  // (every wave has read the previous round's sums)
-      s_part[wave][0][lane] = acc0;
-      s_part[wave][1][lane] = acc1;
-      __syncthreads();
-      uint32_t g0 = 0, g1 = 0;
-#pragma unroll
-      for (int w = 0; w < kSAWaves; ++w) {
-        g0 += s_part[w][0][lane];
-        g1 += s_part[w][1][lane];
-      }
-      const uint64_t r0 = __ballot(g0 >= (uint32_t)k_mid);
-      const uint64_t r1 = two ? __ballot(g1 >= (uint32_t)k_mid) : 0ull;
-      const uint32_t g0_last = (uint32_t)__builtin_amdgcn_readlane((int)g0, 63);
-      if (r0 | r1) {  // (wave-uniform)
-        const int jj = r0 ? 0 : 1;
-        const int t = __builtin_ctzll(r0 ? r0 : r1);
-        T = base + 64 * jj + t;
-        const uint32_t prev = (uint32_t)__builtin_amdgcn_readlane((int)(jj ? g1 : g0), max(t - 1, 0));
-        g_before = t > 0 ? prev : (jj ? g0_last : carry);
-        break;
-      }
-      carry = two ? (uint32_t)__builtin_amdgcn_readlane((int)g1, 63) : g0_last;
-      base += two ? 128 : 64;
-      g_before = carry;  // (kept if no candidate up to kMaxKey reaches k_mid: contradictory records)
+  for (int w = 0; w < kSAWaves; ++w) {  // (wave-uniform)
+    const uint64_t hit = (uint64_t)s_hit[w][0] | ((uint64_t)s_hit[w][1] << 32);
+    if (hit) {
+      const int first = __builtin_ctzll(hit);
+      T = 64 * w + first;
+      g_before = first > 0 ? s_hit[w][2] : (w > 0 ? s_hit[w - 1][3] : 0u);
+      break;
     }
   }
   const uint32_t quota = (uint32_t)k_mid - min(g_before, (uint32_t)k_mid);
+  // cum(T) and cum(T - 1) of the chunks of lane l (l and 64 + l), for E
+  const bool two_groups = nch_b > 64;  // (wave-uniform) chunks 64.. exist
+  uint32_t mv[2] = {0u, 0u}, lv[2] = {0u, 0u};
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    if (gi == 1 && !two_groups) break;
+    const size_t ro = (size_t)min(64 * gi + lane, nch_b - 1) * kRecStride;
+    mv[gi] = grec[ro + T];
+    lv[gi] = grec[ro + max(T - 1, 0)];
+  }
 
   // ---- E. per chunk (every wave, lane l: chunks l and 64 + l): lt =
   // positions below T (slots [0, lt) of its sorted prefix) and m = lt + its
@@ -852,12 +686,11 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       if (gi == 1 && !two_groups) break;
-      const int cc = min(64 * gi + lane, max(nch_b - 1, 0));  // (headers of lanes past nch_b are zero)
-      const int dm = (int)(hd[gi].x & 0xFFFFu), wd = (int)(hd[gi].x >> 16) - dm;
-      const uint32_t n = hd[gi].y >> 16;
-      const int oT = T - dm;
-      const uint32_t m = min(rec_word(cc, kRecHead + min(max(oT, -1), wd)), n);  // (clamps keep garbage in bounds)
-      const uint32_t lt = min(rec_word(cc, kRecHead + min(max(oT - 1, -1), wd)), m);
+      const int cc = 64 * gi + lane;
+      // (clamps keep any workspace content in bounds: m <= the chunk's positions)
+      const uint32_t n = cc < nch_b ? (uint32_t)min(a.chunk, len - cc * a.chunk) : 0u;
+      const uint32_t m = min(mv[gi], n);
+      const uint32_t lt = T > 0 ? min(lv[gi], m) : 0u;
       const uint32_t lt_inc = wave_inclusive_scan_u32(lt), tie_inc = wave_inclusive_scan_u32(m - lt);
       const uint32_t ltb = lt_carry + lt_inc - lt, tb = tie_carry + tie_inc - (m - lt);
       ci[gi] = make_uint4(m, lt, ltb + min(tb, quota), tb);
@@ -866,6 +699,19 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
       mm = max(mm, m);
     }
     max_m = (uint32_t)wave_max((float)mm);  // exact: m <= 4096
+  }
+
+  // ---- prefetch of the always-kept row of this thread.  (Issued only now:
+  // a conditional load earlier would make every later wait on a record or
+  // prefix load wait for these rows as well -- vector loads return in order
+  // and the wait counts of both paths are merged.)
+  uint32_t pe[4] = {0u, 0u, 0u, 0u};
+  if (forced_pos >= 0) {
+    const size_t row = kvoff(forced_pos);
+    pe[0] = *reinterpret_cast<const uint32_t*>(Kg + row);
+    pe[1] = *reinterpret_cast<const uint32_t*>(Kg + row + 64);
+    pe[2] = *reinterpret_cast<const uint32_t*>(Vg + row);
+    pe[3] = *reinterpret_cast<const uint32_t*>(Vg + row + 64);
   }
 
   // ---- prefetch.  Every kept row lies in slots [0, m) of its chunk's sorted
@@ -920,7 +766,6 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     // ---- F (wide chunks). Mark the selected positions in bitmaps with one
     // bit per position: below T -> keep, at T -> tie.  Wave w takes the chunks
     // cc = w (mod 8); a chunk's m entries go one per lane.
-    __syncthreads();  // (every wave is done with the records: the tie bitmap overwrites them)
     for (int i = tid; i < a.bitmap_words; i += kSAThreads) {
       s_keep[i] = 0u;
       s_tie[i] = 0u;
@@ -997,9 +842,12 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     s_list[i - lo_rank] = pp;
     if (a.sel_idx) a.sel_idx[(size_t)bh * a.budget + i] = pp;
   }
-  if (a.sel_idx && split == 0) {
-    // (a 64-bit index: budget may be any positive int32)
-    for (int64_t i = k_eff + tid; i < a.budget; i += kSAThreads) a.sel_idx[(size_t)bh * a.budget + i] = -1;
+  if (a.sel_idx) {
+    // -1 past k_eff, spread over the head's splits (64-bit indices: budget may
+    // be any positive int32)
+    for (int64_t i = (int64_t)k_eff + (int64_t)split * kSAThreads + tid; i < a.budget;
+         i += (int64_t)a.splits * kSAThreads)
+      a.sel_idx[(size_t)bh * a.budget + i] = -1;
   }
   const int nrows = max(0, hi_rank - lo_rank);
   __syncthreads();
@@ -1239,8 +1087,8 @@ hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, c
     if (e != hipSuccess) return e;
   }
   SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
-                scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch, p.rec_win,
-                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words, p.early_prefetch ? 1 : 0,
+                scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch,
+                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words,
                 f.sink, f.recent, kv};
   const auto kernel = kv.table ? select_attend_kernel<true> : select_attend_kernel<false>;
   if (p.lds_select > 65536) {

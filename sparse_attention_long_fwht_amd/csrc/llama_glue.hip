@@ -93,10 +93,13 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(const uint16_t* q
                                                                int Hkv, int cap) {
   const int b = blockIdx.x;
   const int p = pos[b];
+  // a position outside the cache (a precondition violated) writes no cache row
+  const bool in_cache = p >= 0 && p < cap;
   const int width = (Hq + 2 * Hkv) * 128;
   const uint16_t* src = qkv + (size_t)b * width;
   for (int t = threadIdx.x; t < (Hq + Hkv) * 64; t += kThreads) {
     const int hh = t >> 6, i = t & 63;
+    if (hh >= Hq && !in_cache) break;  // (heads in order: only cache rows follow)
     const float ang = (float)p * inv_freq[i];
     const float c = cosf(ang), s = sinf(ang);
     const float x1 = bf(src[hh * 128 + i]), x2 = bf(src[hh * 128 + 64 + i]);
@@ -106,6 +109,7 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(const uint16_t* q
     dst[i] = y1;
     dst[64 + i] = y2;
   }
+  if (!in_cache) return;
   for (int t = threadIdx.x; t < Hkv * 128; t += kThreads) {
     const int g = t >> 7, i = t & 127;
     v_cache[(((size_t)b * Hkv + g) * cap + p) * 128 + i] = src[(Hq + Hkv) * 128 + t];

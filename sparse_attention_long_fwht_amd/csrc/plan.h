@@ -20,9 +20,10 @@ constexpr int kScanTargetChunks = 64;  // chunks per head wanted at most (see ma
 constexpr int64_t kScanBlocks = 256;   // scan blocks wanted at most: one per compute unit
 constexpr int64_t kMaxCapacity = 524288;  // positions per (b, kv head)
 constexpr int kSelMaxChunks = 128;  // chunks per (b, kv head) at most: kMaxCapacity / kScanMaxChunk
-constexpr int kRecHead = 5;          // record words before cum(dmin): dmin, localk, complete, n, zero
-constexpr int kRecStride = 392;      // u16 per (head, chunk) record: kRecHead + up to 386 counts, padded
-static_assert(kRecHead + kMaxKey + 1 <= kRecStride - 1, "the record's last word is padding");
+// u16 per (head, chunk) record: the cumulative count of positions at each
+// selection key 0..kMaxKey, padded (the padding words repeat the last count)
+constexpr int kRecStride = 392;
+static_assert(kMaxKey + 1 <= kRecStride, "a record holds every selection key");
 static_assert(kRecStride % 8 == 0, "records are copied in 16-byte words");
 // Dense baseline: chunks of the split-K attention.
 constexpr int kMaxChunks = 128;      // dense chunks per (b, kv head)
@@ -35,14 +36,12 @@ struct Plan {
   int B, Hq, Hkv, R, cap, budget;
   int chunk;           // positions per chunk (power of two)
   int nch;             // chunks covering cap
-  int rec_win;         // record words per chunk read in one go by the select/attend kernel
   int pre_slots;       // leading sorted slots per chunk the select/attend kernel keeps in LDS
   int splits;          // blocks per query head in the select/attend kernel
   int rows_per_split;  // selected rows each of those blocks attends over
   int bitmap_words;    // ceil(cap / 32)
   size_t lds_select;   // dynamic LDS of the select/attend kernel
   bool supported;      // false: the select/attend kernel's LDS would not fit this shape and budget
-  bool early_prefetch; // select/attend prefetches the likely rows before the selection is known
   size_t off_sorted, off_rec, off_part, off_count, total;
 };
 
@@ -59,7 +58,6 @@ inline int choose_chunk(int cap, int min_chunk, int max_chunks) {
 // units idle (about kSelectBlocks blocks wanted) or a block would attend more
 // than 16 tiles; at most 64 blocks share a head.
 constexpr int kSelectBlocks = 256;
-constexpr int kEarlyPrefetchHeads = 64;
 inline int choose_rows_per_split(int budget, int heads) {
   int splits = (kSelectBlocks + heads - 1) / heads;
   const int tiles = (budget + 127) / 128;
@@ -106,7 +104,6 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
     p.chunk <<= 1;
   p.nch = (cap + p.chunk - 1) / p.chunk;
   if (p.nch > kSelMaxChunks) p.supported = false;  // (not reached for cap <= kMaxCapacity)
-  p.rec_win = 256;
   // about twice the mean number of selected positions per chunk: a power of
   // two, 16..64 (halved below, down to 8, when LDS is short)
   p.pre_slots = 16;
@@ -114,22 +111,12 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   p.rows_per_split = choose_rows_per_split(kb, B * Hq);
   p.splits = (kb + p.rows_per_split - 1) / p.rows_per_split;
   p.bitmap_words = ((cap + 31) / 32 + 3) / 4 * 4;  // keeps the record area 16-byte aligned
-  // The speculative prefetch pays where the selection is latency-bound: a few
-  // heads, one block each, whose rows stay in L2 until the gather.  With many
-  // blocks the extra rows evict each other (measured: batch 16 x 32 heads,
-  // 53.7 -> 64.5 us) and the gather is bandwidth-bound anyway.
-  p.early_prefetch = p.splits == 1 && (int64_t)B * Hq <= kEarlyPrefetchHeads;
-  size_t rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);
-  const size_t tie_bytes = (size_t)p.bitmap_words * sizeof(uint32_t);
+  // [row list][keep bitmap][sorted prefixes][tie bitmap]; the prefix slots
+  // shrink while the LDS is short
   auto lds_for = [&](int pre) {
-    return (size_t)p.rows_per_split * sizeof(int) + (size_t)p.bitmap_words * sizeof(uint32_t) +
-           (size_t)p.nch * pre * sizeof(uint16_t) + (rec_bytes > tie_bytes ? rec_bytes : tie_bytes);
+    return (size_t)p.rows_per_split * sizeof(int) + 2 * (size_t)p.bitmap_words * sizeof(uint32_t) +
+           (size_t)p.nch * pre * sizeof(uint16_t);
   };
-  // record window, then prefix slots, shrink while the LDS is short
-  while (p.rec_win > 64 && lds_for(8) > kSelectDynLdsMax) {
-    p.rec_win >>= 1;
-    rec_bytes = (size_t)p.nch * p.rec_win * sizeof(uint16_t);
-  }
   while (p.pre_slots > 8 && lds_for(p.pre_slots) > kSelectDynLdsMax) p.pre_slots >>= 1;
   p.lds_select = lds_for(p.pre_slots);
   if (p.lds_select > kSelectDynLdsMax) p.supported = false;
@@ -157,6 +144,7 @@ struct KvLayout {
   int Hkv, cap;
 };
 
+#if defined(__HIP__)  // (device code; the plan above also compiles as plain host C++)
 template <bool kPaged>
 __device__ __forceinline__ size_t kv_row(const KvLayout& L, int b, int g, int p) {
   if (!kPaged) return ((size_t)b * L.Hkv + g) * (size_t)L.cap + (size_t)p;
@@ -164,6 +152,7 @@ __device__ __forceinline__ size_t kv_row(const KvLayout& L, int b, int g, int p)
   const int page = min(max(L.table[(size_t)b * L.max_pages + (p >> L.page_log2)], 0), L.num_pages - 1);
   return ((((size_t)page * L.Hkv + g)) << L.page_log2) + (size_t)(p & ((1 << L.page_log2) - 1));
 }
+#endif
 
 // Per-thread kernel-timing events (adamas_profile_events).
 constexpr int kMaxProfileEvents = 16;

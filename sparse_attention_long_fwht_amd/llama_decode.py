@@ -107,6 +107,9 @@ class LlamaShapedDecoder:
         self.tokens = torch.zeros(batch, dtype=torch.int64, device=dev)
         self.kv_len = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.new_len = torch.zeros(batch, dtype=torch.int32, device=dev)
+        # host-side bound on the longest sequence: a step (or a graph replay)
+        # that would append past the capacity is refused before it is issued
+        self.len_hi = 0
         self.attn_out = torch.empty((batch, nq, hd), dtype=torch.float32, device=dev)
         self.x = torch.empty((batch, S.hidden), dtype=torch.bfloat16, device=dev)    # residual stream
         self.h = torch.empty((batch, S.hidden), dtype=torch.bfloat16, device=dev)    # normed input of a GEMM
@@ -139,6 +142,7 @@ class LlamaShapedDecoder:
             if L.codes is not None:
                 encode_keys(L.k, lens, L.codes, num_q_heads=S.q_heads)
         self.kv_len.copy_(lens)
+        self.len_hi = int(max(lengths)) if len(lengths) else 0
         self.tokens.random_(0, S.vocab, generator=g)
 
     # ---- one decode step
@@ -171,8 +175,29 @@ class LlamaShapedDecoder:
             decode_step(q, L.k, L.v, L.codes, self.new_len, self.budget, self.scale, self.attn_out, self.ws,
                         sel_idx=sel, append=True, sink=self.sink, recent=self.recent)
 
+    def reserve(self, n: int):
+        """Account for n more appended tokens; raises before any would pass the
+        cache capacity (the caches hold positions < capacity)."""
+        if self.len_hi + n > self.cap:
+            raise RuntimeError("decode past the cache capacity: longest sequence %d + %d tokens > capacity %d"
+                               % (self.len_hi, n, self.cap))
+        self.len_hi += n
+
+    def state(self):
+        """(tokens, lengths, host bound) to restore() later (device copies)."""
+        return self.tokens.clone(), self.kv_len.clone(), self.len_hi
+
+    def restore(self, st):
+        self.tokens.copy_(st[0])
+        self.kv_len.copy_(st[1])
+        self.len_hi = st[2]
+
     def step(self):
         """Append one token to every sequence: returns the next tokens (device, [B])."""
+        self.reserve(1)
+        return self._step()
+
+    def _step(self):
         S, B = self.shape, self.B
         nq = S.q_heads
         torch.add(self.kv_len, 1, out=self.new_len)
@@ -201,13 +226,17 @@ class LlamaShapedDecoder:
         return self.tokens
 
     def capture(self, steps_per_graph: int = 1):
-        """A HIP graph of `steps_per_graph` decode steps (torch.cuda.graph);
-        each replay advances every sequence by that many tokens."""
+        """A HIP graph of `steps_per_graph` decode steps (torch.cuda.graph),
+        wrapped so that each replay() advances every sequence by that many tokens
+        and is refused (RuntimeError) before it would pass the cache capacity."""
+        if self.len_hi + steps_per_graph > self.cap:
+            raise RuntimeError("a graph of %d steps cannot run: longest sequence %d, capacity %d"
+                               % (steps_per_graph, self.len_hi, self.cap))
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):  # warm-up outside the graph (allocator, library handles)
             saved = (self.tokens.clone(), self.kv_len.clone())
-            self.step()
+            self._step()
             self.tokens.copy_(saved[0])
             self.kv_len.copy_(saved[1])
         torch.cuda.current_stream().wait_stream(s)
@@ -215,6 +244,17 @@ class LlamaShapedDecoder:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(steps_per_graph):
-                self.step()
+                self._step()
         torch.cuda.synchronize()
-        return g
+        return _GuardedGraph(self, g, steps_per_graph)
+
+
+class _GuardedGraph:
+    """A captured decode graph whose replays are counted against the cache capacity."""
+
+    def __init__(self, model, graph, steps):
+        self.model, self.graph, self.steps = model, graph, steps
+
+    def replay(self):
+        self.model.reserve(self.steps)
+        self.graph.replay()

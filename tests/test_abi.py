@@ -338,3 +338,37 @@ def test_workspace_for_any_int32_budget(A):
     assert A.decode_workspace_size(1, 32, 8, 524288, 229376) > 0
     for budget in (229377, 1 << 30, 2 ** 31 - 1):
         assert A.decode_workspace_size(1, 32, 8, 524288, budget) == 0
+
+
+def test_decoder_refuses_steps_past_capacity():
+    """The Llama-shaped decode loop counts appended tokens on the host: a step or
+    a graph replay that would write past the cache capacity raises before
+    anything is issued (CPU tensors: nothing here reaches a kernel)."""
+    import pytest
+    from sparse_attention_long_fwht_amd.llama_decode import DecoderShape, LlamaShapedDecoder, _GuardedGraph
+    shape = DecoderShape(layers=1, hidden=256, q_heads=2, kv_heads=1, ffn=64, vocab=32)
+    m = LlamaShapedDecoder(shape, batch=2, capacity=10, attention="dense", device="cpu")
+    m.len_hi = 9
+    st = m.state()
+    m.reserve(1)  # position 9, the last one, fits
+    assert m.len_hi == 10
+    with pytest.raises(RuntimeError, match="capacity"):
+        m.step()  # raises before any launch
+    assert m.len_hi == 10
+    m.restore(st)
+    assert m.len_hi == 9
+
+    class FakeGraph:
+        replays = 0
+
+        def replay(self):
+            FakeGraph.replays += 1
+
+    g = _GuardedGraph(m, FakeGraph(), 1)
+    g.replay()
+    with pytest.raises(RuntimeError, match="capacity"):
+        g.replay()
+    assert FakeGraph.replays == 1
+    m.len_hi = 8
+    with pytest.raises(RuntimeError, match="cannot run"):
+        m.capture(3)

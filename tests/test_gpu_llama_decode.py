@@ -88,7 +88,7 @@ def test_decode_loop_graph_replays_match_eager(env):
                            dense_last=1, seed=7)
     m.fill_cache([1000, 333], seed=8)
     compared = lambda: (m.layers[0].k, m.layers[0].codes, m.layers[1].v)
-    start = (m.tokens.clone(), m.kv_len.clone())
+    start = m.state()
     start_caches = [t.clone() for t in compared()]
     eager = []
     for _ in range(4):
@@ -96,8 +96,7 @@ def test_decode_loop_graph_replays_match_eager(env):
         eager.append((m.tokens.clone(), m.kv_len.clone()) + tuple(t.clone() for t in compared()))
 
     def reset():  # (rows past the lengths are never read; the compared caches are restored whole)
-        m.tokens.copy_(start[0])
-        m.kv_len.copy_(start[1])
+        m.restore(start)
         for t, t0 in zip(compared(), start_caches):
             t.copy_(t0)
 

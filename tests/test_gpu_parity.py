@@ -170,98 +170,84 @@ def max_chunk_entries(wl, dist, budget):
 
 
 def chunking(cap, groups=1):
-    """The library's chunk size (512 positions, doubled up to 4096 until a head
+    """The library's chunk size: 512 positions, doubled up to 4096 until a head
     has at most 64 chunks and the scan has at most 256 blocks, one per (b, kv
-    head, chunk)) and the select kernel's per-chunk LDS record window (256 words
-    at these sizes)."""
+    head, chunk)."""
     chunk = 512
     while chunk < 4096 and (chunk * 64 < cap or groups * -(-cap // chunk) > 256):
         chunk *= 2
-    return chunk, 256
+    return chunk, None
 
 
-def chunk_records(d, L, chunk, k_eff):
-    """Per chunk of one head: (dmin, localk, complete) as the scan records them."""
+def thresholds(wl, dist, budget):
+    """The threshold distance T (the k-th smallest) of every (b, q head)."""
     out = []
-    for c0 in range(0, L, chunk):
-        dc = np.sort(d[c0:c0 + chunk])
-        kk = min(k_eff, len(dc))
-        out.append((int(dc[0]), int(dc[kk - 1]), kk == len(dc)))
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        for h in range(wl.Hq):
+            out.append(int(np.sort(dist[b, h, :L])[min(budget, L) - 1]))
     return out
 
 
-def widest_record(wl, dist, budget):
-    """Largest per-chunk record (5 header words -- dmin, localk, complete, n and
-    a zero -- then one count per distance from the chunk's smallest distance up
-    to its localk) over all heads, and the LDS window it is compared with."""
-    chunk, window = chunking(wl.cap, wl.B * wl.Hkv)
-    worst = 0
-    for b in range(wl.B):
-        L = int(wl.kv_len[b])
-        k_eff = min(budget, L)
-        for h in range(wl.Hq):
-            for dm, lk, _ in chunk_records(dist[b, h, :L].astype(np.int64), L, chunk, k_eff):
-                worst = max(worst, 5 + lk - dm + 1)
-    return worst, window
+def pm1_query(seed):
+    """A bf16 query whose transform is exactly a +-1 vector (codes 0 and 3 only):
+    its negation is at distance 384, itself at distance 0."""
+    H = np.array([[1.0]], np.float32)
+    while H.shape[0] < 128:
+        H = np.block([[H, H], [H, -H]])
+    s = np.where(np.random.default_rng(seed).random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+    qv = (H @ s) / 128.0  # multiples of 1/64 in [-1, 1]: exact in bf16, and H @ qv == s exactly
+    return W.f32_to_bf16(qv.astype(np.float32)), W.f32_to_bf16(-qv.astype(np.float32))
 
 
-def threshold_search_rounds(wl, dist, budget):
-    """Rounds of the select kernel's threshold search, largest over heads: the
-    candidates start at lo - 1 (lo = the least dmin) and cover 64 distances a
-    round, or 128 while hi = min(least localk of the incomplete chunks, largest
-    localk) lies 64 or more past the round's start."""
-    chunk, _ = chunking(wl.cap, wl.B * wl.Hkv)
-    worst = 0
-    for b in range(wl.B):
-        L = int(wl.kv_len[b])
-        k_eff = min(budget, L)
-        for h in range(wl.Hq):
-            d = dist[b, h, :L].astype(np.int64)
-            recs = chunk_records(d, L, chunk, k_eff)
-            lo = min(r[0] for r in recs)
-            inc = [r[1] for r in recs if not r[2]]
-            hi = min(min(inc) if inc else 384, max(r[1] for r in recs))
-            T = int(np.sort(d)[k_eff - 1])
-            base, rounds = lo - 1, 0
-            while True:
-                rounds += 1
-                width = 128 if hi - base >= 64 else 64
-                if T < base + width:
-                    break
-                base += width
-            worst = max(worst, rounds)
-    return worst
-
-
-def test_decode_record_window_overflow(env):
-    """Wide chunk records.  (a) 40 chunks of 1024, budget 38000 (every chunk
-    complete); one key equals query head 0, so the least dmin is 0 and the
-    threshold lies more than one round of candidate distances (128) past it:
-    the search takes a second round.  (b) 4 chunks, where one query's transform is
-    exactly a +-1 vector (codes 0 and 3 only) and chunk 0 holds keys equal to
-    that query (distance 0) and to its negation (distance 384): that record is
-    longer than the LDS window, so its tail comes from the global record."""
+def test_decode_threshold_extremes(env):
+    """Thresholds at the ends of the distance range and far from the smallest
+    distance: (a) 40 chunks of 1024, budget 38000, one key equal to query head
+    0 (its least distance is 0, its threshold far above); (b) one chunk holding
+    keys at distance 0 and 384 beside random keys; (c) T = 384, the last
+    distance: 10 keys at distance 0, 590 at 384, budget 100 (90 ties at 384,
+    the lowest positions win); (d) T = 0 with more keys at distance 0 than the
+    budget (the lowest 64 of 200 win)."""
     A, torch, oracle = env
     wa = W.llama(50, cap=40000, budget=38000, B=1, Hq=8, Hkv=2)
     wa.k[0, 0, 2600] = wa.q[0, 0]
     wb = W.llama(51, cap=2048, budget=520, B=1, Hq=2, Hkv=1)
-    H = np.array([[1.0]], np.float32)
-    while H.shape[0] < 128:
-        H = np.block([[H, H], [H, -H]])
-    s = np.where(np.random.default_rng(7).random(128) < 0.5, -1.0, 1.0).astype(np.float32)
-    qv = (H @ s) / 128.0  # multiples of 1/64 in [-1, 1]: exact in bf16, and H @ qv == s exactly
-    wb.q[0, 0] = W.f32_to_bf16(qv.astype(np.float32))
-    wb.k[0, 0, 0:100] = W.f32_to_bf16(-qv.astype(np.float32))
-    wb.k[0, 0, 100:110] = wb.q[0, 0]
-    for wl in (wa, wb):
+    q, nq = pm1_query(7)
+    wb.q[0, 0] = q
+    wb.k[0, 0, 0:100] = nq
+    wb.k[0, 0, 100:110] = q
+    wc = W.llama(52, cap=600, budget=100, B=1, Hq=1, Hkv=1)
+    q, nq = pm1_query(8)
+    wc.q[0, 0] = q
+    wc.k[0, 0, :590] = nq
+    wc.k[0, 0, 590:] = q
+    wd = W.llama(53, cap=3000, budget=64, B=1, Hq=1, Hkv=1)
+    rng = np.random.default_rng(9)
+    wd.k[0, 0, np.sort(rng.choice(3000, 200, replace=False))] = wd.q[0, 0]
+    for wl, want in ((wa, None), (wb, None), (wc, 384), (wd, 0)):
         codes_ref = oracle.encode_keys(wl.k, wl.kv_len)
         _, _, dist_r, _ = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, wl.budget, wl.scale, threads=8)
+        T = thresholds(wl, dist_r, wl.budget)
+        if want is not None:
+            assert T[0] == want, T
         if wl is wa:
-            assert threshold_search_rounds(wl, dist_r, wl.budget) >= 2, "case (a) search takes one round"
-        else:
-            worst, window = widest_record(wl, dist_r, wl.budget)
-            assert worst > window, "case (b) record fits the LDS window (%d <= %d)" % (worst, window)
+            assert int(dist_r[0, 0].min()) == 0 and T[0] > 128, T
         check_decode(DeviceCase(wl, A, torch), oracle)
+
+
+def test_decode_budget_twice_capacity(env):
+    """A budget twice the capacity with sel_idx: every position is kept, in
+    ascending order, and the -1 tail (written by all of a head's blocks) runs
+    to the end of the row."""
+    A, torch, oracle = env
+    wl = W.llama(71, cap=3000, budget=6000, B=2, Hq=8, Hkv=2, kv_len=np.array([3000, 1537], np.int32))
+    case = DeviceCase(wl, A, torch)
+    check_decode(case, oracle)
+    _, sel, _, _ = case.decode(want_debug=False)
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        assert np.array_equal(sel[b, :, :L], np.broadcast_to(np.arange(L, dtype=np.int32), (wl.Hq, L)))
+        assert np.all(sel[b, :, L:] == -1)
 
 
 @pytest.mark.parametrize("budget", [300, 2500])
@@ -445,47 +431,40 @@ def test_decode_batched16(env):
     print("batched16: worst relative error %.2e" % err)
 
 
-def test_decode_long512k_sampled_groups(env):
-    """512K context, budget 1024: the whole step runs on the GPU at full size; the
-    oracle recomputes two KV groups (8 q heads) end to end."""
+def test_decode_long512k(env):
+    """512K context, budget 1024: the whole step runs on the GPU at full size and
+    every KV group and query head is compared with the oracle (key codes, query
+    codes, distances, selections, outputs)."""
     A, torch, oracle = env
     wl = W.llama(0, cap=524288, budget=1024, name="long512k")
     case = DeviceCase(wl, A, torch)
     out, sel, dist, qc = case.decode(want_debug=True)
-    codes_gpu = from_dev(case.codes)
-    R = wl.Hq // wl.Hkv
-    for g in (0, 5):
-        kg, vg = wl.k[:, g:g + 1], wl.v[:, g:g + 1]
-        codes_ref = oracle.encode_keys(kg, wl.kv_len)
-        assert np.array_equal(codes_gpu[:, g:g + 1], codes_ref)
-        qg = wl.q[:, g * R:(g + 1) * R]
-        o_r, s_r, d_r, q_r = oracle.decode_step(qg, kg, vg, codes_ref, wl.kv_len, wl.budget, wl.scale, threads=16)
-        hs = slice(g * R, (g + 1) * R)
-        assert np.array_equal(qc[:, hs], q_r)
-        assert np.array_equal(dist[:, hs], d_r)
-        assert np.array_equal(sel[:, hs], s_r)
-        assert_out_close(out[:, hs], o_r)
+    codes_ref = oracle.encode_keys(wl.k, wl.kv_len, threads=16)
+    assert np.array_equal(from_dev(case.codes), codes_ref)
+    o_r, s_r, d_r, q_r = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, wl.budget, wl.scale,
+                                            threads=16)
+    assert np.array_equal(qc, q_r)
+    assert np.array_equal(dist, d_r)
+    assert np.array_equal(sel, s_r)
+    err = assert_out_close(out, o_r)
+    print("long512k: all 32 heads, worst relative error %.2e" % err)
 
 
 def test_decode_long512k_largest_budget(env):
     """The largest supported budget at the largest capacity (229376 of 524288
-    positions: 64 splits of 3584 rows per head); one KV group checked."""
+    positions: 64 splits of 3584 rows per head); every head checked."""
     A, torch, oracle = env
     assert A.decode_workspace_size(1, 32, 8, 524288, 229376) > 0
     assert A.decode_workspace_size(1, 32, 8, 524288, 229377) == 0
     wl = W.llama(4, cap=524288, budget=229376, name="long512k_k224k")
     case = DeviceCase(wl, A, torch)
-    out, sel, _, qc = case.decode(want_debug=False)
-    R = wl.Hq // wl.Hkv
-    g = 3
-    kg, vg = wl.k[:, g:g + 1], wl.v[:, g:g + 1]
-    codes_ref = oracle.encode_keys(kg, wl.kv_len)
-    assert np.array_equal(from_dev(case.codes)[:, g:g + 1], codes_ref)
-    o_r, s_r, _, _ = oracle.decode_step(wl.q[:, g * R:(g + 1) * R], kg, vg, codes_ref, wl.kv_len, wl.budget,
-                                        wl.scale, threads=16, want_dist=False)
-    hs = slice(g * R, (g + 1) * R)
-    assert np.array_equal(sel[:, hs], s_r)
-    assert_out_close(out[:, hs], o_r)
+    out, sel, _, _ = case.decode(want_debug=False)
+    codes_ref = oracle.encode_keys(wl.k, wl.kv_len, threads=16)
+    assert np.array_equal(from_dev(case.codes), codes_ref)
+    o_r, s_r, _, _ = oracle.decode_step(wl.q, wl.k, wl.v, codes_ref, wl.kv_len, wl.budget, wl.scale, threads=16,
+                                        want_dist=False)
+    assert np.array_equal(sel, s_r)
+    assert_out_close(out, o_r)
 
 
 def test_decode_many_heads(env):
