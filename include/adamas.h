@@ -35,7 +35,8 @@
  *     (NULL = the null stream).
  *   - Calls only enqueue work on `stream` and return; results are ready when the
  *     stream reaches them.  No call allocates or frees device memory; scratch
- *     memory is the caller's `workspace`.
+ *     memory is the caller's `workspace` (adamas_decode_step_noalloc: a static
+ *     array the library holds on each device).
  *   - Arguments the host can check are validated before any HIP call; on failure
  *     the call returns a status and enqueues nothing.  Values that live in
  *     device memory (kv_len, start, end) cannot be checked by the host: the
@@ -44,9 +45,11 @@
  *     outside the stated preconditions are unspecified (kv_len = 0 is inside
  *     them: an empty sequence).
  *   - A failed launch returns ADAMAS_ERR_HIP.  The library keeps no mutable
- *     global state (the opt-in profiling setting below is per thread); calls on
- *     different streams with different workspaces may run concurrently.  Two
- *     calls that share a workspace must be ordered.
+ *     global state but the static scratch of adamas_decode_step_noalloc (the
+ *     opt-in profiling setting below is per thread); calls on different streams
+ *     with different workspaces may run concurrently.  Two calls that share a
+ *     workspace (or two adamas_decode_step_noalloc calls on one GPU) must be
+ *     ordered.
  */
 #ifndef ADAMAS_H
 #define ADAMAS_H
@@ -141,6 +144,27 @@ adamas_status adamas_decode_step(const adamas_dims* d, const void* q, const void
                                  float scale, float* out, int32_t* sel_idx, uint16_t* dist,
                                  uint8_t* q_codes, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): adamas_decode_step
+ * with no workspace argument.  Its scratch is a static device array of
+ * ADAMAS_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each GPU it
+ * runs on until the process ends; the first call on a device takes its
+ * address (hipGetSymbolAddress), and no call allocates or frees memory.
+ * Every call on one GPU shares that array, so calls that overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.  The
+ * kernels write every scratch word they read, so no clearing is needed.
+ * Arguments, layouts, results and errors as adamas_decode_step, plus
+ * UNSUPPORTED when adamas_decode_workspace_size(d, budget) exceeds
+ * ADAMAS_NOALLOC_SCRATCH_BYTES (checked before any HIP call), and HIP when
+ * the scratch address cannot be obtained.
+ */
+#define ADAMAS_NOALLOC_SCRATCH_BYTES (64 << 20)
+adamas_status adamas_decode_step_noalloc(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                         const uint8_t* codes, const int32_t* kv_len, int32_t budget,
+                                         float scale, float* out, int32_t* sel_idx, uint16_t* dist,
+                                         uint8_t* q_codes, void* stream);
 
 /*
  * The decode step with the key append folded in: encodes the key at position

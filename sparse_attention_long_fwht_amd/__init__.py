@@ -73,6 +73,9 @@ _lib.adamas_decode_workspace_size.restype = ctypes.c_size_t
 _lib.adamas_decode_step.argtypes = [_dims_p, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp, _vp,
                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.adamas_decode_step.restype = ctypes.c_int
+_lib.adamas_decode_step_noalloc.argtypes = [_dims_p, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp,
+                                            _vp, _vp, _vp, _vp]
+_lib.adamas_decode_step_noalloc.restype = ctypes.c_int
 _lib.adamas_append_decode_step.argtypes = _lib.adamas_decode_step.argtypes
 _lib.adamas_append_decode_step.restype = ctypes.c_int
 _lib.adamas_forced_decode_step.argtypes = [_dims_p, ctypes.POINTER(Forced), ctypes.c_int32, _vp, _vp, _vp, _vp, _vp,
@@ -101,6 +104,7 @@ _lib.adamas_abi_version.argtypes = []
 _lib.adamas_abi_version.restype = ctypes.c_int32
 
 EXPORTED_SYMBOLS = ("adamas_encode_keys", "adamas_decode_workspace_size", "adamas_decode_step",
+                    "adamas_decode_step_noalloc",
                     "adamas_append_decode_step", "adamas_forced_decode_step", "adamas_paged_encode_keys",
                     "adamas_paged_decode_step", "dense_decode_workspace_size", "dense_decode_attention",
                     "dense_paged_decode_attention", "adamas_profile_events", "adamas_status_string",
@@ -276,6 +280,28 @@ def decode_step(q, k, v, codes, kv_len, budget, scale, out, workspace, sel_idx=N
     st = _lib.adamas_paged_decode_step(ctypes.byref(d), ctypes.byref(pc), ctypes.byref(f) if f is not None else None,
                                        1 if append else 0, *tail)
     _check(st, "adamas_paged_decode_step")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_step_noalloc(q, k, v, codes, kv_len, budget, scale, out, sel_idx=None, dist=None, q_codes=None,
+                        stream=None):
+    """adamas_decode_step with the library's static scratch instead of a
+    workspace (no device allocation by the call); concurrent calls on one GPU
+    race.  Same arguments and results as decode_step without append/forced/pages."""
+    B, Hq, Hkv, cap = _check_shapes(q, k, v, codes, kv_len, out, None)
+    _shape(sel_idx, "sel_idx", (B, Hq, int(budget)), q.device)
+    _shape(dist, "dist", (B, Hq, cap), q.device)
+    _shape(q_codes, "q_codes", (B, Hq, CODE_BYTES), q.device)
+    d = dims(B, Hq, Hkv, cap, q.shape[2])
+    st = _lib.adamas_decode_step_noalloc(ctypes.byref(d), _ptr(q, "q", 2), _ptr(k, "k", 2), _ptr(v, "v", 2),
+                                         _ptr(codes, "codes", 1), _ptr(kv_len, "kv_len", 4), int(budget),
+                                         float(scale), _ptr(out, "out", 4),
+                                         _ptr(sel_idx, "sel_idx", 4, optional=True),
+                                         _ptr(dist, "dist", 2, optional=True),
+                                         _ptr(q_codes, "q_codes", 1, optional=True), _stream(stream))
+    _check(st, "adamas_decode_step_noalloc")
 
 
 def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None, pages=None):

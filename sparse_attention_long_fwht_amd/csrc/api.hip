@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "adamas.h"
 #include "plan.h"
 
@@ -239,6 +241,62 @@ adamas_status dense_paged_decode_attention(const adamas_dims* d, const adamas_pa
                                            void* stream) {
   if (!pages) return ADAMAS_ERR_INVALID_ARGUMENT;
   return dense_common(d, pages, q, k_pool, v_pool, kv_len, scale, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The decode step without a caller workspace (adamas_decode_step_noalloc).
+// Its scratch is this file-scope device array: each GPU the library runs on
+// holds its own copy, allocated with the code object and kept until the
+// process ends.  In host code `scratch` names a host-side stand-in, so its
+// device address is taken once per device with hipGetSymbolAddress (with
+// that device current) and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __align__(256) char scratch[ADAMAS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (nullptr on a HIP error).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+adamas_status adamas_decode_step_noalloc(const adamas_dims* d, const void* q, const void* k, const void* v,
+                                         const uint8_t* codes, const int32_t* kv_len, int32_t budget, float scale,
+                                         float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes,
+                                         void* stream) {
+  // the checks of adamas_decode_step, then the size against the static area,
+  // all before any HIP call
+  adamas_status st = check_dims(d, true);
+  if (st != ADAMAS_OK) return st;
+  if (!q || !k || !v || !codes || !kv_len || !out || budget < 1) return ADAMAS_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(codes, 16) || !aligned(kv_len, 4) ||
+      !aligned(out, 4) || (sel_idx && !aligned(sel_idx, 4)) || (dist && !aligned(dist, 2)) ||
+      (q_codes && !aligned(q_codes, 4)))
+    return ADAMAS_ERR_INVALID_ARGUMENT;
+  const Plan p = adamas::make_plan(d->batch, d->num_q_heads, d->num_kv_heads, d->capacity, budget, false);
+  if (!p.supported || p.total > (size_t)ADAMAS_NOALLOC_SCRATCH_BYTES) return ADAMAS_ERR_UNSUPPORTED;
+  void* ws = scratch_for_current_device();
+  if (!ws) return ADAMAS_ERR_HIP;
+  return decode_common(d, nullptr, q, k, v, const_cast<uint8_t*>(codes), false, nullptr, kv_len, budget, scale,
+                       out, sel_idx, dist, q_codes, ws, (size_t)ADAMAS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

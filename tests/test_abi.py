@@ -372,3 +372,26 @@ def test_decoder_refuses_steps_past_capacity():
     m.len_hi = 8
     with pytest.raises(RuntimeError, match="cannot run"):
         m.capture(3)
+
+
+def test_noalloc_decode_rejects_before_any_hip_call(A):
+    """adamas_decode_step_noalloc checks its arguments and the scratch size
+    before touching the GPU (these calls return without a device)."""
+    lib = A.raw_library()
+
+    def call(d, budget=128, q=FAKE, out=FAKE):
+        return lib.adamas_decode_step_noalloc(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, budget,
+                                              ctypes.c_float(0.088), out, None, None, None, None)
+
+    assert lib.adamas_decode_step_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(0.1), FAKE, None,
+                                          None, None, None) == A.ERR_INVALID_ARGUMENT
+    assert call(A.dims(1, 32, 8, 32768), q=None) == A.ERR_INVALID_ARGUMENT
+    assert call(A.dims(1, 32, 8, 32768), budget=0) == A.ERR_INVALID_ARGUMENT
+    assert call(A.dims(1, 32, 8, 32768), q=FAKE + 2) == A.ERR_INVALID_ARGUMENT  # misaligned
+    assert call(A.dims(1, 32, 8, 32768, head_dim=64)) == A.ERR_UNSUPPORTED
+    # workspace beyond the 64 MiB static scratch: 64 sequences of 32K positions
+    assert A.decode_workspace_size(64, 32, 8, 32768, 128) > A.NOALLOC_SCRATCH_BYTES
+    assert call(A.dims(64, 32, 8, 32768)) == A.ERR_UNSUPPORTED
+    # the largest configurations of the benchmark fit
+    for dims, budget in (((1, 32, 8, 32768), 1024), ((16, 32, 8, 32768), 256), ((1, 32, 8, 524288), 1024)):
+        assert 0 < A.decode_workspace_size(*dims, budget) <= A.NOALLOC_SCRATCH_BYTES
