@@ -102,7 +102,9 @@ adamas_status adamas_encode_keys(const adamas_dims* d, const void* k, const int3
 
 /* Bytes of workspace adamas_decode_step needs for these dims and budget (0 if
  * the arguments are invalid or the combination is unsupported).  Any alignment
- * of 256 bytes is sufficient. */
+ * of 256 bytes is sufficient.  (Its first 16.25 KB hold the single-launch
+ * step's per-group generation counters and chunk flags; like the rest, they
+ * need no initialisation.) */
 size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget);
 
 /*
@@ -297,7 +299,8 @@ adamas_status dense_paged_decode_attention(const adamas_dims* d, const adamas_pa
  * stream by the kernel dispatch itself, for every i with 2*i+1 < n_events.
  * Launch order: adamas_encode_keys, adamas_paged_encode_keys -> 0 encode;
  * adamas_decode_step, adamas_append_decode_step, adamas_forced_decode_step and
- * adamas_paged_decode_step -> 0 scan, 1 select+attend; dense_decode_attention
+ * adamas_paged_decode_step -> 0 scan, 1 select+attend (or 0 the single-launch
+ * step, see adamas_decode_launch_mode); dense_decode_attention
  * and dense_paged_decode_attention ->
  * 0 attend, 1 combine.  While timing is on, a call waits (on the host) for each
  * of its kernels before launching the next, so that every event pair brackets
@@ -309,6 +312,31 @@ adamas_status dense_paged_decode_attention(const adamas_dims* d, const adamas_pa
  * n_events > 0.  The setting is thread-local; it changes no result.
  */
 adamas_status adamas_profile_events(void* const* events, int32_t n_events);
+
+/*
+ * How later decode steps of the CALLING THREAD are launched (a tuning and
+ * testing aid; results are the same either way):
+ *   mode 0 (default)  two kernels: scan, then select + attend;
+ *   mode 1            one kernel per step where the shape allows it -- at most
+ *                     64 (batch, kv head) groups, at most 32 chunks of the
+ *                     scan per group, a chunk's block for every (query head,
+ *                     split) of its group, and every block of the grid
+ *                     resident on the device at once; the chunks' records are
+ *                     written through to memory and handed to the selecting
+ *                     blocks by per-chunk flags inside the kernel.  (On MI355X
+ *                     this hand-off costs more than the kernel boundary it
+ *                     replaces, so it is not the default.)
+ * Applies to adamas_decode_step, adamas_append_decode_step,
+ * adamas_forced_decode_step, adamas_paged_decode_step and
+ * adamas_decode_step_noalloc.  With one kernel, adamas_profile_events slot 0
+ * brackets it and slot 1 is not recorded.  Errors: INVALID_ARGUMENT for a mode
+ * other than 0 or 1.
+ */
+adamas_status adamas_decode_launch_mode(int32_t mode);
+
+/* Kernels launched by the calling thread's last decode step call (1 or 2; 0
+ * if it launched none). */
+int32_t adamas_last_launch_count(void);
 
 /* Static, NUL-terminated description of a status code. */
 const char* adamas_status_string(adamas_status s);

@@ -100,6 +100,10 @@ _lib.adamas_status_string.argtypes = [ctypes.c_int]
 _lib.adamas_status_string.restype = ctypes.c_char_p
 _lib.adamas_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
 _lib.adamas_profile_events.restype = ctypes.c_int
+_lib.adamas_decode_launch_mode.argtypes = [ctypes.c_int32]
+_lib.adamas_decode_launch_mode.restype = ctypes.c_int
+_lib.adamas_last_launch_count.argtypes = []
+_lib.adamas_last_launch_count.restype = ctypes.c_int32
 _lib.adamas_abi_version.argtypes = []
 _lib.adamas_abi_version.restype = ctypes.c_int32
 
@@ -108,7 +112,7 @@ EXPORTED_SYMBOLS = ("adamas_encode_keys", "adamas_decode_workspace_size", "adama
                     "adamas_append_decode_step", "adamas_forced_decode_step", "adamas_paged_encode_keys",
                     "adamas_paged_decode_step", "dense_decode_workspace_size", "dense_decode_attention",
                     "dense_paged_decode_attention", "adamas_profile_events", "adamas_status_string",
-                    "adamas_abi_version")
+                    "adamas_abi_version", "adamas_decode_launch_mode", "adamas_last_launch_count")
 
 
 class AdamasError(RuntimeError):
@@ -318,6 +322,17 @@ def dense_decode_attention(q, k, v, kv_len, scale, out, workspace, stream=None, 
     pc = pages.c(k.shape[0])
     _check(_lib.dense_paged_decode_attention(ctypes.byref(d), ctypes.byref(pc), *tail),
            "dense_paged_decode_attention")
+
+
+def decode_launch_mode(mode):
+    """Later decode steps on this thread: 0 = two kernels (default), 1 = one
+    kernel where the shape allows it.  Results are the same either way."""
+    _check(_lib.adamas_decode_launch_mode(int(mode)), "adamas_decode_launch_mode")
+
+
+def last_launch_count():
+    """Kernels launched by this thread's last decode step (1 or 2)."""
+    return int(_lib.adamas_last_launch_count())
 
 
 def profile_events(events):

@@ -14,6 +14,10 @@ using adamas::Plan;
 namespace adamas {
 static thread_local ProfileEvents t_profile{};
 ProfileEvents& profile_events() { return t_profile; }
+static thread_local int t_launch_mode = 0;
+static thread_local int t_launch_count = 0;
+int& launch_mode() { return t_launch_mode; }
+int& launch_count() { return t_launch_count; }
 }  // namespace adamas
 
 namespace {
@@ -72,6 +76,14 @@ const char* adamas_status_string(adamas_status s) {
 }
 
 int32_t adamas_abi_version(void) { return ADAMAS_ABI_VERSION; }
+
+adamas_status adamas_decode_launch_mode(int32_t mode) {
+  if (mode != 0 && mode != 1) return ADAMAS_ERR_INVALID_ARGUMENT;
+  adamas::launch_mode() = mode;
+  return ADAMAS_OK;
+}
+
+int32_t adamas_last_launch_count(void) { return adamas::launch_count(); }
 
 adamas_status adamas_profile_events(void* const* events, int32_t n_events) {
   if (n_events < 0 || n_events > adamas::kMaxProfileEvents || (!events && n_events > 0))

@@ -156,20 +156,27 @@ struct ScanArgs {
 // same XCD, so the group's query rows are fetched into one L2 only.
 constexpr int kXcds = 8;
 
-// kForced: sinks / recent window / special tokens in use (a separate
-// instantiation, so that the plain step pays nothing for them).
-template <int R, bool kForced, bool kPaged>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
-  const int G = (int)gridDim.x / a.nch;  // (b, kv head) groups
-  int bg, c;
+// The (b, kv head) group and the chunk of scan block `blk` of a grid of
+// G * nch blocks.
+__device__ __forceinline__ void scan_block_of(int blk, int grid, int nch, int& bg, int& c) {
+  const int G = grid / nch;
   if (G % kXcds == 0) {
-    const int xcd = (int)blockIdx.x % kXcds, s = (int)blockIdx.x / kXcds;
-    bg = xcd + kXcds * (s / a.nch);
-    c = s % a.nch;
+    const int xcd = blk % kXcds, s = blk / kXcds;
+    bg = xcd + kXcds * (s / nch);
+    c = s % nch;
   } else {
-    bg = (int)blockIdx.x / a.nch;
-    c = (int)blockIdx.x % a.nch;
+    bg = blk / nch;
+    c = blk % nch;
   }
+}
+
+// One scan block: chunk c of group bg.  kForced: sinks / recent window /
+// special tokens in use (a separate instantiation, so that the plain step
+// pays nothing for them).  kCoherent: the records, sorted prefixes and the
+// split counters are written through, for readers in the same kernel (the
+// single-launch step); otherwise the kernel boundary hands them over.
+template <int R, bool kForced, bool kPaged, bool kCoherent>
+__device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
   const int tid = threadIdx.x;
@@ -230,7 +237,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       }
     }
   }
-  if (c == 0 && tid < R) a.counters[(size_t)b * a.Hq + g * R + tid] = 0u;
+  if (c == 0 && tid < R) {
+    uint32_t* cnt = &a.counters[(size_t)b * a.Hq + g * R + tid];
+    if constexpr (kCoherent) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *cnt = 0u;
+  }
   __syncthreads();
   if (p0 >= len) return;
   const int p1 = min(p0 + a.chunk, len);
@@ -408,17 +419,24 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const size_t hc0 = (size_t)(b * a.Hq + g * R) * a.nch + c;  // (head g*R, chunk c)
   if (wave < R && lane < kRecStride / 8) {
     const int r = wave;
-    reinterpret_cast<uint4*>(a.rec + (hc0 + (size_t)r * a.nch) * kRecStride)[lane] =
-        reinterpret_cast<const uint4*>(s_rec[r])[lane];
+    st16<kCoherent>(a.rec + (hc0 + (size_t)r * a.nch) * kRecStride + 8 * lane,
+                    reinterpret_cast<const uint4*>(s_rec[r])[lane]);
   }
   const int wlog = __builtin_ctz(a.chunk) - 3;  // log2(16-byte words per chunk)
 #pragma unroll 1
   for (int i = tid; i < (R << wlog); i += kScanThreads) {
     const int r = i >> wlog, w = i & ((1 << wlog) - 1);
     if (8 * w < (int)s_limit[r])
-      reinterpret_cast<uint4*>(a.sorted + (hc0 + (size_t)r * a.nch) * a.chunk)[w] =
-          reinterpret_cast<const uint4*>(s_sorted + r * a.chunk)[w];
+      st16<kCoherent>(a.sorted + (hc0 + (size_t)r * a.nch) * a.chunk + 8 * w,
+                      reinterpret_cast<const uint4*>(s_sorted + r * a.chunk)[w]);
   }
+}
+
+template <int R, bool kForced, bool kPaged>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
+  int bg, c;
+  scan_block_of((int)blockIdx.x, (int)gridDim.x, a.nch, bg, c);
+  scan_chunk<R, kForced, kPaged, false>(a, bg, c);
 }
 
 // --------------------------------------------------------------------------
@@ -488,7 +506,7 @@ struct SortedEmit {
   int32_t* sel;            // optional sel_idx row of the head
 };
 
-template <int S>
+template <int S, bool kCoherent>
 __device__ __forceinline__ void emit_sorted(const SortedEmit& e) {
   const int lane = lane_id(), wave = wave_id();
   constexpr int cpi = 64 / S;  // chunks per wave per iteration
@@ -509,7 +527,7 @@ __device__ __forceinline__ void emit_sorted(const SortedEmit& e) {
     uint32_t key = 0xFFFFFFFFu;
     if (j < (int)ci.x) {
       uint32_t lp = e.pre[(size_t)cc * e.pre_slots + min(j, e.pre_slots - 1)];
-      if (j >= e.pre_slots) lp = reinterpret_cast<const volatile uint16_t*>(e.gsorted)[(size_t)cc * e.chunk + j];
+      if (j >= e.pre_slots) lp = ld_u16_apart<kCoherent>(e.gsorted + (size_t)cc * e.chunk + j);
       lp = min(lp, (uint32_t)(min(e.chunk, e.len - cc * e.chunk) - 1));  // (a position of the chunk)
       key = ((uint32_t)(cc * e.chunk + (int)lp) << 1) | (j >= (int)ci.y ? 1u : 0u);
     }
@@ -527,10 +545,11 @@ __device__ __forceinline__ void emit_sorted(const SortedEmit& e) {
   }
 }
 
-template <bool kPaged>
-__global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a) {
-  const int bh = blockIdx.x;
-  const int split = blockIdx.y;
+// Selection, gather and attention of query head bh (b * Hq + h), split
+// `split` of its rows.  kCoherent: the records and sorted prefixes were
+// written in the same kernel (the single-launch step) and are read coherently.
+template <bool kPaged, bool kCoherent>
+__device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, int split) {
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int g = h >> __builtin_ctz(a.R);  // R is a power of two
@@ -577,15 +596,16 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     const int cc = i >> pper_log2, j = i & (pper - 1);
     return reinterpret_cast<const uint4*>(gsorted + (size_t)cc * a.chunk + 8 * j);
   };
-  const uint4 tp = *pre_src(min(tid, p16 - 1));  // first pass of the prefixes
+  const uint4 tp = ld16<kCoherent>(pre_src(min(tid, p16 - 1)));  // first pass of the prefixes
   // G(t) = sum over the chunks of cum_c(t): thread t reads key t of every
   // record (one 128-byte line per wave and chunk); the first 32 chunks here
   constexpr int kGBatch = 32;
   const uint16_t* gcol = grec + min(tid, kMaxKey);
   uint32_t cv[kGBatch];
 #pragma unroll
-  for (int u = 0; u < kGBatch; ++u) cv[u] = gcol[(size_t)min(u, a.nch - 1) * kRecStride];
-  asm volatile("" : "+s"(len_raw));
+  for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + (size_t)min(u, a.nch - 1) * kRecStride);
+  // (in the single-launch step kv_len is loaded long before, by the scan)
+  if constexpr (!kCoherent) asm volatile("" : "+s"(len_raw));
   const int len = min(len_raw, a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
   if (len <= 0) {  // no cached position: nothing selected, attention over the empty set is the zero vector
     if (split == 0 && tid < kHeadDim) a.out[(size_t)bh * kHeadDim + tid] = 0.f;
@@ -620,7 +640,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   const int nch_b = (len + a.chunk - 1) >> __builtin_ctz(a.chunk);  // chunk is a power of two
   reinterpret_cast<uint4*>(s_pre)[min(tid, p16 - 1)] = tp;
 #pragma unroll 1
-  for (int i = tid + kSAThreads; i < p16; i += kSAThreads) reinterpret_cast<uint4*>(s_pre)[i] = *pre_src(i);
+  for (int i = tid + kSAThreads; i < p16; i += kSAThreads) reinterpret_cast<uint4*>(s_pre)[i] = ld16<kCoherent>(pre_src(i));
 
   // ---- B. threshold.  G(t) is the exact number of ranked positions at key
   // <= t, non-decreasing, and G(kMaxKey) >= k_mid; the threshold T is the
@@ -633,7 +653,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll 1
   for (int c0 = kGBatch; c0 < nch_b; c0 += kGBatch) {  // (more than 32 chunks)
 #pragma unroll
-    for (int u = 0; u < kGBatch; ++u) cv[u] = gcol[(size_t)min(c0 + u, nch_b - 1) * kRecStride];
+    for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + (size_t)min(c0 + u, nch_b - 1) * kRecStride);
 #pragma unroll
     for (int u = 0; u < kGBatch; ++u) G += c0 + u < nch_b ? cv[u] : 0u;
   }
@@ -670,8 +690,8 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   for (int gi = 0; gi < 2; ++gi) {
     if (gi == 1 && !two_groups) break;
     const size_t ro = (size_t)min(64 * gi + lane, nch_b - 1) * kRecStride;
-    mv[gi] = grec[ro + T];
-    lv[gi] = grec[ro + max(T - 1, 0)];
+    mv[gi] = ld_u16<kCoherent>(grec + ro + T);
+    lv[gi] = ld_u16<kCoherent>(grec + ro + max(T - 1, 0));
   }
 
   // ---- E. per chunk (every wave, lane l: chunks l and 64 + l): lt =
@@ -755,13 +775,13 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
     // among all ties stays below the quota; ranks by ballot.
     const SortedEmit e{{ci[0], ci[1]}, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, len, quota, mlo, mhi,
                        c_lo, c_hi, s_list, a.sel_idx ? a.sel_idx + (size_t)bh * a.budget + s_b : nullptr};
-    if (max_m <= 1) emit_sorted<1>(e);
-    else if (max_m <= 2) emit_sorted<2>(e);
-    else if (max_m <= 4) emit_sorted<4>(e);
-    else if (max_m <= 8) emit_sorted<8>(e);
-    else if (max_m <= 16) emit_sorted<16>(e);
-    else if (max_m <= 32) emit_sorted<32>(e);
-    else emit_sorted<64>(e);
+    if (max_m <= 1) emit_sorted<1, kCoherent>(e);
+    else if (max_m <= 2) emit_sorted<2, kCoherent>(e);
+    else if (max_m <= 4) emit_sorted<4, kCoherent>(e);
+    else if (max_m <= 8) emit_sorted<8, kCoherent>(e);
+    else if (max_m <= 16) emit_sorted<16, kCoherent>(e);
+    else if (max_m <= 32) emit_sorted<32, kCoherent>(e);
+    else emit_sorted<64, kCoherent>(e);
   } else {
     // ---- F (wide chunks). Mark the selected positions in bitmaps with one
     // bit per position: below T -> keep, at T -> tie.  Wave w takes the chunks
@@ -782,7 +802,7 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
 #pragma unroll 1
         for (int jj = lane; jj < m; jj += 64) {
           uint32_t lp = s_pre[(size_t)cc * a.pre_slots + min(jj, a.pre_slots - 1)];
-          if (jj >= a.pre_slots) lp = reinterpret_cast<const volatile uint16_t*>(gsorted)[(size_t)cc * a.chunk + jj];
+          if (jj >= a.pre_slots) lp = ld_u16_apart<kCoherent>(gsorted + (size_t)cc * a.chunk + jj);
           const int pp = cc * a.chunk + min((int)lp, min(a.chunk, len - cc * a.chunk) - 1);
           atomicOr((jj < lt ? s_keep : s_tie) + (pp >> 5), 1u << (pp & 31));
         }
@@ -1026,6 +1046,96 @@ __global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a)
   }
 }
 
+template <bool kPaged>
+__global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a) {
+  select_attend_head<kPaged, false>(a, (int)blockIdx.x, (int)blockIdx.y);
+}
+
+// --------------------------------------------------------------------------
+// Single launch: scan, hand-off, select + attend
+// --------------------------------------------------------------------------
+//
+// Every block scans its chunk (scan_chunk, records and sorted prefixes written
+// through), then publishes a flag for that chunk: a 64-bit hash of (generation
+// + 1, group, chunk).  The group's first R * splits blocks then take one
+// (query head, split) each: they wait until every chunk of the group has
+// published (polling the flags with coherent loads, bounded) and run
+// select_attend_head, which reads the records coherently.  This replaces the
+// kernel boundary between the two kernels (its drain and the second kernel's
+// start-up), and needs no assumption about which XCD a block runs on.
+//
+// The generation of a group is read by every block of the group at its start
+// and advanced by the group's first block once it has seen all the flags, so
+// each call expects new flag values: flags of an earlier call, or any other
+// content of the workspace, do not match (a 64-bit hash).  Every block of the
+// grid must be resident at once (the host checks the occupancy), so a waiting
+// block never holds a compute unit that a block it waits for needs.
+
+struct FusedSync {
+  uint32_t* gen;                // [kFusedMaxGroups]
+  unsigned long long* flags;    // [kFusedMaxGroups][kFusedMaxChunks]
+};
+
+__device__ __forceinline__ unsigned long long flag_value(uint32_t gen, int bg, int c) {
+  // (a splitmix64 finalizer)
+  unsigned long long z = ((unsigned long long)gen << 32) ^ ((unsigned long long)bg << 8) ^ (unsigned long long)c;
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+constexpr int kFusedPollMax = 1 << 21;  // about a second of polling: then the head is given up (NaN output)
+
+template <int R, bool kForced, bool kPaged>
+__global__ __launch_bounds__(kScanThreads) void fused_decode_kernel(ScanArgs sa, SelAttArgs aa, FusedSync fs) {
+  int bg, c;
+  scan_block_of((int)blockIdx.x, (int)gridDim.x, sa.nch, bg, c);
+  __shared__ uint32_t s_gen;
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) s_gen = __hip_atomic_load(&fs.gen[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  scan_chunk<R, kForced, kPaged, true>(sa, bg, c);
+  wait_memory();    // this thread's written-through stores have completed
+  __syncthreads();  // ... and every thread's (s_gen is visible too)
+  const uint32_t gen = s_gen;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&fs.flags[bg * kFusedMaxChunks + c], flag_value(gen + 1, bg, c), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  // chunk c of the group serves query head c / splits of the group, split c % splits
+  const int role = c;
+  if (role >= R * aa.splits) return;
+  if (threadIdx.x < 64) {
+    const int lane = (int)threadIdx.x;
+    const bool mine = lane < sa.nch;
+    const unsigned long long want = mine ? flag_value(gen + 1, bg, lane) : 0ull;
+    bool done = false;
+#pragma unroll 1
+    for (int it = 0; it < kFusedPollMax; ++it) {
+      const unsigned long long f =
+          mine ? __hip_atomic_load(&fs.flags[bg * kFusedMaxChunks + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : want;
+      if (__ballot(f != want) == 0ull) {
+        done = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0) s_ok = done ? 1 : 0;
+  }
+  __syncthreads();
+  if (role == 0 && threadIdx.x == 0)
+    __hip_atomic_store(&fs.gen[bg], gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int b = bg / sa.Hkv, g = bg - b * sa.Hkv;
+  // (readfirstlane: block-uniform values, kept in scalar registers)
+  const int bh = __builtin_amdgcn_readfirstlane(b * sa.Hq + g * R + role / aa.splits);
+  const int split = __builtin_amdgcn_readfirstlane(role % aa.splits);
+  if (!__builtin_amdgcn_readfirstlane(s_ok)) {  // (not expected: a chunk of the group never published)
+    if (split == 0 && threadIdx.x < kHeadDim) aa.out[(size_t)bh * kHeadDim + threadIdx.x] = __builtin_nanf("");
+    return;
+  }
+  select_attend_head<kPaged, true>(aa, bh, split);
+}
+
 // --------------------------------------------------------------------------
 // Launcher
 // --------------------------------------------------------------------------
@@ -1058,6 +1168,56 @@ static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, bool forced, hi
   return forced ? launch_scan<R, true, false>(p, sa, s) : launch_scan<R, false, false>(p, sa, s);
 }
 
+// Whether `grid` blocks of `kernel` (512 threads, `shmem` bytes of dynamic
+// LDS) can all be resident on the current device at once.  (Cached: the last
+// answer per kernel, LDS size and device.)
+static bool all_resident(const void* kernel, int grid, uint32_t shmem) {
+  struct Entry {
+    const void* kernel;
+    uint32_t shmem;
+    int device, capacity;
+  };
+  static thread_local Entry cache[8];
+  static thread_local int next = 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  for (const Entry& e : cache)
+    if (e.kernel == kernel && e.shmem == shmem && e.device == dev) return grid <= e.capacity;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kScanThreads, shmem) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  cache[next] = Entry{kernel, shmem, dev, per_cu * cus};
+  next = (next + 1) % 8;
+  return grid <= per_cu * cus;
+}
+
+// The single-launch step, when every block fits on the device at once.
+// Returns hipErrorNotReady (nothing launched) when it does not.
+template <int R, bool kForced, bool kPaged>
+static hipError_t launch_fused(const Plan& p, const ScanArgs& sa, const SelAttArgs& aa, const FusedSync& fs,
+                               hipStream_t s) {
+  const auto kernel = fused_decode_kernel<R, kForced, kPaged>;
+  const size_t scan_lds = (size_t)R * p.chunk * sizeof(uint16_t);
+  const uint32_t shmem = (uint32_t)(scan_lds > p.lds_select ? scan_lds : p.lds_select);
+  const int grid = p.nch * p.B * p.Hkv;
+  if (shmem > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  if (!all_resident(reinterpret_cast<const void*>(kernel), grid, shmem)) return hipErrorNotReady;
+  launch_k(0, kernel, dim3(grid), dim3(kScanThreads), shmem, s, sa, aa, fs);
+  return hipSuccess;
+}
+
+template <int R>
+static hipError_t launch_fused(const Plan& p, const ScanArgs& sa, const SelAttArgs& aa, const FusedSync& fs,
+                               bool forced, hipStream_t s) {
+  if (sa.kv.table)
+    return forced ? launch_fused<R, true, true>(p, sa, aa, fs, s) : launch_fused<R, false, true>(p, sa, aa, fs, s);
+  return forced ? launch_fused<R, true, false>(p, sa, aa, fs, s) : launch_fused<R, false, false>(p, sa, aa, fs, s);
+}
+
 hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, uint8_t* codes, bool append, const Forced& f, const int32_t* kv_len,
                          float scale, float* out, int32_t* sel_idx, uint16_t* dist, uint8_t* q_codes, char* ws,
@@ -1071,6 +1231,27 @@ hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, c
   ScanArgs sa{q,       k,     codes,   kv_len, ws_sorted, ws_rec,   dist,          q_codes,
               counters, f.mask, p.Hq, p.Hkv, p.cap, p.chunk,   p.nch,    p.budget, append ? 1 : 0,
               f.sink, f.recent, f.mask_words, kv};
+  SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
+                scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch,
+                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words,
+                f.sink, f.recent, kv};
+  launch_count() = 0;
+  if (p.fused && launch_mode() == 1) {
+    const FusedSync fs{reinterpret_cast<uint32_t*>(ws + p.off_sync),
+                       reinterpret_cast<unsigned long long*>(ws + p.off_sync + kSyncFlagOffset)};
+    hipError_t e = hipErrorInvalidValue;
+    switch (p.R) {
+      case 1: e = launch_fused<1>(p, sa, aa, fs, forced, s); break;
+      case 2: e = launch_fused<2>(p, sa, aa, fs, forced, s); break;
+      case 4: e = launch_fused<4>(p, sa, aa, fs, forced, s); break;
+      case 8: e = launch_fused<8>(p, sa, aa, fs, forced, s); break;
+    }
+    if (e == hipSuccess) {
+      launch_count() = 1;
+      return hipGetLastError();
+    }
+    if (e != hipErrorNotReady) return e;
+  }
   hipError_t es = hipErrorInvalidValue;
   switch (p.R) {
     case 1: es = launch_scan<1>(p, sa, forced, s); break;
@@ -1086,10 +1267,6 @@ hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, c
     hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess) return e;
   }
-  SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
-                scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch,
-                p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words,
-                f.sink, f.recent, kv};
   const auto kernel = kv.table ? select_attend_kernel<true> : select_attend_kernel<false>;
   if (p.lds_select > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -1097,6 +1274,7 @@ hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, c
     if (e != hipSuccess) return e;
   }
   launch_k(1, kernel, dim3(p.B * p.Hq, p.splits), dim3(kSAThreads), (uint32_t)p.lds_select, s, aa);
+  launch_count() = 2;
   return hipGetLastError();
 }
 

@@ -272,6 +272,52 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte and 2-byte accesses of data handed between blocks of one kernel:
+// written through (agent-scope atomic stores) and read coherently
+// (agent-scope atomic loads), so that the reader sees the writer's data
+// whatever XCD either runs on.  kCoherent = false: plain accesses (data that
+// a kernel boundary hands over).
+template <bool kCoherent>
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  if constexpr (kCoherent) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    __hip_atomic_store(q, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+}
+template <bool kCoherent>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  if constexpr (kCoherent) {
+    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+template <bool kCoherent>
+__device__ __forceinline__ uint32_t ld_u16(const uint16_t* p) {
+  if constexpr (kCoherent) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t w = __hip_atomic_load(reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return (a & 2) ? (w >> 16) : (w & 0xFFFFu);
+  } else {
+    return *p;
+  }
+}
+// The same for a rare global read beside an LDS read of the same variable:
+// the plain form is volatile, so that the two are never merged into one
+// generic (flat) load with a full wait.
+template <bool kCoherent>
+__device__ __forceinline__ uint32_t ld_u16_apart(const uint16_t* p) {
+  if constexpr (kCoherent) return ld_u16<true>(p);
+  else return *reinterpret_cast<const volatile uint16_t*>(p);
+}
+
 // Wait until every memory operation this thread issued has completed (for the
 // write-through stores above: reached the point of coherence).  The signal
 // fence keeps the compiler from moving the stores past the wait.

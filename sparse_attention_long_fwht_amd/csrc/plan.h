@@ -31,6 +31,16 @@ constexpr int kPartFloats = 132;     // m, l, 2 pad, o[128]
 // Dynamic LDS the select/attend kernel may take (160 KB per block, less what
 // its static arrays need).
 constexpr size_t kSelectDynLdsMax = 144 * 1024;
+// The single-launch step (scan, hand-off and select/attend in one kernel):
+// groups (b, kv head) and chunks per group it serves at most, and its
+// synchronisation words at the start of every decode workspace: a generation
+// per group, then a 64-bit flag per (group, chunk).
+constexpr int kFusedMaxGroups = 64;
+constexpr int kFusedMaxChunks = 32;
+constexpr size_t kSyncFlagOffset = 256;
+constexpr size_t kSyncBytes = kSyncFlagOffset + (size_t)kFusedMaxGroups * kFusedMaxChunks * 8;
+static_assert(kFusedMaxGroups * 4 <= (int)kSyncFlagOffset, "the generations fit before the flags");
+static_assert(kSyncBytes % 256 == 0, "regions stay 256-byte aligned");
 
 struct Plan {
   int B, Hq, Hkv, R, cap, budget;
@@ -42,7 +52,8 @@ struct Plan {
   int bitmap_words;    // ceil(cap / 32)
   size_t lds_select;   // dynamic LDS of the select/attend kernel
   bool supported;      // false: the select/attend kernel's LDS would not fit this shape and budget
-  size_t off_sorted, off_rec, off_part, off_count, total;
+  bool fused;          // the shape allows the single-launch step (the host also checks residency)
+  size_t off_sync, off_sorted, off_rec, off_part, off_count, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -120,6 +131,11 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   while (p.pre_slots > 8 && lds_for(p.pre_slots) > kSelectDynLdsMax) p.pre_slots >>= 1;
   p.lds_select = lds_for(p.pre_slots);
   if (p.lds_select > kSelectDynLdsMax) p.supported = false;
+  // single launch: few enough groups and chunks for the sync words, and a
+  // block of the group for every (query head, split)
+  p.fused = (int64_t)B * Hkv <= kFusedMaxGroups && p.nch <= kFusedMaxChunks && p.R * p.splits <= p.nch;
+  p.off_sync = off;
+  off += kSyncBytes;
   p.off_sorted = off;
   off = align256(off + bhq * (size_t)p.nch * p.chunk * sizeof(uint16_t));
   p.off_rec = off;
@@ -161,6 +177,11 @@ struct ProfileEvents {
   int n;
 };
 ProfileEvents& profile_events();  // this thread's setting
+// This thread's decode launch setting (adamas_decode_launch_mode: 1 = single
+// launch where possible, 0 = always two kernels) and the number of kernels its
+// last decode call launched.
+int& launch_mode();
+int& launch_count();
 
 // ---- launchers (kernels.hip, decode.hip); kv.table == nullptr: contiguous caches ----
 hipError_t launch_encode_keys(int B, const KvLayout& kv, const uint16_t* k, const int32_t* start,

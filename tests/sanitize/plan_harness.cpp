@@ -38,6 +38,11 @@ static void check(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   if (dense) return;
   REQUIRE(p.off_sorted % 256 == 0 && p.off_rec % 256 == 0 && p.off_rec > p.off_sorted && p.off_part > p.off_rec,
           fmt, ARGS);
+  REQUIRE(p.off_sync == 0 && p.off_sorted >= adamas::kSyncBytes, fmt, ARGS);  // sync words at a fixed place
+  if (p.fused)  // single launch: groups and chunks within the sync words, a block per (head, split)
+    REQUIRE((int64_t)B * Hkv <= adamas::kFusedMaxGroups && p.nch <= adamas::kFusedMaxChunks &&
+                p.R * p.splits <= p.nch,
+            fmt, ARGS);
   // every region holds what the kernels index in it
   const size_t bhq = (size_t)B * Hq;
   REQUIRE(p.off_rec - p.off_sorted >= bhq * p.nch * (size_t)p.chunk * sizeof(uint16_t), fmt, ARGS);

@@ -78,17 +78,21 @@ def test_profile_events_time_each_kernel_and_change_nothing():
     wl = W.llama(43, cap=9000, budget=300, B=1)
     case = DeviceCase(wl, A, torch)
     ref = case.decode(want_debug=False)
-    A.profile_events(evs)
-    try:
-        got = case.decode(want_debug=False)
-    finally:
-        A.profile_events(None)
-    for x, y in zip(ref[:2], got[:2]):
-        assert np.array_equal(x, y)
-    for i in range(2):
-        ms = ctypes.c_float()
-        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * i], evs[2 * i + 1]) == 0
-        assert 0.0 < ms.value < 100.0
+    for mode, launches in ((0, 2), (1, 1)):  # two kernels; the single-launch step
+        A.decode_launch_mode(mode)
+        A.profile_events(evs)
+        try:
+            got = case.decode(want_debug=False)
+        finally:
+            A.profile_events(None)
+            A.decode_launch_mode(0)
+        assert A.last_launch_count() == launches
+        for x, y in zip(ref[:2], got[:2]):
+            assert np.array_equal(x, y)
+        for i in range(launches):
+            ms = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * i], evs[2 * i + 1]) == 0
+            assert 0.0 < ms.value < 100.0
 
 
 def test_graph_replay_forced_and_paged():
