@@ -45,8 +45,8 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=640)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=640, help="timed steps (exactly)")
+    ap.add_argument("--warmup", type=int, default=64, help="untimed steps before them (exactly)")
     ap.add_argument("--budget", type=int, default=128)
     ap.add_argument("--context", type=int, default=32768)
     ap.add_argument("--copies", type=int, default=64, help="rotating cache copies (cold-cache timing)")
@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the context x budget sweep (4K..128K x 64..1024) in the extras")
     ap.add_argument("--no-e2e", action="store_true",
                     help="skip the end-to-end decode of the 32-layer Llama-3.1-8B-shaped stack (random weights)")
     ap.add_argument("--e2e-steps", type=int, default=16, help="timed tokens per end-to-end variant")
@@ -131,7 +133,7 @@ def main():
         return sweep(A, W, np, torch, dev, log)
     if args.only_workload:
         make, ncopy = OTHER_WORKLOADS[args.only_workload]
-        r = other_workload(A, np, torch, dev, make(W, args.seed), ncopy)
+        r = other_workload(A, np, torch, dev, make(W, args.seed), ncopy, hip)
         print(json.dumps(dict(r, workload=args.only_workload)), flush=True)
         return
 
@@ -211,10 +213,53 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * n_per_replay), reps * n_per_replay
 
-    # ---- headline: cold-cache decode step, graph replay
-    g_cold = graph_of(step, copies)
-    ms_step, steps_done = time_graph(g_cold, R, args.steps, args.warmup)
-    log("[bench] decode step (adamas_append_decode_step), cold: %.2f us" % (ms_step * 1e3))
+    # ---- headline: exactly --warmup untimed steps, then exactly --steps timed
+    # steps, each a graph of that many steps over the rotating copies (step i
+    # reads copy i mod R)
+    K, Wu = max(1, args.steps), max(0, args.warmup)
+    g_main = graph_of(step, [copies[i % R] for i in range(K)])
+    g_wu = graph_of(step, [copies[(K + i) % R] for i in range(Wu)]) if Wu else None
+    torch.cuda.synchronize()
+    if g_wu is not None:
+        g_wu.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_main.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / K
+    steps_done = K
+    del g_main, g_wu
+    log("[bench] decode step (adamas_append_decode_step), cold: %.2f us over exactly %d steps after %d warm-up"
+        % (ms_step * 1e3, K, Wu))
+    def replay_spread(fn, n_replays=24, per_graph=16):
+        """Mean step time of each of n_replays timed replays of 16-step graphs
+        that together cycle through every copy (so the rotation stays cold):
+        median, p10, p90, min, max over the replays."""
+        gs = [graph_of(fn, [copies[(j * per_graph + i) % R] for i in range(per_graph)])
+              for j in range(max(1, R // per_graph))]
+        for g in gs:
+            g.replay()
+        torch.cuda.synchronize()
+        per = []
+        for i in range(n_replays):
+            e0.record()
+            gs[i % len(gs)].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / per_graph)
+        del gs
+        per.sort()
+        return {"steps": n_replays * per_graph, "replay_steps": per_graph, "median_us": round(per[len(per) // 2], 3),
+                "p10_us": round(per[int(0.1 * (len(per) - 1))], 3),
+                "p90_us": round(per[int(0.9 * (len(per) - 1))], 3), "min_us": round(per[0], 3),
+                "max_us": round(per[-1], 3)}
+
+    # the spread: 24 timed replays of 16-step graphs (384 steps)
+    spread = replay_spread(step)
+    log("[bench] spread over 24 x 16 steps: %s" % spread)
+    g_cold = None
 
     # ---- kernel-by-kernel durations (dispatch-recorded HIP events), cold rotation
     names = ["scan", "select_attend"]
@@ -265,9 +310,12 @@ def main():
                 "kernel": dominant + "_kernel", "kernel_us": round(kern_us[dominant], 3),
                 "algorithmic_bytes_per_launch": algo[dominant]}
 
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
     extra = {"kernel_us": {k: round(v, 3) for k, v in kern_us.items()},
              "step_algorithmic_bytes": step_bytes,
-             "step_achieved_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+             "step_achieved_GBps": round(step_gbs, 1),
+             "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+             "step_spread": spread,
              "gathered_rows_unique": uniq, "gathered_rows_no_dedup": nodedup,
              "cache_copies": R}
 
@@ -334,6 +382,15 @@ def main():
             extra["step_us_paged_page%d" % page] = round(ms_p * 1e3, 3)
             log("[bench] paged (page %d): %.2f us" % (page, ms_p * 1e3))
             del g_p, pcopies
+        # the single-launch step (adamas_decode_launch_mode(1)) beside the
+        # two-kernel one, same rotation and replays
+        A.decode_launch_mode(1)
+        sl = replay_spread(step)
+        assert A.last_launch_count() == 1
+        A.decode_launch_mode(0)
+        extra["step_us_single_launch_median"] = sl["median_us"]
+        extra["step_us_two_kernels_median"] = spread["median_us"]
+        log("[bench] single-launch step: median %.2f us (two kernels %.2f)" % (sl["median_us"], spread["median_us"]))
         # full-cache key encode (prefill) pass, cold rotation
         g_enc = graph_of(lambda c: A.encode_keys(c[1], kv_len, c[3]), copies[:16])
         ms_enc, _ = time_graph(g_enc, 16, 64, 16)
@@ -343,10 +400,18 @@ def main():
         log("[bench] prefill key encode: %.2f us (%.0f GB/s)" % (ms_enc * 1e3, extra["prefill_encode_GBps"]))
         del copies, g_cold, g_warm, g_dense, g_enc
         torch.cuda.empty_cache()
+        # budget 1024 on the same layer: kernels, deduplicated bytes, fractions
+        extra["llama32k_b1024"] = other_workload(A, np, torch, dev, W.llama(args.seed, cap=cap, budget=1024), 8,
+                                                 hip)
+        log("[bench] budget 1024: %s" % extra["llama32k_b1024"])
+        torch.cuda.empty_cache()
         # the batched and long-context workloads
         for name, (make, ncopy) in OTHER_WORKLOADS.items():
-            extra[name] = other_workload(A, np, torch, dev, make(W, args.seed), ncopy)
+            extra[name] = other_workload(A, np, torch, dev, make(W, args.seed), ncopy, hip)
             log("[bench] %s: %s" % (name, extra[name]))
+            torch.cuda.empty_cache()
+        if not args.no_sweep:
+            extra["sweep_context_x_budget"] = sweep_rows(A, W, np, torch, dev, log, hip)
             torch.cuda.empty_cache()
 
     if not args.no_extra and not args.no_e2e:
@@ -362,7 +427,7 @@ def main():
         cpu = cpu_baseline(wl, budget, args.cpu_seconds, log)
 
     res = {"metric": METRIC, "value": round(ms_step * 1e3, 3), "unit": "us", "n_gpus": 1, "steps": steps_done,
-           "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": False,
+           "warmup": Wu, "ms_per_step": round(ms_step, 6), "higher_is_better": False,
            "scaling": "weak", "vs_baseline": None, "dtype": "u8+fp32", "data": "synthetic",
            "config": {"workload": "llama3.1-8b-shaped decode layer: batch 1, 32 q / 8 kv heads, head_dim 128, "
                                   "%d cached positions, budget %d; append-encode + decode per step; cold cache"
@@ -730,9 +795,38 @@ def upload(np, torch, dev, a):
     return torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
 
 
-def other_workload(A, np, torch, dev, wl, ncopy):
+def kernel_means(A, torch, hip, fn, cases, names):
+    """Mean duration (us) of each kernel of fn(case), from HIP events recorded
+    by the kernels' own dispatches (adamas_profile_events), over the cases."""
+    evs = [hip.event() for _ in range(2 * len(names))]
+    sums = [0.0] * len(names)
+    n = 0
+    for i in range(len(cases) + 2):
+        A.profile_events(evs)
+        fn(cases[i % len(cases)])
+        A.profile_events(None)
+        torch.cuda.synchronize()
+        if i >= 2:
+            for j in range(len(names)):
+                sums[j] += hip.elapsed_ms(evs[2 * j], evs[2 * j + 1])
+            n += 1
+    return {names[j]: sums[j] / n * 1e3 for j in range(len(names))}
+
+
+def unique_rows(np, sel, Hkv):
+    """K/V rows one step must read: the union of the selections of each (b, kv
+    head)'s query heads (int32 [B][Hq][budget], -1 padded)."""
+    B, Hq, _ = sel.shape
+    grp = Hq // Hkv
+    return sum(len(np.unique(s[s >= 0])) for b in range(B) for g in range(Hkv)
+               for s in (sel[b, g * grp:(g + 1) * grp],))
+
+
+def other_workload(A, np, torch, dev, wl, ncopy, hip=None):
     """Step latency (append-encode + decode, rotating `ncopy` copies of q, K, V
-    and codes) and the dense baseline on one workload."""
+    and codes) and the dense baseline on one workload; with `hip`, also the
+    kernels' durations, the deduplicated algorithmic bytes and the fractions of
+    the HBM peak they reach."""
     kv_len = upload(np, torch, dev, wl.kv_len)
     q, k, v = upload(np, torch, dev, wl.q), upload(np, torch, dev, wl.k), upload(np, torch, dev, wl.v)
     codes = torch.zeros((wl.B, wl.Hkv, wl.cap, 32), dtype=torch.uint8, device=dev)
@@ -741,60 +835,110 @@ def other_workload(A, np, torch, dev, wl, ncopy):
     out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device=dev)
     ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, wl.budget), dev)
     wsd = A.alloc_workspace(A.dense_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap), dev)
-    step_us = timed_graph_steps(torch, lambda c: A.decode_step(c[0], c[1], c[2], c[3], kv_len, wl.budget,
-                                                               wl.scale, out, ws, append=True),
-                                cases * max(1, 16 // ncopy), 5)
+    step = lambda c: A.decode_step(c[0], c[1], c[2], c[3], kv_len, wl.budget, wl.scale, out, ws, append=True)
+    step_us = timed_graph_steps(torch, step, cases * max(1, 16 // ncopy), 5)
     dense_us = timed_graph_steps(torch, lambda c: A.dense_decode_attention(c[0], c[1], c[2], kv_len, wl.scale,
                                                                            out, wsd), cases, 5)
     L = int(wl.kv_len.astype(np.int64).sum())
     code_bytes = L * wl.Hkv * 32
     gathered_max = wl.B * wl.Hq * wl.budget * 512  # no-dedup upper bound
-    return {"batch": wl.B, "context": wl.cap, "positions": L, "budget": wl.budget, "cache_copies": ncopy,
-            "step_us": round(step_us, 3), "dense_us": round(dense_us, 3),
-            "speedup_vs_dense": round(dense_us / step_us, 3),
-            "dense_GBps": round(L * wl.Hkv * 512 / (dense_us * 1e3), 1),
-            "step_GBps_codes_plus_gather_upper_bound": round((code_bytes + gathered_max) / (step_us * 1e3), 1)}
+    res = {"batch": wl.B, "context": wl.cap, "positions": L, "budget": wl.budget, "cache_copies": ncopy,
+           "step_us": round(step_us, 3), "dense_us": round(dense_us, 3),
+           "speedup_vs_dense": round(dense_us / step_us, 3),
+           "dense_GBps": round(L * wl.Hkv * 512 / (dense_us * 1e3), 1),
+           "dense_hbm_frac": round(L * wl.Hkv * 512 / (dense_us * 1e3) / HBM_PEAK_GBS, 4),
+           "step_GBps_codes_plus_gather_upper_bound": round((code_bytes + gathered_max) / (step_us * 1e3), 1)}
+    if hip is None:
+        return res
+    sel = torch.empty((wl.B, wl.Hq, wl.budget), dtype=torch.int32, device=dev)
+    A.decode_step(q, k, v, codes, kv_len, wl.budget, wl.scale, out, ws, sel_idx=sel)
+    torch.cuda.synchronize()
+    uniq = unique_rows(np, sel.cpu().numpy(), wl.Hkv)
+    qo = wl.B * wl.Hq * (256 + 512)
+    algo = {"scan": code_bytes + wl.B * wl.Hq * 256 + wl.B * wl.Hkv * 288, "select_attend": uniq * 512 + qo}
+    step_bytes = code_bytes + uniq * 512 + qo + wl.B * wl.Hkv * 288
+    kus = kernel_means(A, torch, hip, step, cases, ["scan", "select_attend"])
+    res.update({"gathered_rows_unique": uniq, "step_algorithmic_bytes": step_bytes,
+                "step_GBps": round(step_bytes / (step_us * 1e3), 1),
+                "step_hbm_frac": round(step_bytes / (step_us * 1e3) / HBM_PEAK_GBS, 4),
+                "kernel_us": {n: round(t, 3) for n, t in kus.items()},
+                "kernel_GBps": {n: round(algo[n] / (kus[n] * 1e3), 1) for n in kus},
+                "kernel_hbm_frac": {n: round(algo[n] / (kus[n] * 1e3) / HBM_PEAK_GBS, 4) for n in kus}})
+    return res
 
 
-def sweep(A, W, np, torch, dev, log):
+SWEEP_CONTEXTS = (4096, 8192, 16384, 32768, 65536, 131072)
+SWEEP_BUDGETS = (64, 128, 256, 512, 1024)
+
+
+def sweep_rows(A, W, np, torch, dev, log, hip=None):
     """Contexts 4K..128K x budgets 64..1024 on the 32/8-head layer: step latency
-    (4 rotating copies) and the dense baseline, one JSON line per context."""
-    for cap in (4096, 8192, 16384, 32768, 65536, 131072):
+    (4 rotating copies) and the dense baseline, one row per context."""
+    rows = []
+    for cap in SWEEP_CONTEXTS:
         wl = W.llama(0, cap=cap, budget=64)
         row = {"context": cap, "step_us": {}}
-        for budget in (64, 128, 256, 512, 1024):
+        for budget in SWEEP_BUDGETS:
             wl.budget = budget
             r = other_workload(A, np, torch, dev, wl, 4)
             row["step_us"][budget] = r["step_us"]
             row["dense_us"] = r["dense_us"]
             log("[sweep] context %d budget %d: %.2f us (dense %.2f us)" % (cap, budget, r["step_us"], r["dense_us"]))
             torch.cuda.empty_cache()
+        rows.append(row)
+    return rows
+
+
+def sweep(A, W, np, torch, dev, log):
+    for row in sweep_rows(A, W, np, torch, dev, log):
         print(json.dumps(row), flush=True)
 
 
-def cpu_baseline(wl, budget, seconds, log):
-    """The oracle as it stands, timed on this host's cores for a bounded number
-    of full decode steps of the same workload."""
-    import numpy as np
-    import oracle
+def host_cpu():
+    """(logical CPUs this process may run on, CPU model name) of the host."""
     try:
-        ncpu = len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:
-        ncpu = os.cpu_count() or 1
-    threads = max(1, min(16, ncpu))
-    codes = oracle.encode_keys(wl.k, wl.kv_len)
-    t0 = time.time()
-    oracle.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, budget, wl.scale, threads=threads, want_dist=False)
-    one = time.time() - t0
-    n = max(1, int(seconds / max(one, 1e-3)))
-    t0 = time.time()
-    for _ in range(n):
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(wl, budget, seconds, log):
+    """The oracle as it stands, timed on this host for a bounded number of full
+    decode steps of the same workload: on all the host's CPUs (OpenMP over
+    (b, q head)) and on one thread."""
+    import oracle
+    ncpu, model = host_cpu()
+    codes = oracle.encode_keys(wl.k, wl.kv_len, threads=ncpu)
+
+    def timed(threads, budget_s):
+        t0 = time.time()
         oracle.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, budget, wl.scale, threads=threads, want_dist=False)
-    dt = (time.time() - t0) / n
-    log("[bench] cpu oracle: %.1f us/step over %d steps with %d threads" % (dt * 1e6, n, threads))
-    return {"value": round(dt * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+        one = time.time() - t0
+        n = max(1, int(budget_s / max(one, 1e-3)))
+        t0 = time.time()
+        for _ in range(n):
+            oracle.decode_step(wl.q, wl.k, wl.v, codes, wl.kv_len, budget, wl.scale, threads=threads,
+                               want_dist=False)
+        return (time.time() - t0) / n, n
+
+    dt_all, n_all = timed(ncpu, seconds)
+    dt_one, n_one = timed(1, seconds)
+    log("[bench] cpu oracle: %.1f us/step with %d threads (%d steps), %.1f us/step on one thread (%d steps); %s"
+        % (dt_all * 1e6, ncpu, n_all, dt_one * 1e6, n_one, model))
+    return {"value": round(dt_all * 1e6, 1), "unit": "us", "cores": ncpu, "kind": "oracle",
             "sample": "%d full decode steps (query encode, distances, top-%d, fp64 attention) of the same "
-                      "32K-context layer, codes precomputed" % (n, budget)}
+                      "32K-context layer on %d threads, then %d on one thread; key codes precomputed"
+                      % (n_all, budget, ncpu, n_one),
+            "value_single_thread": round(dt_one * 1e6, 1), "host_logical_cpus": ncpu, "cpu_model": model}
 
 
 if __name__ == "__main__":

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "plan.h"
 
@@ -129,29 +131,39 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
   }
 }
 
-template <int R>
-struct AttnSmem {
-  float S[64][R + 1];     // scores, then probabilities, of one 64-row tile
-  float mrun[R], lrun[R], corr[R];
-  float red[4][R][kHeadDim];
-};
+// lane (16 k + h)'s value for every lane 16 k + j of its 16-lane row (DPP
+// row_newbcast)
+template <int H>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + H, 0xF, 0xF, false));
+}
+
+constexpr int kDenseWaves = 4;  // waves per dense block; each streams its own 16-row tiles
 
 // Exact softmax attention of the group's R queries over positions
 // [p0, p0 + nrows) of one KV head, written as one partial (m, l, o[128]) per
 // head: m = running max of the scaled log2 scores, l = sum 2^(s - m),
-// o = sum 2^(s - m) V.
-//   q . K^T: MFMA 16x16x32 bf16, 16 rows x 16 columns (the R heads, rest zero)
-//            per wave, 64 rows per tile;
-//   P . V:   VALU, 16 lanes per row (8 dims each), 4 rows per instruction.
+// o = sum 2^(s - m) V.  Wave w takes the 16-row tiles w, w + 4, ... and keeps
+// its own online softmax; the K/V rows of its next two tiles are loaded while
+// it computes the current one, and no barrier is taken until the four waves'
+// partials are merged at the end.
+//   q . K^T: MFMA 16x16x32 bf16, the tile's rows as the A operand and the R
+//            heads as columns 0..R-1 of B: lane (col, kg) gets the scores of
+//            rows 4 kg + i (i = 0..3) for head col;
+//   softmax: per head, over those lanes (lane swaps across the 16-lane rows);
+//   P . V:   lane (col, kg) accumulates dims 8 col .. 8 col + 7 of every head
+//            over rows 4 kg + i, taking head h's probabilities from lane
+//            (h, kg) of its row (DPP row broadcast); the four k-groups are
+//            summed once, at the end.
 template <int R, bool kPaged>
-__device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, int c, int p0, int nrows,
-                                            AttnSmem<R>& sm) {
+__device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, int c, int p0, int nrows) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = wave_id();
-  const int col = lane & 15;  // MFMA column = head (A: row in tile, PV: 8-dim block)
-  const int kg = lane >> 4;   // MFMA k-group
-  auto pos = [&](int i) { return p0 + i; };
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  __shared__ float s_m[kDenseWaves][R], s_l[kDenseWaves][R];
+  __shared__ float s_o[kDenseWaves][R][kHeadDim];
 
   uint4 qf[4];
   {
@@ -160,15 +172,6 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
     for (int s = 0; s < 4; ++s)
       qf[s] = col < R ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * kg) : make_uint4(0, 0, 0, 0);
   }
-  if (tid < R) {
-    sm.mrun[tid] = -INFINITY;
-    sm.lrun[tid] = 0.f;
-  }
-  float o[R][8];
-#pragma unroll
-  for (int h = 0; h < R; ++h)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
   // K and V rows of position p: Kg + kvoff(p), Vg + kvoff(p)
   const size_t kv_base = kPaged ? (size_t)0 : ((size_t)b * a.Hkv + g) * (size_t)a.cap * kHeadDim;
   const uint16_t* Kg = a.k + kv_base;
@@ -177,104 +180,136 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
     if constexpr (kPaged) return kv_row<true>(a.kv, b, g, p) * kHeadDim;
     else return (size_t)p * kHeadDim;
   };
-  __syncthreads();
-
-  for (int t0 = 0; t0 < nrows; t0 += 64) {
-    // K rows for the A operand and V rows for P.V of this wave's 16 rows;
-    // rows past the end are clamped to row 0 and masked out below.
-    uint4 ka[4], vv[4];
-    {
-      const int ia = t0 + 16 * w + col;
-      const int pa = pos(ia < nrows ? ia : 0);
-      const uint16_t* kr = Kg + kvoff(pa) + 8 * kg;
+  // the wave's rows of tile t (rows past nrows read row p0; their scores are masked)
+  auto gather = [&](int t, uint4 (&ka)[4], uint4 (&vv)[4]) {
+    const int ia = 16 * t + col;
+    const uint16_t* kr = Kg + kvoff(p0 + (ia < nrows ? ia : 0)) + 8 * kg;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
+    for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int iv = t0 + 16 * w + 4 * i + kg;
-        const int pv = pos(iv < nrows ? iv : 0);
-        vv[i] = *reinterpret_cast<const uint4*>(Vg + kvoff(pv) + 8 * col);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int iv = 16 * t + 4 * kg + i;
+      vv[i] = *reinterpret_cast<const uint4*>(Vg + kvoff(p0 + (iv < nrows ? iv : 0)) + 8 * col);
     }
+  };
+  float m_run = -INFINITY, l_run = 0.f;  // head col's running max and sum (lanes col < R)
+  float o[R][8];
+#pragma unroll
+  for (int h = 0; h < R; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
+  const int ntiles = (nrows + 15) >> 4;
+  // the wave's tiles t and t + 4 are in registers or in flight while it
+  // requests t + 8 (two tiles ahead)
+  uint4 ka[4], vv[4], k1[4], v1[4];
+  if (w < ntiles) gather(w, ka, vv);
+  if (w + kDenseWaves < ntiles) gather(w + kDenseWaves, k1, v1);
+#pragma unroll 1
+  for (int t = w; t < ntiles; t += kDenseWaves) {
+    uint4 kn[4], vn[4];
+    if (t + 2 * kDenseWaves < ntiles) gather(t + 2 * kDenseWaves, kn, vn);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma_16x16x32_bf16(ka[s], qf[s], acc);
-    if (col < R) {
+    float sc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * w + 4 * kg + i;
-        const int idx = t0 + rr;
-        sm.S[rr][col] = idx < nrows ? acc[i] * a.qscale : -INFINITY;
-      }
-    }
-    __syncthreads();
-    // running max / rescale / probabilities: wave w owns heads w, w+4; lane = row
+    for (int i = 0; i < 4; ++i) sc[i] = 16 * t + 4 * kg + i < nrows ? acc[i] * a.qscale : -INFINITY;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __uint_as_float(xor16_u32(__float_as_uint(mx))));
+    mx = fmaxf(mx, __uint_as_float(xor32_u32(__float_as_uint(mx))));
+    const float m_new = fmaxf(m_run, mx);  // (finite: every tile has a valid row)
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run is -inf
+    float pr[4];
 #pragma unroll
-    for (int h = w; h < R; h += 4) {
-      const float x = sm.S[lane][h];
-      const float mo = sm.mrun[h];
-      const float mn = fmaxf(mo, wave_max(x));
-      const float cr = (mn == -INFINITY) ? 1.f : exp2f(mo - mn);
-      const float pr = (x == -INFINITY) ? 0.f : exp2f(x - mn);
-      sm.S[lane][h] = pr;
-      const float ts = wave_sum(pr);
-      if (lane == 0) {
-        sm.corr[h] = cr;
-        sm.mrun[h] = mn;
-        sm.lrun[h] = __builtin_fmaf(sm.lrun[h], cr, ts);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < R; ++h) {
-      const float cr = sm.corr[h];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[h][j] *= cr;
-    }
+    for (int i = 0; i < 4; ++i) pr[i] = sc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[i] - m_new);
+    float ls = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    ls += __uint_as_float(xor16_u32(__float_as_uint(ls)));
+    ls += __uint_as_float(xor32_u32(__float_as_uint(ls)));
+    l_run = __builtin_fmaf(l_run, corr, ls);
+    m_run = m_new;
+    float vf[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * w + 4 * i + kg;
       const uint32_t vw[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-      float vf[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        vf[2 * j] = bf16_lo(vw[j]);
-        vf[2 * j + 1] = bf16_hi(vw[j]);
-      }
-#pragma unroll
-      for (int h = 0; h < R; ++h) {
-        const float pr = sm.S[rr][h];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[h][j] = __builtin_fmaf(pr, vf[j], o[h][j]);
+        vf[i][2 * j] = bf16_lo(vw[j]);
+        vf[i][2 * j + 1] = bf16_hi(vw[j]);
       }
     }
-    __syncthreads();
+    auto pv = [&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float ch = row_bcast<h>(corr);
+      float ph[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ph[i] = row_bcast<h>(pr[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float x = o[h][j] * ch;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x = __builtin_fmaf(ph[i], vf[i][j], x);
+        o[h][j] = x;
+      }
+    };
+    pv(std::integral_constant<int, 0>{});
+    if constexpr (R > 1) pv(std::integral_constant<int, 1>{});
+    if constexpr (R > 2) {
+      pv(std::integral_constant<int, 2>{});
+      pv(std::integral_constant<int, 3>{});
+    }
+    if constexpr (R > 4) {
+      pv(std::integral_constant<int, 4>{});
+      pv(std::integral_constant<int, 5>{});
+      pv(std::integral_constant<int, 6>{});
+      pv(std::integral_constant<int, 7>{});
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      ka[s] = k1[s];
+      vv[s] = v1[s];
+      k1[s] = kn[s];
+      v1[s] = vn[s];
+    }
   }
-
-  // reduce o over the four k-groups of the wave, then over the four waves
+  // the wave's partials: o summed over its four k-groups; m and l of head h
+  // sit in lane h
 #pragma unroll
   for (int h = 0; h < R; ++h)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float v = o[h][j];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
+      v += __uint_as_float(xor16_u32(__float_as_uint(v)));
+      v += __uint_as_float(xor32_u32(__float_as_uint(v)));
       o[h][j] = v;
     }
   if (kg == 0) {
 #pragma unroll
     for (int h = 0; h < R; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sm.red[w][h][8 * col + j] = o[h][j];
+      for (int j = 0; j < 8; ++j) s_o[w][h][8 * col + j] = o[h][j];
+  }
+  if (lane < R) {
+    s_m[w][lane] = m_run;  // -inf for a wave without rows
+    s_l[w][lane] = l_run;
   }
   __syncthreads();
-  for (int i = tid; i < R * kHeadDim; i += 256) {
+  for (int i = tid; i < R * kHeadDim; i += kDenseWaves * 64) {
     const int h = i / kHeadDim, d = i - h * kHeadDim;
-    const float O = (sm.red[0][h][d] + sm.red[1][h][d]) + (sm.red[2][h][d] + sm.red[3][h][d]);
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kDenseWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDenseWaves; ++ww) {
+      const float mw = s_m[ww][h];
+      const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L = __builtin_fmaf(s_l[ww][h], wt, L);
+      O = __builtin_fmaf(s_o[ww][h][d], wt, O);
+    }
     float* pc = a.ws_part + (((size_t)b * a.Hq + (size_t)(g * R + h)) * a.nch + c) * kPartFloats;
     if (d == 0) {
-      pc[0] = sm.mrun[h];
-      pc[1] = sm.lrun[h];
+      pc[0] = M;
+      pc[1] = L;
     }
     pc[4 + d] = O;
   }
@@ -284,7 +319,7 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
 // over positions [c*chunk, min((c+1)*chunk, kv_len[b])) and writes one partial
 // per head; combine_kernel merges the chunks.
 template <int R, bool kPaged>
-__global__ __launch_bounds__(256) void dense_attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(AttendArgs a) {
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
@@ -294,8 +329,7 @@ __global__ __launch_bounds__(256) void dense_attend_kernel(AttendArgs a) {
   if (c >= nch_b) return;
   const int p0 = c * a.chunk;
   const int p1 = min(p0 + a.chunk, len);
-  __shared__ AttnSmem<R> sm;
-  attend_rows<R, kPaged>(a, b, g, c, p0, p1 - p0, sm);
+  attend_rows<R, kPaged>(a, b, g, c, p0, p1 - p0);
 }
 
 // Dense path: one block per (b, kv head) merges the chunk partials of its R heads.
@@ -353,9 +387,9 @@ static hipError_t launch_dense_r(const Plan& p, const KvLayout& kv, const uint16
   float* ws_part = reinterpret_cast<float*>(ws + p.off_part);
   AttendArgs aa{q, k, v, kv_len, ws_part, scale * 1.4426950408889634f, p.Hq, p.Hkv, p.cap, p.chunk, p.nch, kv};
   if (kv.table)
-    launch_k(0, dense_attend_kernel<R, true>, dim3(p.nch, p.B * p.Hkv), dim3(256), 0, s, aa);
+    launch_k(0, dense_attend_kernel<R, true>, dim3(p.nch, p.B * p.Hkv), dim3(kDenseWaves * 64), 0, s, aa);
   else
-    launch_k(0, dense_attend_kernel<R, false>, dim3(p.nch, p.B * p.Hkv), dim3(256), 0, s, aa);
+    launch_k(0, dense_attend_kernel<R, false>, dim3(p.nch, p.B * p.Hkv), dim3(kDenseWaves * 64), 0, s, aa);
   if (profile_events().n >= 4) {  // timing mode: see adamas_profile_events
     hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess) return e;
