@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--only-workload", choices=sorted(OTHER_WORKLOADS),
                     help="instead of the headline: only this secondary workload's step and dense baseline, one "
                          "JSON line (the program SQ_COMMAND profiles)")
+    ap.add_argument("--only-prefill-encode", action="store_true",
+                    help="instead of the headline: only the full-cache key encode (prefill) of the 32K layer, "
+                         "graph replay over 16 rotating cold copies, one JSON line (profiled by SQ_COMMAND)")
     ap.add_argument("--summarize-sq", nargs=3, metavar=("WORKLOAD", "DIR_A", "DIR_B"),
                     help="no GPU: write the SQ counter summary (occupancy, VALU, LDS bank conflicts per kernel) "
                          "under profiles/ from the CSV output of the two SQ_COMMAND passes on WORKLOAD "
@@ -131,6 +134,9 @@ def main():
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     if args.sweep:
         return sweep(A, W, np, torch, dev, log)
+    if args.only_prefill_encode:
+        print(json.dumps(prefill_encode_only(A, W, np, torch, dev, args.seed, log)), flush=True)
+        return
     if args.only_workload:
         make, ncopy = OTHER_WORKLOADS[args.only_workload]
         r = other_workload(A, np, torch, dev, make(W, args.seed), ncopy, hip)
@@ -563,11 +569,13 @@ def summarize_counters(fetch_dir, write_dir):
 # Two SQ counter passes per workload (each within one pass's limits: at most
 # 8 SQ and 2 GRBM counters); GRBM_GUI_ACTIVE in both, for the normalisation.
 SQ_PASSES = {
-    "a": "SQ_WAVES,SQ_WAVE_CYCLES,SQ_BUSY_CU_CYCLES,SQ_ACTIVE_INST_VALU,GRBM_GUI_ACTIVE",
+    "a": "SQ_WAVES,SQ_WAVE_CYCLES,SQ_BUSY_CU_CYCLES,SQ_ACTIVE_INST_VALU,SQ_ACTIVE_INST_ANY,SQ_WAIT_INST_ANY,"
+         "GRBM_GUI_ACTIVE",
     "b": "SQ_INSTS_VALU,SQ_INSTS_LDS,SQ_LDS_BANK_CONFLICT,SQ_LDS_IDX_ACTIVE,GRBM_GUI_ACTIVE",
 }
 SQ_ARGS = {WORKLOAD_TAG: "--steps 8 --warmup 2 --copies 4 --no-extra --no-cpu"}
 SQ_ARGS.update({name: "--only-workload " + name for name in OTHER_WORKLOADS})
+SQ_ARGS["prefill_encode32k"] = "--only-prefill-encode"
 SQ_COMMAND = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc {counters} "
               "--output-format csv -d gpurun_out/sq_{workload}_{p} -o pmc -- python3 bench.py {args}")
 CU_NUM = 256
@@ -617,27 +625,34 @@ def summarize_sq(workload, dir_a, dir_b):
             "  w/SIMD  = SQ_WAVE_CYCLES / SQ_BUSY_CU_CYCLES: waves resident per SIMD while its CU has work (of 8)",
             "  VALU/cy = SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES: wave-cycles on VALU instructions per busy SIMD",
             "            cycle (the issue share of the SIMD when at most one wave's VALU instruction is in flight)",
+            "  ANY/cy  = SQ_ACTIVE_INST_ANY / SQ_BUSY_CU_CYCLES: the same for instructions of any kind",
+            "  wait    = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: share of resident wave-cycles spent waiting on a",
+            "            dependency (s_waitcnt on memory, LDS or a VALU result)",
             "  VALU/w, LDS/w = SQ_INSTS_VALU, SQ_INSTS_LDS per wave",
             "  cf/LDS  = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS: bank-conflict stall cycles per LDS instruction",
             "  cf/act  = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE: share of LDS-busy cycles lost to bank conflicts",
             "",
-            "%-32s %5s %7s %5s %8s %7s %7s %9s %7s %7s %7s" % (
-                "kernel", "disp", "waves", "w/blk", "us", "w/SIMD", "VALU/cy", "VALU/w", "LDS/w", "cf/LDS",
-                "cf/act")]
+            "%-32s %5s %7s %5s %8s %7s %7s %7s %6s %9s %7s %7s %7s" % (
+                "kernel", "disp", "waves", "w/blk", "us", "w/SIMD", "VALU/cy", "ANY/cy", "wait", "VALU/w", "LDS/w",
+                "cf/LDS", "cf/act")]
     for k in sorted({kk for kk, _, _ in per}):
         waves, n = mean(k, "a", "SQ_WAVES")
         wcyc, _ = mean(k, "a", "SQ_WAVE_CYCLES")
         busy, _ = mean(k, "a", "SQ_BUSY_CU_CYCLES")
         valu_act, _ = mean(k, "a", "SQ_ACTIVE_INST_VALU")
+        any_act, _ = mean(k, "a", "SQ_ACTIVE_INST_ANY")
+        wait, _ = mean(k, "a", "SQ_WAIT_INST_ANY")
         valu, _ = mean(k, "b", "SQ_INSTS_VALU")
         lds, _ = mean(k, "b", "SQ_INSTS_LDS")
         conf, _ = mean(k, "b", "SQ_LDS_BANK_CONFLICT")
         lact, _ = mean(k, "b", "SQ_LDS_IDX_ACTIVE")
         us = sum(dur[k]) / len(dur[k])
-        text.append("%-32s %5d %7.0f %5d %8.2f %7.2f %7.3f %9.1f %7.1f %7.2f %7.3f" % (
-            k[:32], n, waves, wpb[k], us, wcyc / busy, valu_act / busy, valu / waves, lds / waves,
+        text.append("%-32s %5d %7.0f %5d %8.2f %7.2f %7.3f %7.3f %6.3f %9.1f %7.1f %7.2f %7.3f" % (
+            k[:32], n, waves, wpb[k], us, wcyc / busy, valu_act / busy, any_act / busy, wait / wcyc, valu / waves,
+            lds / waves,
             conf / lds if lds else 0.0, conf / lact if lact else 0.0))
-    text += ["", "source sha256[:16]: %s  (%s)" % (source_hash("scan"), ", ".join(KERNEL_SOURCES["scan"]))]
+    src = "append_encode" if workload == "prefill_encode32k" else "scan"
+    text += ["", "source sha256[:16]: %s  (%s)" % (source_hash(src), ", ".join(KERNEL_SOURCES[src]))]
     os.makedirs(PROFILE_DIR, exist_ok=True)
     path = os.path.join(PROFILE_DIR, "sq_counters_%s.txt" % workload)
     with open(path, "w") as fh:
@@ -675,6 +690,23 @@ def summarize_trace(trace_dir, bench_json):
     with open(path, "w") as fh:
         fh.write("\n".join(text) + "\n")
     print(path)
+
+
+def prefill_encode_only(A, W, np, torch, dev, seed, log, ncopy=16, reps=8):
+    """Key encode of every cached position of the 32K layer (8 KV heads), as a
+    HIP graph of `ncopy` calls over rotating copies of K and the codes."""
+    wl = W.llama(seed, cap=32768, budget=128)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+    k0, kv_len = up(wl.k), up(wl.kv_len)
+    cases = [(k0 if i == 0 else k0.clone(), torch.zeros((wl.B, wl.Hkv, wl.cap, 32), dtype=torch.uint8, device=dev))
+             for i in range(ncopy)]
+    us = timed_graph_steps(torch, lambda c: A.encode_keys(c[0], kv_len, c[1]), cases, reps)
+    ref = cases[0][1]
+    assert all(torch.equal(c[1], ref) for c in cases[1:])
+    nbytes = int(wl.Hkv * wl.kv_len.sum()) * (256 + 32)
+    log("[bench] prefill key encode: %.2f us (%.0f GB/s)" % (us, nbytes / (us * 1e-6) / 1e9))
+    return {"workload": "prefill_encode32k", "us": round(us, 3), "bytes": nbytes,
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def timed_graph_steps(torch, fn, cases, reps):

@@ -56,6 +56,35 @@ __device__ __forceinline__ void widen32(const uint4 (&w)[4], float (&x)[32]) {
   }
 }
 
+// x[i] += s * (x[i] of the quad partner), i = base .. base+15, in one v_fmac_f32
+// per element with the partner read through a quad_perm DPP source (the
+// compiler does not fold a DPP move into fmac by itself).  A VALU write of a
+// VGPR needs two wait states before a DPP read of it, and the hazard pass does
+// not look inside asm: the block opens with s_nop 1, and inside it no
+// instruction reads through DPP a register written earlier in the block.
+#define ADAMAS_FMAC_DPP(i, sel) "v_fmac_f32_dpp %" #i ", %" #i ", %16 " sel " row_mask:0xf bank_mask:0xf\n"
+#define ADAMAS_FMAC_DPP16(sel)                                                                              \
+  "s_nop 1\n" ADAMAS_FMAC_DPP(0, sel) ADAMAS_FMAC_DPP(1, sel) ADAMAS_FMAC_DPP(2, sel) ADAMAS_FMAC_DPP(3, sel) \
+      ADAMAS_FMAC_DPP(4, sel) ADAMAS_FMAC_DPP(5, sel) ADAMAS_FMAC_DPP(6, sel) ADAMAS_FMAC_DPP(7, sel)        \
+      ADAMAS_FMAC_DPP(8, sel) ADAMAS_FMAC_DPP(9, sel) ADAMAS_FMAC_DPP(10, sel) ADAMAS_FMAC_DPP(11, sel)      \
+      ADAMAS_FMAC_DPP(12, sel) ADAMAS_FMAC_DPP(13, sel) ADAMAS_FMAC_DPP(14, sel) ADAMAS_FMAC_DPP(15, sel)
+template <int CTRL>
+__device__ __forceinline__ void fmac_quad16(float (&x)[32], int base, float s) {
+  static_assert(CTRL == kQuadXor1 || CTRL == kQuadXor2, "quad partner permutes only");
+  float* y = x + base;
+#define ADAMAS_FMAC_OPERANDS                                                                                   \
+  : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7]), "+v"(y[8]), \
+    "+v"(y[9]), "+v"(y[10]), "+v"(y[11]), "+v"(y[12]), "+v"(y[13]), "+v"(y[14]), "+v"(y[15])                   \
+  : "v"(s)
+  if constexpr (CTRL == kQuadXor1)
+    asm(ADAMAS_FMAC_DPP16("quad_perm:[1,0,3,2]") ADAMAS_FMAC_OPERANDS);
+  else
+    asm(ADAMAS_FMAC_DPP16("quad_perm:[2,3,0,1]") ADAMAS_FMAC_OPERANDS);
+#undef ADAMAS_FMAC_OPERANDS
+}
+#undef ADAMAS_FMAC_DPP16
+#undef ADAMAS_FMAC_DPP
+
 // Transform, bucketize and pack one vector held by a quad (see the layout above).
 // `quarter` = lane & 3.  Outputs this lane's 32 low-plane bits (code bit 0 of
 // coordinates 32*quarter + e at bit e) and 32 high-plane bits.
@@ -74,23 +103,21 @@ __device__ __forceinline__ void encode_quad(float (&x)[32], int quarter, uint32_
       }
     }
   }
-  // half-width 32: partner is lane ^ 1.  The lane holding x[j] (bit clear) forms
-  // partner + own = x[j] + x[j+32] (addition commutes exactly); the lane holding
-  // x[j+32] forms partner + (-own) = x[j] - x[j+32] (negation is exact).  One
-  // add with the partner as a DPP source and the sign-flipped own value.
-  {
-    const uint32_t sgn = (quarter & 1) ? 0x80000000u : 0u;
-#pragma unroll
-    for (int e = 0; e < 32; ++e)
-      x[e] = quad_perm_src<kQuadXor1>(x[e]) + __uint_as_float(__float_as_uint(x[e]) ^ sgn);
-  }
-  // half-width 64: partner is lane ^ 2
-  {
-    const uint32_t sgn = (quarter & 2) ? 0x80000000u : 0u;
-#pragma unroll
-    for (int e = 0; e < 32; ++e)
-      x[e] = quad_perm_src<kQuadXor2>(x[e]) + __uint_as_float(__float_as_uint(x[e]) ^ sgn);
-  }
+  // Half-widths 32 and 64 pair lane q with q ^ 1, then q ^ 2.  Each lane forms
+  // own + s * partner in one fma with the partner as a DPP source: the lane with
+  // the bit clear (s = +1) gets a + b; the lane with it set (s = -1) gets b - a,
+  // the exact negation of the textbook a - b (products by +-1 are exact and
+  // round-to-nearest is symmetric, so the fma rounds exactly like the add or
+  // subtract it replaces).  A lane therefore holds sigma * y with
+  // sigma = s32 * s64, i.e. -1 for quarters 1 and 2, +1 for quarters 0 and 3;
+  // the sign of a zero never matters, since a zero only ever yields a zero.
+  const float s32 = (quarter & 1) ? -1.0f : 1.0f;
+  const float s64 = (quarter & 2) ? -1.0f : 1.0f;
+  fmac_quad16<kQuadXor1>(x, 0, s32);
+  fmac_quad16<kQuadXor1>(x, 16, s32);
+  fmac_quad16<kQuadXor2>(x, 0, s64);
+  fmac_quad16<kQuadXor2>(x, 16, s64);
+  const float sigma = s32 * s64;
   // m = max |y| over the 128 coordinates (exact), t = m / 2
   float m = 0.0f;
 #pragma unroll
@@ -98,20 +125,19 @@ __device__ __forceinline__ void encode_quad(float (&x)[32], int quarter, uint32_
   m = fmaxf(m, quad_perm_src<kQuadXor1>(m));
   m = fmaxf(m, quad_perm_src<kQuadXor2>(m));
   const float t = 0.5f * m;
-  // code = [y >= -t] + [y >= 0] + [y >= t]; low bit = XOR of the three tests,
-  // high bit = [y >= 0].  Each test is the sign bit of an exactly-signed value:
-  // y + t < 0 iff y < -t, y < 0, y - t < 0 iff y < t, where y is first mapped
-  // -0 -> +0 so that -0 counts as "not below 0" (and, with t = 0, not below t).
-  // The sign bits (negated) are shifted into the two words, coordinate 31 first.
+  // code = [y >= -t] + [y >= 0] + [y >= t]; high bit = [y >= 0], low bit = 1 for
+  // codes 1 and 3.  With y = sigma * held + 0 (exact, and -0 maps to +0 so that
+  // -0 counts as "not below 0"): for y >= 0 the low bit is [y >= t], for y < 0
+  // it is [y >= -t]; both are "y - copysign(t, y) is not below 0", read from the
+  // sign bit of that exactly-signed difference (an exact zero is +0).  The
+  // negated sign bits are shifted into the two words, coordinate 31 first.
   uint32_t nlo = 0, nhi = 0;
 #pragma unroll
   for (int e = 31; e >= 0; --e) {
-    const float y = x[e] + 0.0f;
-    const uint32_t sy = __float_as_uint(y);
-    // (one three-input XOR: truth table 0x96)
-    const uint32_t sl = __builtin_amdgcn_bitop3_b32(__float_as_uint(y + t), sy, __float_as_uint(y - t), 0x96);
-    nlo = __builtin_amdgcn_alignbit(nlo, sl, 31);
-    nhi = __builtin_amdgcn_alignbit(nhi, sy, 31);
+    const float y = __builtin_fmaf(x[e], sigma, 0.0f);
+    const float v = y - __builtin_copysignf(t, y);
+    nlo = __builtin_amdgcn_alignbit(nlo, __float_as_uint(v), 31);
+    nhi = __builtin_amdgcn_alignbit(nhi, __float_as_uint(y), 31);
   }
   lo_word = ~nlo;
   hi_word = ~nhi;

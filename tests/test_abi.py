@@ -298,7 +298,7 @@ def test_bench_summarizes_sq_counters(tmp_path, monkeypatch):
     cols = ["Dispatch_Id", "Kernel_Name", "Workgroup_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
             "End_Timestamp"]
     passes = {"a": {"SQ_WAVES": 64, "SQ_WAVE_CYCLES": 800, "SQ_BUSY_CU_CYCLES": 400, "SQ_ACTIVE_INST_VALU": 100,
-                    "GRBM_GUI_ACTIVE": 9},
+                    "SQ_ACTIVE_INST_ANY": 200, "SQ_WAIT_INST_ANY": 400, "GRBM_GUI_ACTIVE": 9},
               "b": {"SQ_INSTS_VALU": 6400, "SQ_INSTS_LDS": 640, "SQ_LDS_BANK_CONFLICT": 320,
                     "SQ_LDS_IDX_ACTIVE": 1280, "GRBM_GUI_ACTIVE": 9}}
     dirs = []
@@ -320,9 +320,9 @@ def test_bench_summarizes_sq_counters(tmp_path, monkeypatch):
     text = open(tmp_path / "out" / "sq_counters_llama32k_b128.txt").read()
     row = [line for line in text.splitlines() if line.startswith("scan_kernel<4, false, false>")]
     assert len(row) == 1 and "copyBuffer" not in text
-    f = row[0].split()[-10:]
-    # dispatches, waves, waves/block, us, w/SIMD, VALU/cy, VALU/w, LDS/w, cf/LDS, cf/act
-    assert f == ["2", "64", "8", "7.00", "2.00", "0.250", "100.0", "10.0", "0.50", "0.250"], f
+    f = row[0].split()[-12:]
+    # dispatches, waves, waves/block, us, w/SIMD, VALU/cy, ANY/cy, wait, VALU/w, LDS/w, cf/LDS, cf/act
+    assert f == ["2", "64", "8", "7.00", "2.00", "0.250", "0.500", "0.500", "100.0", "10.0", "0.50", "0.250"], f
     assert "--only-workload" not in text and "--pmc SQ_WAVES" in text
 
 
