@@ -65,9 +65,14 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB, three times (the reference "
                          "kernel that scales the HBM byte counters of a rocprofv3 --pmc run)")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU: write the counter summary of the dominant kernel under profiles/ from the CSV "
-                         "output of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of PMC_COMMAND")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: write the HBM byte counter summaries of the step's kernels on WORKLOAD "
+                         "(llama32k_b128 or a secondary workload's name) under profiles/ from the CSV output of "
+                         "two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of PMC_COMMAND")
+    ap.add_argument("--only-launch-modes", action="store_true",
+                    help="instead of the headline: the 32K step in both launch modes (two kernels, single "
+                         "launch) on the same cold rotation, one JSON line (the program TRACE_COMMAND traces "
+                         "for the launch-mode comparison)")
     ap.add_argument("--only-workload", choices=sorted(OTHER_WORKLOADS),
                     help="instead of the headline: only this secondary workload's step and dense baseline, one "
                          "JSON line (the program SQ_COMMAND profiles)")
@@ -78,9 +83,10 @@ def parse():
                     help="no GPU: write the SQ counter summary (occupancy, VALU, LDS bank conflicts per kernel) "
                          "under profiles/ from the CSV output of the two SQ_COMMAND passes on WORKLOAD "
                          "(llama32k_b128 or a secondary workload's name)")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
-                    help="no GPU: write the kernel-trace summary under profiles/ from the CSV output of "
-                         "TRACE_COMMAND and the JSON line of a plain bench.py run on the same box and sources")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("NAME", "TRACE_DIR", "BENCH_JSON"),
+                    help="no GPU: write the kernel-trace summary NAME (a key of TRACE_ARGS) under profiles/ from "
+                         "the CSV output of TRACE_COMMAND and the JSON line of the same bench.py command run "
+                         "without the profiler on the same box and sources")
     return ap.parse_args()
 
 
@@ -134,15 +140,6 @@ def main():
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     if args.sweep:
         return sweep(A, W, np, torch, dev, log)
-    if args.only_prefill_encode:
-        print(json.dumps(prefill_encode_only(A, W, np, torch, dev, args.seed, log)), flush=True)
-        return
-    if args.only_workload:
-        make, ncopy = OTHER_WORKLOADS[args.only_workload]
-        r = other_workload(A, np, torch, dev, make(W, args.seed), ncopy, hip)
-        print(json.dumps(dict(r, workload=args.only_workload)), flush=True)
-        return
-
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
         src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
@@ -152,6 +149,17 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: %d MiB x 3" % args.calibrate_copy_mib)
         del src, dst
+    if args.only_prefill_encode:
+        print(json.dumps(prefill_encode_only(A, W, np, torch, dev, args.seed, log)), flush=True)
+        return
+    if args.only_launch_modes:
+        print(json.dumps(launch_modes_only(A, W, np, torch, dev, args.seed, log)), flush=True)
+        return
+    if args.only_workload:
+        make, ncopy = OTHER_WORKLOADS[args.only_workload]
+        r = other_workload(A, np, torch, dev, make(W, args.seed), ncopy, hip, name=args.only_workload)
+        print(json.dumps(dict(r, workload=args.only_workload)), flush=True)
+        return
 
     cap = args.context
     budget = args.budget
@@ -312,7 +320,7 @@ def main():
     step_bytes = code_bytes + gather_bytes + q_bytes + out_bytes + B * Hkv * (256 + 32)
 
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(dominant, algo[dominant]),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(dominant),
                 "kernel": dominant + "_kernel", "kernel_us": round(kern_us[dominant], 3),
                 "algorithmic_bytes_per_launch": algo[dominant]}
 
@@ -413,7 +421,7 @@ def main():
         torch.cuda.empty_cache()
         # the batched and long-context workloads
         for name, (make, ncopy) in OTHER_WORKLOADS.items():
-            extra[name] = other_workload(A, np, torch, dev, make(W, args.seed), ncopy, hip)
+            extra[name] = other_workload(A, np, torch, dev, make(W, args.seed), ncopy, hip, name=name)
             log("[bench] %s: %s" % (name, extra[name]))
             torch.cuda.empty_cache()
         if not args.no_sweep:
@@ -453,11 +461,24 @@ KERNEL_SOURCES = {
     "append_encode": ["kernels.hip", "device_common.h", "plan.h"],
 }
 WORKLOAD_TAG = "llama32k_b128"
-PMC_ARGS = "--steps 8 --warmup 2 --copies 4 --no-extra --no-cpu --calibrate-copy-mib 64"
+# bench.py arguments of the program each HBM byte counter run profiles
+PMC_ARGS = {WORKLOAD_TAG: "--steps 8 --warmup 2 --copies 4 --no-extra --no-cpu --calibrate-copy-mib 64"}
+PMC_ARGS.update({name: "--only-workload %s --calibrate-copy-mib 64" % name for name in OTHER_WORKLOADS})
 PMC_COMMAND = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc {counter} "
-               "--output-format csv -d gpurun_out/pmc_{tag} -o pmc -- python3 bench.py " + PMC_ARGS)
+               "--output-format csv -d gpurun_out/pmc_{workload}_{tag} -o pmc -- python3 bench.py {args}")
+# bench.py arguments of the program each kernel trace covers
+TRACE_ARGS = {WORKLOAD_TAG: "--no-extra",
+              "llama32k_b128_launch_modes": "--only-launch-modes",
+              "batched16_ragged16k-32k_b256": "--only-workload batched16_ragged16k-32k_b256"}
 TRACE_COMMAND = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -k 10 300 rocprofv3 --kernel-trace "
-                 "--stats --output-format csv -d gpurun_out/trace -o trace -- python3 bench.py --no-extra")
+                 "--stats --output-format csv -d gpurun_out/trace_{name} -o trace -- python3 bench.py {args}")
+WORKLOAD_TEXT = {
+    WORKLOAD_TAG: "Llama-3.1-8B-shaped decode layer (batch 1, 32 q / 8 kv heads, head_dim 128, 32768 cached "
+                  "positions, budget 128)",
+    "batched16_ragged16k-32k_b256": "batch 16, 32 q / 8 kv heads, head_dim 128, ragged 16K-32K cached positions, "
+                                    "budget 256",
+    "long512k_b1024": "batch 1, 32 q / 8 kv heads, head_dim 128, 524288 cached positions, budget 1024",
+}
 COPY_KIB = 64 * 1024  # the calibration copy: reads and writes 64 MiB
 
 
@@ -469,14 +490,15 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def counters_path(kernel):
-    return os.path.join(PROFILE_DIR, "%s_kernel_%s_counters.txt" % (kernel, WORKLOAD_TAG))
+def counters_path(kernel, workload=WORKLOAD_TAG):
+    return os.path.join(PROFILE_DIR, "%s_kernel_%s_counters.txt" % (kernel, workload))
 
 
-def read_traffic(kernel, algo_bytes):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; otherwise None."""
-    path = counters_path(kernel)
+def read_traffic(kernel, workload=WORKLOAD_TAG):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    otherwise None."""
+    path = counters_path(kernel, workload)
     if not os.path.exists(path):
         return None
     recorded, hbm = None, None
@@ -503,40 +525,53 @@ def _csv_rows(d, suffix):
     return rows
 
 
-def _per_dispatch(rows, counter):
+def _per_dispatch(rows, counter, with_ids=False):
     """{kernel name: [value per dispatch]} for one counter (summed over the
-    dimensions rocprofv3 reports it in)."""
+    dimensions rocprofv3 reports it in); with_ids: [(dispatch id, value)] in
+    dispatch order."""
     acc = {}
     for r in rows:
         if r.get("Counter_Name") != counter:
             continue
-        key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
+        key = (r["Kernel_Name"], int(r.get("Dispatch_Id", r.get("Correlation_Id"))))
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
     out = {}
-    for (name, _), v in acc.items():
-        out.setdefault(name, []).append(v)
+    for (name, did), v in sorted(acc.items(), key=lambda kv: kv[0][1]):
+        out.setdefault(name, []).append((did, v) if with_ids else v)
     return out
 
 
-def summarize_counters(fetch_dir, write_dir):
-    """Counter summary of the step's dominant kernel: FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch), each scaled by calibration against a copy of known size."""
+def _calibration_kib(table):
+    """The counter value of the calibration copy: the first device copies of
+    the program (--calibrate-copy-mib runs three before anything else), their
+    largest reading."""
+    copies = sorted((did, v) for name, vals in table.items() if "copyBuffer" in name for did, v in vals)
+    if len(copies) < 3:
+        raise SystemExit("fewer than three copyBuffer dispatches (was --calibrate-copy-mib given?)")
+    return max(v for _, v in copies[:3])
+
+
+def summarize_counters(workload, fetch_dir, write_dir):
+    """Counter summaries of the step's two kernels on one workload: FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by calibration against a copy
+    of known size."""
     import statistics
-    fetch = _per_dispatch(_csv_rows(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
-    write = _per_dispatch(_csv_rows(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    if workload not in PMC_ARGS:
+        raise SystemExit("unknown workload %r (one of %s)" % (workload, sorted(PMC_ARGS)))
+    fetch = _per_dispatch(_csv_rows(fetch_dir, "counter_collection.csv"), "FETCH_SIZE", with_ids=True)
+    write = _per_dispatch(_csv_rows(write_dir, "counter_collection.csv"), "WRITE_SIZE", with_ids=True)
 
     def pick(table, sub):
         names = [n for n in table if sub in n]
         if not names:
             raise SystemExit("no kernel matching %r in %s" % (sub, sorted(table)))
-        vals = [v for n in names for v in table[n]]
+        vals = [v for n in names for _, v in table[n]]
         return names, vals
 
-    _, cf = pick(fetch, "copyBuffer")
-    _, cw = pick(write, "copyBuffer")
-    # the calibration copies are the largest dispatches of the copy kernel
-    f_scale = COPY_KIB / max(cf)
-    w_scale = COPY_KIB / max(cw)
+    cf, cw = _calibration_kib(fetch), _calibration_kib(write)
+    # scale: the copy reads and writes COPY_KIB
+    f_scale = COPY_KIB / cf
+    w_scale = COPY_KIB / cw
     lines = []
     for kernel in ("select_attend", "scan"):
         nf, vf = pick(fetch, kernel + "_kernel")
@@ -544,23 +579,24 @@ def summarize_counters(fetch_dir, write_dir):
         fk, wk = statistics.mean(vf), statistics.mean(vw)
         hbm = (fk * f_scale + wk * w_scale) * 1024
         text = [
-            "rocprofv3 HBM byte counters: %s_kernel, Llama-3.1-8B-shaped decode layer "
-            "(batch 1, 32 q / 8 kv heads, head_dim 128, 32768 cached positions, budget 128)" % kernel,
+            "rocprofv3 HBM byte counters: %s_kernel, %s" % (kernel, WORKLOAD_TEXT[workload]),
             "",
-            "command (FETCH_SIZE): " + PMC_COMMAND.format(counter="FETCH_SIZE", tag="fetch"),
-            "command (WRITE_SIZE): " + PMC_COMMAND.format(counter="WRITE_SIZE", tag="write"),
+            "command (FETCH_SIZE): " + PMC_COMMAND.format(counter="FETCH_SIZE", workload=workload, tag="fetch",
+                                                          args=PMC_ARGS[workload]),
+            "command (WRITE_SIZE): " + PMC_COMMAND.format(counter="WRITE_SIZE", workload=workload, tag="write",
+                                                          args=PMC_ARGS[workload]),
             "kernel: " + nf[0],
             "dispatches: %d (FETCH_SIZE run), %d (WRITE_SIZE run)" % (len(vf), len(vw)),
             "FETCH_SIZE KiB/dispatch mean: %.1f  (min %.1f, max %.1f)" % (fk, min(vf), max(vf)),
             "WRITE_SIZE KiB/dispatch mean: %.1f  (min %.1f, max %.1f)" % (wk, min(vw), max(vw)),
-            "calibration copy (%d KiB read + written): FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB" % (
-                COPY_KIB, max(cf), max(cw)),
+            "calibration copy (%d KiB read + written, the first copies of the program): FETCH_SIZE %.1f KiB, "
+            "WRITE_SIZE %.1f KiB" % (COPY_KIB, cf, cw),
             "scale: FETCH_SIZE x %.3f, WRITE_SIZE x %.3f" % (f_scale, w_scale),
             "hbm_bytes_per_launch: %d" % int(hbm),
             "source sha256[:16]: %s  (%s)" % (source_hash(kernel), ", ".join(KERNEL_SOURCES[kernel])),
         ]
         os.makedirs(PROFILE_DIR, exist_ok=True)
-        with open(counters_path(kernel), "w") as fh:
+        with open(counters_path(kernel, workload), "w") as fh:
             fh.write("\n".join(text) + "\n")
         lines.append("%s: %.0f bytes/launch" % (kernel, hbm))
     print("\n".join(lines))
@@ -660,9 +696,11 @@ def summarize_sq(workload, dir_a, dir_b):
     print(path)
 
 
-def summarize_trace(trace_dir, bench_json):
-    """Kernel-trace statistics of TRACE_COMMAND beside the bench's own
-    event-timed kernel means from the same run."""
+def summarize_trace(name, trace_dir, bench_json):
+    """Kernel-trace statistics of one TRACE_COMMAND beside the JSON line of the
+    same bench.py command run without the profiler."""
+    if name not in TRACE_ARGS:
+        raise SystemExit("unknown trace %r (one of %s)" % (name, sorted(TRACE_ARGS)))
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
     res = None
     for line in open(bench_json):
@@ -671,25 +709,51 @@ def summarize_trace(trace_dir, bench_json):
             res = json.loads(line)
     if res is None:
         raise SystemExit("no JSON line in " + bench_json)
-    text = ["rocprofv3 kernel trace: Adamas decode step, Llama-3.1-8B-shaped decode layer "
-            "(batch 1, 32 q / 8 kv heads, head_dim 128, 32768 cached positions, budget 128)", "",
-            "command: " + TRACE_COMMAND, "",
+    what = WORKLOAD_TEXT.get(name, WORKLOAD_TEXT[WORKLOAD_TAG])
+    text = ["rocprofv3 kernel trace (%s): Adamas decode step, %s" % (name, what), "",
+            "command: " + TRACE_COMMAND.format(name=name, args=TRACE_ARGS[name]), "",
             "%-60s %7s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         nm = r["Name"].split("(")[0]
         text.append("%-60s %7s %10.3f %10.3f %10.3f" % (nm[-60:], r["Calls"], float(r["AverageNs"]) / 1e3,
                                                        float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
-    text += ["", "python3 bench.py without the profiler, same box and sources, just before (HIP events recorded by",
-             "each kernel's own dispatch; under the profiler those events read high, so they are not used):",
-             "kernel_us: " + json.dumps(res["extra"]["kernel_us"]),
-             "step us (graph replay, cold): %s" % res["value"],
-             "source sha256[:16]: %s  (%s)" % (source_hash("select_attend"),
+    text += ["", "python3 bench.py %s without the profiler, same box and sources, just before (under the profiler" %
+             TRACE_ARGS[name], "the library's dispatch-recorded events read high, so they are not used):"]
+    if "extra" in res:  # the headline line
+        text += ["kernel_us: " + json.dumps(res["extra"]["kernel_us"]),
+                 "step us (graph replay, cold): %s" % res["value"]]
+    else:
+        text += ["result: " + json.dumps(res)]
+    text += ["source sha256[:16]: %s  (%s)" % (source_hash("select_attend"),
                                              ", ".join(KERNEL_SOURCES["select_attend"]))]
     os.makedirs(PROFILE_DIR, exist_ok=True)
-    path = os.path.join(PROFILE_DIR, "decode_step_%s_kernel_trace.txt" % WORKLOAD_TAG)
+    path = os.path.join(PROFILE_DIR, "decode_step_%s_kernel_trace.txt" % name)
     with open(path, "w") as fh:
         fh.write("\n".join(text) + "\n")
     print(path)
+
+
+def launch_modes_only(A, W, np, torch, dev, seed, log, ncopy=16, steps=64):
+    """The 32K step (append-encode + decode) as graphs of `steps` steps over
+    rotating copies, in launch mode 0 (two kernels) and 1 (single launch)."""
+    wl = W.llama(seed, cap=32768, budget=128)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+    q, k, v, kv_len = up(wl.q), up(wl.k), up(wl.v), up(wl.kv_len)
+    codes = torch.zeros((wl.B, wl.Hkv, wl.cap, 32), dtype=torch.uint8, device=dev)
+    A.encode_keys(k, kv_len, codes)
+    cases = [(q, k, v, codes)] + [tuple(t.clone() for t in (q, k, v, codes)) for _ in range(ncopy - 1)]
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device=dev)
+    ws = A.alloc_workspace(A.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap, wl.budget), dev)
+    step = lambda c: A.decode_step(c[0], c[1], c[2], c[3], kv_len, wl.budget, wl.scale, out, ws, append=True)
+    res = {"workload": "llama32k_b128_launch_modes", "steps_per_mode": 2 * steps}
+    for mode, key in ((0, "two_kernels"), (1, "single_launch")):
+        A.decode_launch_mode(mode)
+        us = timed_graph_steps(torch, step, [cases[i % ncopy] for i in range(steps)], 2)
+        res[key + "_us"] = round(us, 3)
+        res[key + "_launches_per_step"] = A.last_launch_count()
+        log("[bench] launch mode %d: %.2f us per step (%d launches)" % (mode, us, A.last_launch_count()))
+    A.decode_launch_mode(0)
+    return res
 
 
 def prefill_encode_only(A, W, np, torch, dev, seed, log, ncopy=16, reps=8):
@@ -854,7 +918,7 @@ def unique_rows(np, sel, Hkv):
                for s in (sel[b, g * grp:(g + 1) * grp],))
 
 
-def other_workload(A, np, torch, dev, wl, ncopy, hip=None):
+def other_workload(A, np, torch, dev, wl, ncopy, hip=None, name=None):
     """Step latency (append-encode + decode, rotating `ncopy` copies of q, K, V
     and codes) and the dense baseline on one workload; with `hip`, also the
     kernels' durations, the deduplicated algorithmic bytes and the fractions of
@@ -896,6 +960,10 @@ def other_workload(A, np, torch, dev, wl, ncopy, hip=None):
                 "kernel_us": {n: round(t, 3) for n, t in kus.items()},
                 "kernel_GBps": {n: round(algo[n] / (kus[n] * 1e3), 1) for n in kus},
                 "kernel_hbm_frac": {n: round(algo[n] / (kus[n] * 1e3) / HBM_PEAK_GBS, 4) for n in kus}})
+    if name is not None:
+        # HBM bytes per launch from the committed counter summaries (None when
+        # absent or taken on other sources)
+        res["kernel_traffic_bytes"] = {n: read_traffic(n, name) for n in kus}
     return res
 
 

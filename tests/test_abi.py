@@ -326,6 +326,48 @@ def test_bench_summarizes_sq_counters(tmp_path, monkeypatch):
     assert "--only-workload" not in text and "--pmc SQ_WAVES" in text
 
 
+def test_bench_summarizes_byte_counters(tmp_path, monkeypatch):
+    """The HBM byte counter summary scales each kernel's FETCH_SIZE and
+    WRITE_SIZE by the first device copies of the program (the calibration
+    copies), not by larger copies made later, and records the command of the
+    workload it covers."""
+    import csv
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod_pmc", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    dirs = []
+    for counter, calib, big, sel, scan in (("FETCH_SIZE", 32768.0, 500000.0, 300.0, 1000.0),
+                                           ("WRITE_SIZE", 16384.0, 250000.0, 2.0, 40.0)):
+        d = tmp_path / counter
+        d.mkdir()
+        with open(d / "pmc_counter_collection.csv", "w", newline="") as fh:
+            w = csv.writer(fh)
+            w.writerow(cols)
+            did = 1
+            for _ in range(3):  # calibration copies, two XCD halves each
+                for half in (0.5, 0.5):
+                    w.writerow([did, "__amd_rocclr_copyBuffer", counter, calib * half])
+                did += 1
+            w.writerow([did, "__amd_rocclr_copyBuffer", counter, big])  # a later clone of a big tensor
+            did += 1
+            for _ in range(2):
+                w.writerow([did, "void adamas::scan_kernel<4, false, false>(adamas::ScanArgs)", counter, scan])
+                w.writerow([did + 1, "void adamas::select_attend_kernel<false>(adamas::SelectArgs)", counter, sel])
+                did += 2
+        dirs.append(str(d))
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path / "out"))
+    bench.summarize_counters("batched16_ragged16k-32k_b256", *dirs)
+    text = open(tmp_path / "out" / "scan_kernel_batched16_ragged16k-32k_b256_counters.txt").read()
+    # scale 2 for FETCH (65536 / 32768), 4 for WRITE (65536 / 16384)
+    assert "hbm_bytes_per_launch: %d" % int((1000 * 2 + 40 * 4) * 1024) in text, text
+    assert "--only-workload batched16_ragged16k-32k_b256 --calibrate-copy-mib 64" in text
+    # read back for the bench line while the kernel sources are the ones hashed
+    assert bench.read_traffic("scan", "batched16_ragged16k-32k_b256") == (1000 * 2 + 40 * 4) * 1024
+    assert bench.read_traffic("scan", "long512k_b1024") is None
+
+
 def test_workspace_for_any_int32_budget(A):
     """A budget past the capacity plans like budget = capacity (no step selects
     more rows), so every positive int32 budget gives a sane size and no
