@@ -276,15 +276,16 @@ def test_bench_reads_committed_counters():
     spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
     bench = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(bench)
-    for kernel in ("scan", "select_attend"):
-        path = bench.counters_path(kernel)
-        assert os.path.exists(path), path
-        text = open(path).read()
-        got = bench.read_traffic(kernel, 0)
-        if bench.source_hash(kernel) in text:
-            assert got is not None and got > 0
-        else:
-            assert got is None
+    for workload in bench.PMC_ARGS:
+        for kernel in ("scan", "select_attend"):
+            path = bench.counters_path(kernel, workload)
+            assert os.path.exists(path), path
+            text = open(path).read()
+            got = bench.read_traffic(kernel, workload)
+            if bench.source_hash(kernel) in text:
+                assert got is not None and got > 0
+            else:
+                assert got is None
 
 
 def test_bench_summarizes_sq_counters(tmp_path, monkeypatch):
