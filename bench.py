@@ -191,7 +191,7 @@ def main():
 
     def step_unfused(c):
         q, k, v, codes = c
-        A.encode_keys(k, kv_len, codes, start=start)
+        A.encode_keys(k, kv_len, codes, start=start, max_rows=1)
         A.decode_step(q, k, v, codes, kv_len, budget, wl.scale, out, ws)
 
     def dense_step(c):
@@ -285,7 +285,7 @@ def main():
     for i in range(n_prof + 8):
         q, k, v, codes = copies[i % R]
         A.profile_events(ev_enc)
-        A.encode_keys(k, kv_len, codes, start=start)
+        A.encode_keys(k, kv_len, codes, start=start, max_rows=1)
         A.profile_events(evs)
         A.decode_step(q, k, v, codes, kv_len, budget, wl.scale, out, ws, append=True)
         A.profile_events(None)

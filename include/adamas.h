@@ -273,6 +273,26 @@ adamas_status adamas_paged_encode_keys(const adamas_dims* d, const adamas_pages*
                                        const int32_t* start, const int32_t* end, uint8_t* codes_pool,
                                        void* stream);
 
+/*
+ * adamas_encode_keys (and its paged form) for a caller that knows, on the host,
+ * a bound on how many positions each range holds -- an append of one key per
+ * step (max_rows = 1), a chunked prefill.  The ranges stay in device memory, so
+ * without the bound the launch is sized for the whole capacity; with it, for
+ * max_rows positions per (b, kv head).  Same operation and outputs (the blog
+ * "ADAMAS：稀疏注意力优化技术解析与应用实践", section 3.1: key codes maintained
+ * per appended key).
+ *   max_rows  > 0; intended: >= end[b] - start[b] for every b.  It sizes the grid
+ *             only: every block walks its positions with a stride, so a bound that
+ *             is too small encodes every position all the same, only more slowly.
+ * Errors: as adamas_encode_keys / adamas_paged_encode_keys, plus INVALID_ARGUMENT
+ * for max_rows < 1.
+ */
+adamas_status adamas_encode_keys_bounded(const adamas_dims* d, const void* k, const int32_t* start,
+                                         const int32_t* end, int32_t max_rows, uint8_t* codes, void* stream);
+adamas_status adamas_paged_encode_keys_bounded(const adamas_dims* d, const adamas_pages* pages,
+                                               const void* k_pool, const int32_t* start, const int32_t* end,
+                                               int32_t max_rows, uint8_t* codes_pool, void* stream);
+
 /* The decode step on paged pools: what adamas_forced_decode_step computes
  * (forced may be NULL: no forced positions; append 0 or 1), reading K, V and
  * codes through the block table.  dist and sel_idx stay indexed by position.
@@ -297,7 +317,8 @@ adamas_status dense_paged_decode_attention(const adamas_dims* d, const adamas_pa
  * CALLING THREAD: launch i of a call (counting from 0) is bracketed by the HIP
  * events events[2*i] (start) and events[2*i+1] (stop), recorded on the call's
  * stream by the kernel dispatch itself, for every i with 2*i+1 < n_events.
- * Launch order: adamas_encode_keys, adamas_paged_encode_keys -> 0 encode;
+ * Launch order: adamas_encode_keys, adamas_paged_encode_keys and their _bounded
+ * forms -> 0 encode;
  * adamas_decode_step, adamas_append_decode_step, adamas_forced_decode_step and
  * adamas_paged_decode_step -> 0 scan, 1 select+attend (or 0 the single-launch
  * step, see adamas_decode_launch_mode); dense_decode_attention

@@ -84,6 +84,10 @@ _lib.adamas_forced_decode_step.argtypes = [_dims_p, ctypes.POINTER(Forced), ctyp
 _lib.adamas_forced_decode_step.restype = ctypes.c_int
 _lib.adamas_paged_encode_keys.argtypes = [_dims_p, _pages_p, _vp, _vp, _vp, _vp, _vp]
 _lib.adamas_paged_encode_keys.restype = ctypes.c_int
+_lib.adamas_encode_keys_bounded.argtypes = [_dims_p, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp]
+_lib.adamas_encode_keys_bounded.restype = ctypes.c_int
+_lib.adamas_paged_encode_keys_bounded.argtypes = [_dims_p, _pages_p, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp]
+_lib.adamas_paged_encode_keys_bounded.restype = ctypes.c_int
 _lib.adamas_paged_decode_step.argtypes = [_dims_p, _pages_p, ctypes.POINTER(Forced), ctypes.c_int32, _vp, _vp, _vp,
                                           _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
                                           ctypes.c_size_t, _vp]
@@ -110,6 +114,7 @@ _lib.adamas_abi_version.restype = ctypes.c_int32
 EXPORTED_SYMBOLS = ("adamas_encode_keys", "adamas_decode_workspace_size", "adamas_decode_step",
                     "adamas_decode_step_noalloc",
                     "adamas_append_decode_step", "adamas_forced_decode_step", "adamas_paged_encode_keys",
+                    "adamas_encode_keys_bounded", "adamas_paged_encode_keys_bounded",
                     "adamas_paged_decode_step", "dense_decode_workspace_size", "dense_decode_attention",
                     "dense_paged_decode_attention", "adamas_profile_events", "adamas_status_string",
                     "adamas_abi_version", "adamas_decode_launch_mode", "adamas_last_launch_count")
@@ -172,9 +177,10 @@ def _check(status, where):
         raise AdamasError(status, where)
 
 
-def encode_keys(k, end, codes, start=None, stream=None, num_q_heads=None, pages=None):
+def encode_keys(k, end, codes, start=None, stream=None, num_q_heads=None, pages=None, max_rows=None):
     """Encode keys at positions [start[b], end[b]) of k [B][Hkv][cap][128] into codes [B][Hkv][cap][32]
-    (with `pages`: of the pools k [num_pages][Hkv][page][128] into codes [num_pages][Hkv][page][32])."""
+    (with `pages`: of the pools k [num_pages][Hkv][page][128] into codes [num_pages][Hkv][page][32]).
+    max_rows: the caller's bound on end[b] - start[b] (adamas_encode_keys_bounded: it sizes the launch)."""
     if k.dim() != 4:
         raise ValueError("k must be 4-D")
     dev = k.device
@@ -184,6 +190,12 @@ def encode_keys(k, end, codes, start=None, stream=None, num_q_heads=None, pages=
         _shape(end, "end", (B,), dev)
         _shape(start, "start", (B,), dev)
         d = dims(B, num_q_heads or Hkv, Hkv, cap, hd)
+        if max_rows is not None:
+            st = _lib.adamas_encode_keys_bounded(ctypes.byref(d), _ptr(k, "k", 2),
+                                                 _ptr(start, "start", 4, optional=True), _ptr(end, "end", 4),
+                                                 int(max_rows), _ptr(codes, "codes", 1), _stream(stream))
+            _check(st, "adamas_encode_keys_bounded")
+            return
         st = _lib.adamas_encode_keys(ctypes.byref(d), _ptr(k, "k", 2), _ptr(start, "start", 4, optional=True),
                                      _ptr(end, "end", 4), _ptr(codes, "codes", 1), _stream(stream))
         _check(st, "adamas_encode_keys")
@@ -198,6 +210,12 @@ def encode_keys(k, end, codes, start=None, stream=None, num_q_heads=None, pages=
     _shape(pages.table, "block_table", pages.table.shape, dev)
     d = dims(B, num_q_heads or Hkv, Hkv, pages.capacity, hd)
     pc = pages.c(num_pages)
+    if max_rows is not None:
+        st = _lib.adamas_paged_encode_keys_bounded(ctypes.byref(d), ctypes.byref(pc), _ptr(k, "k", 2),
+                                                   _ptr(start, "start", 4, optional=True), _ptr(end, "end", 4),
+                                                   int(max_rows), _ptr(codes, "codes", 1), _stream(stream))
+        _check(st, "adamas_paged_encode_keys_bounded")
+        return
     st = _lib.adamas_paged_encode_keys(ctypes.byref(d), ctypes.byref(pc), _ptr(k, "k", 2),
                                        _ptr(start, "start", 4, optional=True), _ptr(end, "end", 4),
                                        _ptr(codes, "codes", 1), _stream(stream))

@@ -99,16 +99,17 @@ adamas_status adamas_profile_events(void* const* events, int32_t n_events) {
 namespace {
 
 adamas_status encode_common(const adamas_dims* d, const adamas_pages* pages, const void* k, const int32_t* start,
-                            const int32_t* end, uint8_t* codes, void* stream) {
+                            const int32_t* end, uint8_t* codes, void* stream, int32_t max_rows = 0) {
   adamas_status st = check_dims(d, false);
   if (st != ADAMAS_OK) return st;
+  if (max_rows < 0) return ADAMAS_ERR_INVALID_ARGUMENT;
   if (!k || !end || !codes) return ADAMAS_ERR_INVALID_ARGUMENT;
   if (!aligned(k, 16) || !aligned(codes, 16) || !aligned(end, 4) || (start && !aligned(start, 4)))
     return ADAMAS_ERR_INVALID_ARGUMENT;
   adamas::KvLayout kv = contiguous_layout(d);
   if (pages && (st = paged_layout(d, pages, &kv)) != ADAMAS_OK) return st;
   hipError_t e = adamas::launch_encode_keys(d->batch, kv, static_cast<const uint16_t*>(k), start, end, codes,
-                                            static_cast<hipStream_t>(stream));
+                                            static_cast<hipStream_t>(stream), max_rows);
   return e == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_HIP;
 }
 
@@ -126,6 +127,19 @@ adamas_status adamas_paged_encode_keys(const adamas_dims* d, const adamas_pages*
                                        void* stream) {
   if (!pages) return ADAMAS_ERR_INVALID_ARGUMENT;
   return encode_common(d, pages, k_pool, start, end, codes_pool, stream);
+}
+
+adamas_status adamas_encode_keys_bounded(const adamas_dims* d, const void* k, const int32_t* start,
+                                         const int32_t* end, int32_t max_rows, uint8_t* codes, void* stream) {
+  if (max_rows < 1) return ADAMAS_ERR_INVALID_ARGUMENT;
+  return encode_common(d, nullptr, k, start, end, codes, stream, max_rows);
+}
+
+adamas_status adamas_paged_encode_keys_bounded(const adamas_dims* d, const adamas_pages* pages,
+                                               const void* k_pool, const int32_t* start, const int32_t* end,
+                                               int32_t max_rows, uint8_t* codes_pool, void* stream) {
+  if (!pages || max_rows < 1) return ADAMAS_ERR_INVALID_ARGUMENT;
+  return encode_common(d, pages, k_pool, start, end, codes_pool, stream, max_rows);
 }
 
 size_t adamas_decode_workspace_size(const adamas_dims* d, int32_t budget) {

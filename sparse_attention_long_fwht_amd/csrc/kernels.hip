@@ -368,9 +368,10 @@ static void launch_k(int i, Kernel kernel, dim3 grid, dim3 block, uint32_t shmem
 }
 
 hipError_t launch_encode_keys(int B, const KvLayout& kv, const uint16_t* k, const int32_t* start,
-                              const int32_t* end, uint8_t* codes, hipStream_t s) {
+                              const int32_t* end, uint8_t* codes, hipStream_t s, int max_rows) {
   const int bg = B * kv.Hkv;
-  int nblk = (kv.cap + 63) / 64;
+  const int rows = max_rows > 0 && max_rows < kv.cap ? max_rows : kv.cap;
+  int nblk = (rows + 63) / 64;
   const int cap_blocks = 2048 / bg > 0 ? 2048 / bg : 1;
   if (nblk > cap_blocks) nblk = cap_blocks;
   if (kv.table)

@@ -191,8 +191,10 @@ int& launch_mode();
 int& launch_count();
 
 // ---- launchers (kernels.hip, decode.hip); kv.table == nullptr: contiguous caches ----
+// max_rows > 0: the caller's bound on end[b] - start[b], which sizes the grid
+// only (each block walks its range with a stride, so any bound stays correct)
 hipError_t launch_encode_keys(int B, const KvLayout& kv, const uint16_t* k, const int32_t* start,
-                              const int32_t* end, uint8_t* codes, hipStream_t s);
+                              const int32_t* end, uint8_t* codes, hipStream_t s, int max_rows = 0);
 
 // Forced positions of a decode step: p < sink, p >= kv_len[b] - recent, or bit
 // p % 32 of mask[b * mask_words + p / 32] (mask may be null).  All zero: none.

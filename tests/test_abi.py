@@ -162,6 +162,13 @@ def test_encode_and_dense_reject_invalid_arguments(A):
     assert lib.adamas_encode_keys(ctypes.byref(d), FAKE, None, None, FAKE, None) == A.ERR_INVALID_ARGUMENT
     assert lib.adamas_encode_keys(ctypes.byref(A.dims(1, 8, 8, 1024, head_dim=256)), FAKE, None, FAKE, FAKE,
                                   None) == A.ERR_UNSUPPORTED
+    # the bounded form: a bound below 1 is rejected, the other checks are the same
+    for bad in (0, -1, -(1 << 31)):
+        assert lib.adamas_encode_keys_bounded(ctypes.byref(d), FAKE, None, FAKE, bad, FAKE,
+                                              None) == A.ERR_INVALID_ARGUMENT
+    assert lib.adamas_encode_keys_bounded(ctypes.byref(d), None, None, FAKE, 1, FAKE, None) == A.ERR_INVALID_ARGUMENT
+    assert lib.adamas_paged_encode_keys_bounded(ctypes.byref(d), None, FAKE, None, FAKE, 1, FAKE,
+                                                None) == A.ERR_INVALID_ARGUMENT
     assert lib.dense_decode_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE, 0,
                                       None) == A.ERR_WORKSPACE
     assert lib.dense_decode_attention(ctypes.byref(d), FAKE, None, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE,

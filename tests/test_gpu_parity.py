@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from helpers import DeviceCase, assert_out_close, from_dev, to_dev
+from helpers import DeviceCase, assert_out_close, from_dev, paginate, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -513,6 +513,52 @@ def test_encode_keys_arbitrary_ranges(env):
         s, e = int(start[b]), int(end[b])
         assert np.array_equal(got[b, :, s:e], ref[b, :, s:e])
         assert np.all(got[b, :, :s] == 0xA5) and np.all(got[b, :, e:] == 0xA5)
+
+
+def test_encode_keys_bounded(env):
+    """adamas_encode_keys_bounded writes exactly what adamas_encode_keys writes,
+    whatever the bound: one key per sequence with max_rows = 1, whole ragged
+    ranges with a bound far below their lengths (every block then walks many
+    passes) and one above the capacity; and the paged form into shuffled pages."""
+    A, torch, oracle = env
+    wl = W.llama(41, cap=3000, budget=8, B=3, Hq=8, Hkv=2, kv_len=np.array([3000, 1537, 1], np.int32))
+    case = DeviceCase(wl, A, torch, encode=False)
+    end = to_dev(wl.kv_len, torch)
+    ref = oracle.encode_keys(wl.k, wl.kv_len)
+    # appended keys
+    start = to_dev(wl.kv_len - 1, torch)
+    case.codes.fill_(0x5A)
+    A.encode_keys(case.k, end, case.codes, start=start, max_rows=1)
+    torch.cuda.synchronize()
+    got = from_dev(case.codes)
+    for b in range(wl.B):
+        L = int(wl.kv_len[b])
+        assert np.array_equal(got[b, :, L - 1], ref[b, :, L - 1])
+        assert np.all(got[b, :, : L - 1] == 0x5A) and np.all(got[b, :, L:] == 0x5A)
+    # whole ranges, bounds too small and too large
+    for bound in (5, 64, 65, 1 << 30):
+        case.codes.fill_(0x5A)
+        A.encode_keys(case.k, end, case.codes, max_rows=bound)
+        torch.cuda.synchronize()
+        got = from_dev(case.codes)
+        for b in range(wl.B):
+            L = int(wl.kv_len[b])
+            assert np.array_equal(got[b, :, :L], ref[b, :, :L]), bound
+            assert np.all(got[b, :, L:] == 0x5A), bound
+    # paged pools (pages of 64, shuffled), bound 1 for the appended keys
+    page = 64
+    pool_k, table = paginate(wl.k, page, np.random.default_rng(5))
+    num_pages = pool_k.shape[0]
+    pk = to_dev(pool_k, torch)
+    pcodes = torch.full((num_pages, wl.Hkv, page, 32), 0x5A, dtype=torch.uint8, device="cuda")
+    pages = A.Pages(to_dev(table, torch), page, capacity=wl.cap)
+    A.encode_keys(pk, end, pcodes, start=start, pages=pages, max_rows=1)
+    torch.cuda.synchronize()
+    pc = from_dev(pcodes)
+    for b in range(wl.B):
+        p = int(wl.kv_len[b]) - 1
+        row = table[b, p // page]
+        assert np.array_equal(pc[row, :, p % page], ref[b, :, p])
 
 
 def test_dense_llama32k(env):
