@@ -235,7 +235,12 @@ size_t dense_decode_workspace_size(const adamas_dims* d);
  * Dense decode attention, the comparison baseline the pages measure Adamas
  * against: out[b][h] = softmax attention of q[b][h] over every position
  * p < kv_len[b] of KV head g = h / (Hq/Hkv) (0 where kv_len[b] = 0).  Same
- * layouts, preconditions and errors as adamas_decode_step.
+ * layouts, preconditions and errors as adamas_decode_step.  One launch: each
+ * block attends one chunk of positions and the last block of a (b, KV head)
+ * group to finish merges the group's chunk partials.  The workspace needs no
+ * initialisation (its per-group counters carry a tag of the call); calls that
+ * share a workspace must not overlap in time (the same holds for every entry
+ * point's workspace).
  */
 adamas_status dense_decode_attention(const adamas_dims* d, const void* q, const void* k, const void* v,
                                      const int32_t* kv_len, float scale, float* out, void* workspace,
@@ -322,8 +327,7 @@ adamas_status dense_paged_decode_attention(const adamas_dims* d, const adamas_pa
  * adamas_decode_step, adamas_append_decode_step, adamas_forced_decode_step and
  * adamas_paged_decode_step -> 0 scan, 1 select+attend (or 0 the single-launch
  * step, see adamas_decode_launch_mode); dense_decode_attention
- * and dense_paged_decode_attention ->
- * 0 attend, 1 combine.  While timing is on, a call waits (on the host) for each
+ * and dense_paged_decode_attention -> 0 attend (and merge).  While timing is on, a call waits (on the host) for each
  * of its kernels before launching the next, so that every event pair brackets
  * one kernel and not the dispatch gap after the previous one.
  *   events    array of hipEvent_t handles (as void*) created by the caller with

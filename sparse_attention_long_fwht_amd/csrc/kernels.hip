@@ -11,8 +11,8 @@
 //                      (prefill and append), four lanes per key vector
 // dense_attend_kernel  per (b, kv head, chunk): exact softmax attention of the
 //                      group's R queries over every cached position of the chunk,
-//                      one (m, l, o) partial per head
-// combine_kernel       per (b, kv head): merges the chunk partials into out
+//                      one (m, l, o) partial per head; the block that finds all
+//                      of its group's partials in place merges them into out
 // (The sparse decode step itself lives in decode.hip.)
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -75,6 +75,8 @@ struct AttendArgs {
   const uint16_t* v;
   const int32_t* kv_len;
   float* ws_part;       // [B][Hq][nch][kPartFloats]
+  unsigned long long* ws_gen;  // [B][Hkv]: the group's generation, advanced once per call
+  float* out;           // [B][Hq][128]
   float qscale;         // softmax scale * log2(e)
   int Hq, Hkv, cap, chunk, nch;
   KvLayout kv;
@@ -87,7 +89,12 @@ struct AttendArgs {
 template <int R>
 __device__ __forceinline__ void combine_group(const float* __restrict__ part, int nch, int nch_b,
                                               float* __restrict__ out, float (*s_w)[kMaxChunks], float* s_L) {
-  auto ld = [](const float* p) { return *p; };
+  // (the partials were written through by other blocks of this kernel: read
+  // them coherently)
+  auto ld = [](const float* p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+  };
   const int tid = threadIdx.x;
   // 1. m and l of every (head, chunk)
   for (int i = tid; i < R * kMaxChunks; i += 256) {
@@ -306,50 +313,80 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
       L = __builtin_fmaf(s_l[ww][h], wt, L);
       O = __builtin_fmaf(s_o[ww][h][d], wt, O);
     }
-    float* pc = a.ws_part + (((size_t)b * a.Hq + (size_t)(g * R + h)) * a.nch + c) * kPartFloats;
+    // written through, for the group's merging block in this same kernel
+    uint32_t* pc = reinterpret_cast<uint32_t*>(a.ws_part) +
+                   (((size_t)b * a.Hq + (size_t)(g * R + h)) * a.nch + c) * kPartFloats;
     if (d == 0) {
-      pc[0] = M;
-      pc[1] = L;
+      __hip_atomic_store(pc, __float_as_uint(M), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pc + 1, __float_as_uint(L), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    pc[4 + d] = O;
+    __hip_atomic_store(pc + 4 + d, __float_as_uint(O), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// The tag chunk c of a group writes beside its partial in a call whose
+// generation is gen: a 64-bit hash (a splitmix64 finalizer), so that no partial
+// left by another call, and no other content of the workspace, matches it.
+__device__ __forceinline__ unsigned long long chunk_tag(unsigned long long gen, int c) {
+  unsigned long long z = gen * 0x100000001B3ull + (unsigned long long)c + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
 }
 
 // Dense decode attention: block (c, b*Hkv + g) attends the group's R queries
 // over positions [c*chunk, min((c+1)*chunk, kv_len[b])) and writes one partial
-// per head; combine_kernel merges the chunks.
+// per head; a block that finds every chunk's partial of its group in place
+// merges them into out.  No block waits for another:
+//   - every block reads the group's generation word when it starts;
+//   - it writes its partial through to the point of coherence, then a tag of
+//     (generation, chunk) in the pad words of its head-0 partial;
+//   - it then reads every chunk's tag; if all match, it merges and advances
+//     the generation.
+// Of two blocks finishing together at least one sees all tags (each reads only
+// after its own tag has reached the point of coherence); if both do, both
+// write the same out (the merge order is fixed).  The next call sees the new
+// generation, so tags left by this one never match; arbitrary workspace
+// content matches no hash, so the workspace needs no initialisation.
 template <int R, bool kPaged>
 __global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(AttendArgs a) {
+  __shared__ float s_w[R][kMaxChunks];
+  __shared__ float s_lc[R * (kMaxChunks + 1)];
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
   const int c = blockIdx.x;
   const int len = min(a.kv_len[b], a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
   const int nch_b = (max(len, 0) + a.chunk - 1) / a.chunk;
+  const size_t bh0 = (size_t)b * a.Hq + (size_t)(g * R);
+  if (nch_b == 0) {  // no cached position: attention over the empty set is the zero vector
+    if (c == 0)
+      for (int i = threadIdx.x; i < R * kHeadDim; i += kDenseWaves * 64) a.out[bh0 * kHeadDim + i] = 0.f;
+    return;
+  }
   if (c >= nch_b) return;
+  unsigned long long* genp = a.ws_gen + bg;
+  const unsigned long long gen = __hip_atomic_load(genp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int p0 = c * a.chunk;
   const int p1 = min(p0 + a.chunk, len);
   attend_rows<R, kPaged>(a, b, g, c, p0, p1 - p0);
-}
-
-// Dense path: one block per (b, kv head) merges the chunk partials of its R heads.
-template <int R>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, const int32_t* kv_len,
-                                                      float* __restrict__ out, int Hq, int Hkv, int chunk,
-                                                      int nch) {
-  __shared__ float s_w[R][kMaxChunks];
-  __shared__ float s_l[R * (kMaxChunks + 1)];
-  const int bg = blockIdx.x;
-  const int b = bg / Hkv;
-  const int g = bg - b * Hkv;
-  // (clamped like the attend kernel's: the nch chunks cover the capacity)
-  const int nch_b = (max(min(kv_len[b], nch * chunk), 0) + chunk - 1) / chunk;
-  const size_t bh0 = (size_t)b * Hq + (size_t)(g * R);
-  if (nch_b == 0) {  // no cached position: attention over the empty set is the zero vector
-    for (int i = threadIdx.x; i < R * kHeadDim; i += 256) out[bh0 * kHeadDim + i] = 0.f;
-    return;
+  // (the tag of chunk t: pad words 2 and 3 of head 0's partial of chunk t)
+  auto tag_at = [&](int t) {
+    return reinterpret_cast<unsigned long long*>(a.ws_part + (bh0 * a.nch + (size_t)t) * kPartFloats + 2);
+  };
+  wait_memory();  // this thread's part of the partial has reached the point of coherence
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(tag_at(c), chunk_tag(gen, c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_memory();
   }
-  combine_group<R>(part + bh0 * nch * kPartFloats, nch, nch_b, out + bh0 * kHeadDim, s_w, s_l);
+  __syncthreads();
+  bool ok = true;
+  for (int t = threadIdx.x; t < nch_b; t += kDenseWaves * 64)
+    ok = ok && __hip_atomic_load(tag_at(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == chunk_tag(gen, t);
+  if (!__syncthreads_and(ok)) return;
+  combine_group<R>(a.ws_part + bh0 * a.nch * kPartFloats, a.nch, nch_b, a.out + bh0 * kHeadDim, s_w, s_lc);
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(genp, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------------------------
@@ -386,17 +423,13 @@ static hipError_t launch_dense_r(const Plan& p, const KvLayout& kv, const uint16
                                  const uint16_t* v, const int32_t* kv_len, float scale, float* out, char* ws,
                                  hipStream_t s) {
   float* ws_part = reinterpret_cast<float*>(ws + p.off_part);
-  AttendArgs aa{q, k, v, kv_len, ws_part, scale * 1.4426950408889634f, p.Hq, p.Hkv, p.cap, p.chunk, p.nch, kv};
+  auto* ws_gen = reinterpret_cast<unsigned long long*>(ws + p.off_count);
+  AttendArgs aa{q, k, v, kv_len, ws_part, ws_gen, out, scale * 1.4426950408889634f, p.Hq, p.Hkv, p.cap, p.chunk,
+                p.nch, kv};
   if (kv.table)
     launch_k(0, dense_attend_kernel<R, true>, dim3(p.nch, p.B * p.Hkv), dim3(kDenseWaves * 64), 0, s, aa);
   else
     launch_k(0, dense_attend_kernel<R, false>, dim3(p.nch, p.B * p.Hkv), dim3(kDenseWaves * 64), 0, s, aa);
-  if (profile_events().n >= 4) {  // timing mode: see adamas_profile_events
-    hipError_t e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return e;
-  }
-  launch_k(1, combine_kernel<R>, dim3(p.B * p.Hkv), dim3(256), 0, s, (const float*)ws_part, kv_len, out, p.Hq,
-           p.Hkv, p.chunk, p.nch);
   return hipGetLastError();
 }
 

@@ -107,8 +107,8 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
     p.splits = 1;
     p.off_part = off;
     off = align256(off + bhq * p.nch * kPartFloats * sizeof(float));
-    p.off_count = off;
-    off = align256(off + bhq * sizeof(uint32_t));
+    p.off_count = off;  // one 64-bit generation word per (b, kv head)
+    off = align256(off + (size_t)B * Hkv * sizeof(uint64_t));
     p.total = off;
     return p;
   }

@@ -4,11 +4,13 @@ The step's launches are captured once and replayed several times, with eager
 work and synchronisations between replays; every replay must reproduce the
 eager result bit for bit (same kernels, same inputs, deterministic).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
 import workloads as W
-from helpers import DeviceCase, from_dev
+from helpers import DeviceCase, assert_out_close, from_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -145,3 +147,55 @@ def test_graph_replay_forced_and_paged():
         assert np.array_equal(from_dev(out), ref_out), "replay %d: out differs" % i
         assert np.array_equal(from_dev(sel), ref_sel), "replay %d: sel_idx differs" % i
 
+
+
+def test_dense_graph_replays_and_stale_workspace():
+    """The dense baseline merges a group's chunk partials in the block that finds
+    all of them tagged with the group's current generation (a word in the
+    workspace, advanced by every call).  Replays of a captured graph, eager calls
+    on the same workspace between them, and workspaces holding arbitrary bytes
+    all give the eager result bit for bit, and that result is the oracle's dense
+    attention."""
+    import torch
+    import sparse_attention_long_fwht_amd as A
+    import oracle
+
+    # (an idle slot: drawn with length 1, then emptied)
+    wl = W.llama(23, cap=6000, budget=8, B=3, Hq=8, Hkv=2, kv_len=np.array([6000, 3111, 1], np.int32))
+    wl = dataclasses.replace(wl, kv_len=np.array([6000, 3111, 0], np.int32))
+    case = DeviceCase(wl, A, torch, encode=False)
+    ref = case.dense()  # (poisoned workspace)
+    assert_out_close(ref, oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale, threads=16))
+    ws = A.alloc_workspace(A.dense_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.cap))
+    gen = torch.Generator(device="cuda")
+    for seed in range(3):  # arbitrary workspace contents, then the same workspace reused
+        gen.manual_seed(seed)
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda", generator=gen))
+        for _ in range(2):
+            out = torch.full((wl.B, wl.Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+            A.dense_decode_attention(case.q, case.k, case.v, case.kv_len, wl.scale, out, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(out), ref)
+    # a captured call replayed, eager calls on the same workspace in between
+    gout = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device="cuda")
+    call = lambda: A.dense_decode_attention(case.q, case.k, case.v, case.kv_len, wl.scale, gout, ws)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in range(5):
+        gout.fill_(float("nan"))
+        if i % 2:
+            eout = torch.empty_like(gout)
+            A.dense_decode_attention(case.q, case.k, case.v, case.kv_len, wl.scale, eout, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(eout), ref), "eager call between replays %d" % i
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(gout), ref), "replay %d" % i
