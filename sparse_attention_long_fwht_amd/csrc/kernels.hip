@@ -187,17 +187,38 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
     if constexpr (kPaged) return kv_row<true>(a.kv, b, g, p) * kHeadDim;
     else return (size_t)p * kHeadDim;
   };
-  // the wave's rows of tile t (rows past nrows read row p0; their scores are masked)
+  // The wave's rows of tile t.  Rows past nrows read the tile's first row, and
+  // a tile past the last one (a request ahead of the end) reads row p0: in
+  // bounds, finite, and on the tile's own page.  Pages of 16 positions or more
+  // hold a whole tile (p0 is a multiple of 16), so the tile takes one
+  // block-table entry, read through the scalar unit: its wait is then not one
+  // on the vector loads still in flight for the tiles ahead.
   auto gather = [&](int t, uint4 (&ka)[4], uint4 (&vv)[4]) {
-    const int ia = 16 * t + col;
-    const uint16_t* kr = Kg + kvoff(p0 + (ia < nrows ? ia : 0)) + 8 * kg;
+    const int r0 = 16 * t < nrows ? 16 * t : 0;
+    const int ia = 16 * t + col < nrows ? 16 * t + col : r0;
+    int iv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) iv[i] = 16 * t + 4 * kg + i < nrows ? 16 * t + 4 * kg + i : r0;
+    size_t ok, ov[4];
+    if (kPaged && a.kv.page_log2 >= 4) {
+      const int mask = (1 << a.kv.page_log2) - 1;
+      const int32_t* entry = a.kv.table + (size_t)b * a.kv.max_pages + ((p0 + r0) >> a.kv.page_log2);
+      const int page = min(max(*reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+                                   reinterpret_cast<uintptr_t>(entry)), 0), a.kv.num_pages - 1);
+      const size_t base = (((size_t)page * a.Hkv + g) << a.kv.page_log2);
+      ok = (base + ((p0 + ia) & mask)) * kHeadDim;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = (base + ((p0 + iv[i]) & mask)) * kHeadDim;
+    } else {
+      ok = kvoff(p0 + ia);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = kvoff(p0 + iv[i]);
+    }
+    const uint16_t* kr = Kg + ok + 8 * kg;
 #pragma unroll
     for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int iv = 16 * t + 4 * kg + i;
-      vv[i] = *reinterpret_cast<const uint4*>(Vg + kvoff(p0 + (iv < nrows ? iv : 0)) + 8 * col);
-    }
+    for (int i = 0; i < 4; ++i) vv[i] = *reinterpret_cast<const uint4*>(Vg + ov[i] + 8 * col);
   };
   float m_run = -INFINITY, l_run = 0.f;  // head col's running max and sum (lanes col < R)
   float o[R][8];
@@ -206,15 +227,9 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
   const int ntiles = (nrows + 15) >> 4;
-  // the wave's tiles t and t + 4 are in registers or in flight while it
-  // requests t + 8 (two tiles ahead)
-  uint4 ka[4], vv[4], k1[4], v1[4];
-  if (w < ntiles) gather(w, ka, vv);
-  if (w + kDenseWaves < ntiles) gather(w + kDenseWaves, k1, v1);
-#pragma unroll 1
-  for (int t = w; t < ntiles; t += kDenseWaves) {
-    uint4 kn[4], vn[4];
-    if (t + 2 * kDenseWaves < ntiles) gather(t + 2 * kDenseWaves, kn, vn);
+  // one tile: scores, online softmax update and P . V from its K rows ka and
+  // V rows vv
+  auto tile = [&](int t, const uint4 (&ka)[4], const uint4 (&vv)[4]) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma_16x16x32_bf16(ka[s], qf[s], acc);
@@ -270,14 +285,46 @@ __device__ __forceinline__ void attend_rows(const AttendArgs& a, int b, int g, i
       pv(std::integral_constant<int, 6>{});
       pv(std::integral_constant<int, 7>{});
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      ka[s] = k1[s];
-      vv[s] = v1[s];
-      k1[s] = kn[s];
-      v1[s] = vn[s];
-    }
+  };
+  // Three register sets take the wave's tiles in turn, so that tiles t + 4
+  // and t + 8 are in flight while tile t is computed.  (Rotating one set into
+  // another instead makes the compiler copy registers, and a copy waits for
+  // its load: the tile ahead would then have to land before the current one
+  // is computed.)  The requests are issued unconditionally -- past the last
+  // tile gather reads row p0 -- and every request is fenced on both sides
+  // (`issue`): an empty asm with a memory clobber keeps the compiler from
+  // sinking the loads down to the tile that uses them, and a scheduling
+  // barrier keeps it from hoisting a later tile's arithmetic above them or
+  // from interleaving two tiles' loads (the wait before a tile counts the
+  // loads issued after it, and one count serves every iteration); neither
+  // emits an instruction or a wait.  The loop takes whole triples and has one
+  // exit: an exit from its middle would reach the loop's head, for the
+  // compiler, with the third set's loads still pending, and the head would
+  // wait for them.  The last one or two tiles follow it.
+  auto issue = [&](int t, uint4 (&ka)[4], uint4 (&vv)[4]) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    gather(t, ka, vv);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int nt = ntiles > w ? (ntiles - w + kDenseWaves - 1) / kDenseWaves : 0;  // the wave's tiles
+  uint4 ka[4], va[4], kb[4], vb[4], kc[4], vc[4];
+  issue(w, ka, va);
+  issue(w + kDenseWaves, kb, vb);
+  int t = w;
+#pragma unroll 1
+  for (int n = nt; n >= 3; n -= 3, t += 3 * kDenseWaves) {
+    issue(t + 2 * kDenseWaves, kc, vc);
+    tile(t, ka, va);
+    issue(t + 3 * kDenseWaves, ka, va);
+    tile(t + kDenseWaves, kb, vb);
+    issue(t + 4 * kDenseWaves, kb, vb);
+    tile(t + 2 * kDenseWaves, kc, vc);
   }
+  const int left = nt % 3;
+  if (left >= 1) tile(t, ka, va);
+  if (left == 2) tile(t + kDenseWaves, kb, vb);
   // the wave's partials: o summed over its four k-groups; m and l of head h
   // sit in lane h
 #pragma unroll

@@ -133,10 +133,14 @@ def test_paged_empty_sequences(env):
     assert_out_close(dense, oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale, threads=8))
 
 
-def test_paged_dense(env):
+@pytest.mark.parametrize("page", [1, 8, 16, 64, 1024])
+def test_paged_dense(env, page):
+    """Pages under 16 positions (a tile's rows on several pages: one table entry
+    per row) and of 16 or more (one entry per tile): the same output as the
+    contiguous cache, bit for bit."""
     A, torch, oracle = env
     wl = ragged(52, 64)
-    case = PagedCase(wl, A, torch, 64, seed=3)
+    case = PagedCase(wl, A, torch, page, seed=3)
     assert_out_close(case.dense(), oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale, threads=8))
     assert np.array_equal(case.dense(), DeviceCase(wl, A, torch).dense())
 
