@@ -84,9 +84,10 @@ struct AttendArgs {
 
 // Merge the per-chunk partials (m, l, o[128]) of R heads into out.  `part`
 // points at head 0's partials; head r's are r * nch chunks further.  Runs with
-// all threads of the block.  Loads are issued in batches with clamped indices
-// so that they overlap.
-template <int R>
+// all kThreads threads of the block.  Each of its two passes over the
+// partials is one round of loads: every load is issued before any is used
+// (indices past the last chunk read the last chunk again).
+template <int R, int kThreads>
 __device__ __forceinline__ void combine_group(const float* __restrict__ part, int nch, int nch_b,
                                               float* __restrict__ out, float (*s_w)[kMaxChunks], float* s_L) {
   // (the partials were written through by other blocks of this kernel: read
@@ -97,17 +98,27 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
   };
   const int tid = threadIdx.x;
   // 1. m and l of every (head, chunk)
-  for (int i = tid; i < R * kMaxChunks; i += 256) {
+  constexpr int kIt = (R * kMaxChunks + kThreads - 1) / kThreads;
+  float mv[kIt], lv[kIt];
+#pragma unroll
+  for (int k = 0; k < kIt; ++k) {
+    const int i = min(tid + k * kThreads, R * kMaxChunks - 1);
     const int r = i / kMaxChunks, c = i - r * kMaxChunks;
-    const float* pc = part + ((size_t)r * nch + (c < nch_b ? c : 0)) * kPartFloats;
-    const float m = ld(pc);
-    const float l = ld(pc + 1);
-    s_w[r][c] = c < nch_b ? m : -INFINITY;
-    if (c < nch_b) s_L[R + r * kMaxChunks + c] = l;  // scratch: l values after the R totals
+    const float* pc = part + ((size_t)r * nch + min(c, nch_b - 1)) * kPartFloats;
+    mv[k] = ld(pc);
+    lv[k] = ld(pc + 1);
+  }
+#pragma unroll
+  for (int k = 0; k < kIt; ++k) {
+    const int i = tid + k * kThreads;
+    if (kIt * kThreads != R * kMaxChunks && i >= R * kMaxChunks) continue;
+    const int r = i / kMaxChunks, c = i - r * kMaxChunks;
+    s_w[r][c] = c < nch_b ? mv[k] : -INFINITY;
+    if (c < nch_b) s_L[R + r * kMaxChunks + c] = lv[k];  // scratch: l values after the R totals
   }
   __syncthreads();
   // 2. per head: M = max m, weights 2^(m - M), L = sum weight * l
-  for (int r = wave_id(); r < R; r += 4) {
+  for (int r = wave_id(); r < R; r += kThreads / 64) {
     const int lane = lane_id();
     const float m0 = s_w[r][lane], m1 = s_w[r][lane + 64];
     const float M = wave_max(fmaxf(m0, m1));
@@ -121,20 +132,37 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
     if (lane == 0) s_L[r] = L;
   }
   __syncthreads();
-  // 3. out[r][d] = sum_c w_c o_c[d] / L, 16 loads in flight per thread
-  for (int i = tid; i < R * kHeadDim; i += 256) {
-    const int r = i / kHeadDim, d = i - r * kHeadDim;
-    const float* pr = part + (size_t)r * nch * kPartFloats + 4 + d;
-    float O = 0.f;
-    for (int c0 = 0; c0 < nch_b; c0 += 16) {
-      float v[16];
+  // 3. out[r][d] = sum_c w_c o_c[d] / L over the thread's kPer outputs, with
+  // the o values of kBatch chunks of each in flight at once (64 loads per
+  // thread: one round up to kBatch chunks)
+  constexpr int kPer = (R * kHeadDim + kThreads - 1) / kThreads;
+  constexpr int kBatch = 64 / kPer;
+  const float* pr[kPer];
+  float O[kPer];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = ld(pr + (size_t)min(c0 + u, nch_b - 1) * kPartFloats);
+  for (int k = 0; k < kPer; ++k) {
+    const int i = min(tid + k * kThreads, R * kHeadDim - 1);
+    pr[k] = part + (size_t)(i / kHeadDim) * nch * kPartFloats + 4 + (i % kHeadDim);
+    O[k] = 0.f;
+  }
+  for (int c0 = 0; c0 < nch_b; c0 += kBatch) {
+    float v[kPer][kBatch];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (c0 + u < nch_b) O = __builtin_fmaf(s_w[r][c0 + u], v[u], O);
+    for (int k = 0; k < kPer; ++k)
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[k][u] = ld(pr[k] + (size_t)min(c0 + u, nch_b - 1) * kPartFloats);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int r = min(tid + k * kThreads, R * kHeadDim - 1) / kHeadDim;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (c0 + u < nch_b) O[k] = __builtin_fmaf(s_w[r][c0 + u], v[k][u], O[k]);
     }
-    out[(size_t)r * kHeadDim + d] = O / s_L[r];
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = tid + k * kThreads;
+    if (R * kHeadDim % kThreads == 0 || i < R * kHeadDim) out[i] = O[k] / s_L[i / kHeadDim];
   }
 }
 
@@ -432,7 +460,8 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(AttendAr
   for (int t = threadIdx.x; t < nch_b; t += kDenseWaves * 64)
     ok = ok && __hip_atomic_load(tag_at(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == chunk_tag(gen, t);
   if (!__syncthreads_and(ok)) return;
-  combine_group<R>(a.ws_part + bh0 * a.nch * kPartFloats, a.nch, nch_b, a.out + bh0 * kHeadDim, s_w, s_lc);
+  combine_group<R, kDenseWaves * 64>(a.ws_part + bh0 * a.nch * kPartFloats, a.nch, nch_b, a.out + bh0 * kHeadDim,
+                                     s_w, s_lc);
   if (threadIdx.x == 0) __hip_atomic_fetch_add(genp, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
