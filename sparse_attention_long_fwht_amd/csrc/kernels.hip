@@ -89,7 +89,8 @@ struct AttendArgs {
 // (indices past the last chunk read the last chunk again).
 template <int R, int kThreads>
 __device__ __forceinline__ void combine_group(const float* __restrict__ part, int nch, int nch_b,
-                                              float* __restrict__ out, float (*s_w)[kMaxChunks], float* s_L) {
+                                              float* __restrict__ out, float (*s_w)[kMaxChunks], float* s_L,
+                                              unsigned long long* genp, unsigned long long gen) {
   // (the partials were written through by other blocks of this kernel: read
   // them coherently)
   auto ld = [](const float* p) {
@@ -97,6 +98,18 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
                                              __HIP_MEMORY_SCOPE_AGENT));
   };
   const int tid = threadIdx.x;
+  // 0. the election: of the blocks that found the group complete, the one
+  // whose compare-and-swap advances the generation merges (no retry: a failed
+  // swap means another block won).  Issued before the loads of step 1, its
+  // round trip overlaps theirs.
+  __shared__ int s_won;
+  unsigned long long seen = ~gen;
+  if (tid == 0) {
+    unsigned long long expected = gen;
+    __hip_atomic_compare_exchange_strong(genp, &expected, gen + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    seen = expected;  // the word's value before the swap (gen iff it succeeded)
+  }
   // 1. m and l of every (head, chunk)
   constexpr int kIt = (R * kMaxChunks + kThreads - 1) / kThreads;
   float mv[kIt], lv[kIt];
@@ -108,6 +121,10 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
     mv[k] = ld(pc);
     lv[k] = ld(pc + 1);
   }
+  // (the empty asm takes `seen` as an operand after the loads above are
+  // issued, so the wait for the swap's result is not placed before them)
+  asm volatile("" : "+v"(seen) : : "memory");
+  if (tid == 0) s_won = seen == gen;
 #pragma unroll
   for (int k = 0; k < kIt; ++k) {
     const int i = tid + k * kThreads;
@@ -117,6 +134,7 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
     if (c < nch_b) s_L[R + r * kMaxChunks + c] = lv[k];  // scratch: l values after the R totals
   }
   __syncthreads();
+  if (!s_won) return;
   // 2. per head: M = max m, weights 2^(m - M), L = sum weight * l
   for (int r = wave_id(); r < R; r += kThreads / 64) {
     const int lane = lane_id();
@@ -416,13 +434,15 @@ __device__ __forceinline__ unsigned long long chunk_tag(unsigned long long gen, 
 //   - every block reads the group's generation word when it starts;
 //   - it writes its partial through to the point of coherence, then a tag of
 //     (generation, chunk) in the pad words of its head-0 partial;
-//   - it then reads every chunk's tag; if all match, it merges and advances
-//     the generation.
-// Of two blocks finishing together at least one sees all tags (each reads only
-// after its own tag has reached the point of coherence); if both do, both
-// write the same out (the merge order is fixed).  The next call sees the new
-// generation, so tags left by this one never match; arbitrary workspace
-// content matches no hash, so the workspace needs no initialisation.
+//   - it then reads every chunk's tag; if all match, the group is complete
+//     (a tag is written only after its partial), and the block tries to
+//     advance the generation with a compare-and-swap: the one block that
+//     succeeds merges.
+// Of blocks finishing together at least one sees all tags (each reads only
+// after its own tag has reached the point of coherence), so exactly one
+// merges.  The next call sees the new generation, so tags left by this one
+// never match; arbitrary workspace content matches no hash, so the workspace
+// needs no initialisation.
 template <int R, bool kPaged>
 __global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(AttendArgs a) {
   __shared__ float s_w[R][kMaxChunks];
@@ -461,8 +481,7 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(AttendAr
     ok = ok && __hip_atomic_load(tag_at(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == chunk_tag(gen, t);
   if (!__syncthreads_and(ok)) return;
   combine_group<R, kDenseWaves * 64>(a.ws_part + bh0 * a.nch * kPartFloats, a.nch, nch_b, a.out + bh0 * kHeadDim,
-                                     s_w, s_lc);
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(genp, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                     s_w, s_lc, genp, gen);
 }
 
 // --------------------------------------------------------------------------
