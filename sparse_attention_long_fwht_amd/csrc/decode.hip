@@ -126,6 +126,15 @@ __device__ __forceinline__ void encode_wave(uint32_t qlo_bits, uint32_t qhi_bits
 // every selected position.
 
 constexpr int kScanThreads = 512;  // one key per thread per pass
+// popcount(x) + acc in one instruction.  (Left to itself the compiler sums a
+// run of popcounts as a tree of three-input adds, one more instruction per
+// three terms; the distance is a run of eight.)
+__device__ __forceinline__ uint32_t popc_acc(uint32_t x, uint32_t acc) {
+  uint32_t r;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(acc));
+  return r;
+}
+
 constexpr int kHistBins = 7 * 64;  // bins as scanned by one wave: 7 per lane (up to kMaxKey + 1 used)
 // the last bin takes the keys a forced-position scan does not rank (sinks and
 // window): counted like the others so that no atomic sits behind a branch, then
@@ -318,8 +327,8 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
           for (int w = 0; w < 4; ++w) {
             const uint32_t L = lo[w] ^ ql[r][w];
             const uint32_t M = (hi[w] ^ qh[r][w]) & ~(L & x[w]);
-            cl += __builtin_popcount(L);
-            cm += __builtin_popcount(M);
+            cl = w == 0 ? (uint32_t)__builtin_popcount(L) : popc_acc(L, cl);
+            cm = w == 0 ? (uint32_t)__builtin_popcount(M) : popc_acc(M, cm);
           }
           const uint32_t d = cl + 2u * cm;
           const uint32_t key = kForced ? (!ranked ? (uint32_t)kSpareBin : special ? 0u : d + 1u) : d;
