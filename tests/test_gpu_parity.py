@@ -495,6 +495,17 @@ def test_dense_group_sizes(env, Hq, Hkv):
     assert_out_close(case.dense(), oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale))
 
 
+@pytest.mark.parametrize("Hq", [8, 4])
+def test_dense_many_chunks(env, Hq):
+    """One kv head at 128K positions: 128 chunks per group (the most a group
+    has), so the merge runs several batches of chunks and its second half of
+    lanes; the second sequence's 69 chunks end mid-chunk."""
+    A, torch, oracle = env
+    wl = W.llama(42, cap=131072, budget=1, B=2, Hq=Hq, Hkv=1, kv_len=np.array([131072, 70001], np.int32))
+    case = DeviceCase(wl, A, torch, encode=False)
+    assert_out_close(case.dense(), oracle.dense_attention(wl.q, wl.k, wl.v, wl.kv_len, wl.scale, threads=16))
+
+
 def test_encode_keys_arbitrary_ranges(env):
     """Ranges [start[b], end[b]) anywhere in the cache (empty ones included):
     exactly those rows are written, equal to the oracle's codes; the rest of
