@@ -163,6 +163,10 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
     pr[k] = part + (size_t)(i / kHeadDim) * nch * kPartFloats + 4 + (i % kHeadDim);
     O[k] = 0.f;
   }
+  // The weights of chunks past nch_b are 0 (step 2) and their clamped loads
+  // read a finite partial, so every term is added unconditionally; the
+  // weights come from LDS 16 bytes at a time.  (Guarding each term and
+  // reading its weight alone made the terms a chain of LDS round trips.)
   for (int c0 = 0; c0 < nch_b; c0 += kBatch) {
     float v[kPer][kBatch];
 #pragma unroll
@@ -172,9 +176,15 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int r = min(tid + k * kThreads, R * kHeadDim - 1) / kHeadDim;
+      const float4* wr = reinterpret_cast<const float4*>(&s_w[r][c0]);
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (c0 + u < nch_b) O[k] = __builtin_fmaf(s_w[r][c0 + u], v[k][u], O[k]);
+      for (int u4 = 0; u4 < kBatch / 4; ++u4) {
+        const float4 wq = wr[u4];
+        O[k] = __builtin_fmaf(wq.x, v[k][4 * u4], O[k]);
+        O[k] = __builtin_fmaf(wq.y, v[k][4 * u4 + 1], O[k]);
+        O[k] = __builtin_fmaf(wq.z, v[k][4 * u4 + 2], O[k]);
+        O[k] = __builtin_fmaf(wq.w, v[k][4 * u4 + 3], O[k]);
+      }
     }
   }
 #pragma unroll
@@ -445,7 +455,7 @@ __device__ __forceinline__ unsigned long long chunk_tag(unsigned long long gen, 
 // needs no initialisation.
 template <int R, bool kPaged>
 __global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(AttendArgs a) {
-  __shared__ float s_w[R][kMaxChunks];
+  __shared__ __attribute__((aligned(16))) float s_w[R][kMaxChunks];  // (rows read 16 bytes at a time)
   __shared__ float s_lc[R * (kMaxChunks + 1)];
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv;
