@@ -84,8 +84,8 @@ struct AttendArgs {
 
 // Merge the per-chunk partials (m, l, o[128]) of R heads into out.  `part`
 // points at head 0's partials; head r's are r * nch chunks further.  Runs with
-// all kThreads threads of the block.  Each of its two passes over the
-// partials is one round of loads: every load is issued before any is used
+// all kThreads threads of the block.  Up to kBatch chunks its reads of the
+// partials are one round of loads: every load is issued before any is used
 // (indices past the last chunk read the last chunk again).
 template <int R, int kThreads>
 __device__ __forceinline__ void combine_group(const float* __restrict__ part, int nch, int nch_b,
@@ -121,6 +121,24 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
     mv[k] = ld(pc);
     lv[k] = ld(pc + 1);
   }
+  // The o values of the first kBatch chunks (step 3) are requested now too:
+  // their loads need no weight, so they share this round trip.
+  constexpr int kPer = (R * kHeadDim + kThreads - 1) / kThreads;
+  constexpr int kBatch = 64 / kPer;
+  const float* pr[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = min(tid + k * kThreads, R * kHeadDim - 1);
+    pr[k] = part + (size_t)(i / kHeadDim) * nch * kPartFloats + 4 + (i % kHeadDim);
+  }
+  float v[kPer][kBatch];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[k][u] = ld(pr[k] + (size_t)min(c0 + u, nch_b - 1) * kPartFloats);
+  };
+  load_batch(0);
   // (the empty asm takes `seen` as an operand after the loads above are
   // issued, so the wait for the swap's result is not placed before them)
   asm volatile("" : "+v"(seen) : : "memory");
@@ -150,29 +168,18 @@ __device__ __forceinline__ void combine_group(const float* __restrict__ part, in
     if (lane == 0) s_L[r] = L;
   }
   __syncthreads();
-  // 3. out[r][d] = sum_c w_c o_c[d] / L over the thread's kPer outputs, with
-  // the o values of kBatch chunks of each in flight at once (64 loads per
-  // thread: one round up to kBatch chunks)
-  constexpr int kPer = (R * kHeadDim + kThreads - 1) / kThreads;
-  constexpr int kBatch = 64 / kPer;
-  const float* pr[kPer];
+  // 3. out[r][d] = sum_c w_c o_c[d] / L over the thread's kPer outputs, the
+  // o values of kBatch chunks of each at a time (64 loads per thread; the
+  // first batch was requested with step 1).  The weights of chunks past
+  // nch_b are 0 (step 2) and their clamped loads read a finite partial, so
+  // every term is added unconditionally; the weights come from LDS 16 bytes
+  // at a time.  (Guarding each term and reading its weight alone made the
+  // terms a chain of LDS round trips.)
   float O[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = min(tid + k * kThreads, R * kHeadDim - 1);
-    pr[k] = part + (size_t)(i / kHeadDim) * nch * kPartFloats + 4 + (i % kHeadDim);
-    O[k] = 0.f;
-  }
-  // The weights of chunks past nch_b are 0 (step 2) and their clamped loads
-  // read a finite partial, so every term is added unconditionally; the
-  // weights come from LDS 16 bytes at a time.  (Guarding each term and
-  // reading its weight alone made the terms a chain of LDS round trips.)
+  for (int k = 0; k < kPer; ++k) O[k] = 0.f;
   for (int c0 = 0; c0 < nch_b; c0 += kBatch) {
-    float v[kPer][kBatch];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) v[k][u] = ld(pr[k] + (size_t)min(c0 + u, nch_b - 1) * kPartFloats);
+    if (c0 > 0) load_batch(c0);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int r = min(tid + k * kThreads, R * kHeadDim - 1) / kHeadDim;
