@@ -1021,20 +1021,11 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   __syncthreads();
   if (!s_last) return;
   if (tid < kHeadDim) {
+    // (m, l and o of the first eight splits are requested in one round; with
+    // more splits, the max over the rest takes one more round first)
     const float* p0 = a.part + (size_t)bh * a.splits * kPartFloats;
-    float M = -INFINITY;
-#pragma unroll 1
-    for (int s0 = 0; s0 < a.splits; s0 += 8) {
-      float mv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) mv[u] = load_coherent(p0 + (size_t)min(s0 + u, a.splits - 1) * kPartFloats);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
-    }
-    float L = 0.f, O = 0.f;
-#pragma unroll 1
-    for (int s0 = 0; s0 < a.splits; s0 += 8) {
-      float mv[8], lv[8], ov[8];
+    float mv[8], lv[8], ov[8];
+    auto load_batch = [&](int s0) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float* ps = p0 + (size_t)min(s0 + u, a.splits - 1) * kPartFloats;
@@ -1042,6 +1033,23 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
         lv[u] = load_coherent(ps + 1);
         ov[u] = load_coherent(ps + 4 + tid);
       }
+    };
+    load_batch(0);
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
+#pragma unroll 1
+    for (int s0 = 8; s0 < a.splits; s0 += 8) {
+      float mm[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mm[u] = load_coherent(p0 + (size_t)min(s0 + u, a.splits - 1) * kPartFloats);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) M = fmaxf(M, mm[u]);
+    }
+    float L = 0.f, O = 0.f;
+#pragma unroll 1
+    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+      if (s0 > 0) load_batch(s0);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (s0 + u < a.splits && mv[u] != -INFINITY) {
