@@ -764,10 +764,14 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
       c_lo = min(c_lo, 64 * gi + __builtin_ctzll(mb));
       c_hi = max(c_hi, 64 * gi + 63 - __builtin_clzll(mb));
     }
+    // slots [0, lt) are all kept; the ties at T, slots [lt, m), are kept in
+    // position order across the chunks, so a chunk keeps all, some (one chunk
+    // per head) or none of them -- with none kept they are not prefetched
+    const int pf_n = kept > c.y ? (int)c.x : (int)c.y;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = wave + kSAWaves * jj;
-      if (mine && j < (int)c.x && j < a.pre_slots) {
+      if (mine && j < pf_n && j < a.pre_slots) {
         const int lp = min((int)s_pre[(size_t)cc * a.pre_slots + j], min(a.chunk, len - cc * a.chunk) - 1);
         const size_t row = kvoff(cc * a.chunk + lp);
         pf[gi][jj][0] = *reinterpret_cast<const uint32_t*>(Kg + row);
