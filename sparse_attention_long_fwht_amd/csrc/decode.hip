@@ -141,7 +141,8 @@ constexpr int kHistBins = 7 * 64;  // bins as scanned by one wave: 7 per lane (u
 // left out of the records and the scatter
 constexpr int kSpareBin = kHistBins - 1;
 static_assert(kSpareBin > kMaxKey, "every selection key has a bin, and the spare bin is none of them");
-constexpr int kScanPasses = kScanMaxChunk / kScanThreads;
+constexpr int kScanPasses = kScanMaxChunk / kScanThreads;  // 16
+constexpr int kSmallPasses = 8;                             // chunks up to 4096 positions
 
 struct ScanArgs {
   const uint16_t* q;
@@ -184,7 +185,7 @@ __device__ __forceinline__ void scan_block_of(int blk, int grid, int nch, int& b
 // pays nothing for them).  kCoherent: the records, sorted prefixes and the
 // split counters are written through, for readers in the same kernel (the
 // single-launch step); otherwise the kernel boundary hands them over.
-template <int R, bool kForced, bool kPaged, bool kCoherent>
+template <int R, bool kForced, bool kPaged, bool kCoherent, int kPasses>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
@@ -273,9 +274,9 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
 
   // special tokens (kForced with a mask): the caller's bitmap words of every
   // pass, requested before the first wait on the key codes
-  uint32_t fw[kScanPasses];
+  uint32_t fw[kPasses];
 #pragma unroll
-  for (int pass = 0; pass < kScanPasses; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     fw[pass] = 0u;
     if (kForced && a.fmask && p0 + pass * kScanThreads < p1)
       fw[pass] = a.fmask[(size_t)b * a.fmask_words + ((min(p0 + pass * kScanThreads + tid, p1 - 1)) >> 5)];
@@ -285,13 +286,13 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   // distance + 1 for the other ranked keys and kSpareBin for the unranked);
   // each (key, head) takes the next rank in its key's bin.  The next pass's
   // codes are loaded while this pass computes.
-  uint32_t dr[kScanPasses][R];  // (key << 16) | rank inside the bin
+  uint32_t dr[kPasses][R];  // (key << 16) | rank inside the bin
 #pragma unroll
-  for (int pass = 0; pass < kScanPasses; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int base = p0 + pass * kScanThreads;
     if (base < p1) {
       uint4 nlo = klo, nhi = khi;
-      if (pass + 1 < kScanPasses && base + kScanThreads < p1) {
+      if (pass + 1 < kPasses && base + kScanThreads < p1) {
         const int pn = min(base + kScanThreads + tid, p1 - 1);
         const uint4* cn = code_src(pn);
         nlo = cn[0];
@@ -345,7 +346,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   // debug distances of the plain step: the key is the distance
   if (!kForced && a.dist_out) {
 #pragma unroll
-    for (int pass = 0; pass < kScanPasses; ++pass) {
+    for (int pass = 0; pass < kPasses; ++pass) {
       const int pp = p0 + pass * kScanThreads + tid;
       if (p0 + pass * kScanThreads < p1 && pp < p1) {
 #pragma unroll
@@ -406,7 +407,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   // head's kept slots are stored too (slots stay below the chunk length);
   // nothing reads them.
 #pragma unroll
-  for (int pass = 0; pass < kScanPasses; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int pp = p0 + pass * kScanThreads + tid;
     if (p0 + pass * kScanThreads < p1 && pp < p1 && (!kForced || (pp >= m0 && pp < m1))) {
 #pragma unroll
@@ -414,7 +415,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
     }
   }
 #pragma unroll
-  for (int pass = 0; pass < kScanPasses; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int pp = p0 + pass * kScanThreads + tid;
     if (p0 + pass * kScanThreads < p1 && pp < p1 && (!kForced || (pp >= m0 && pp < m1))) {
 #pragma unroll
@@ -441,11 +442,15 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   }
 }
 
-template <int R, bool kForced, bool kPaged>
+// kPasses: passes of kScanThreads keys per block at most (the chunk divided by
+// kScanThreads, rounded up to 8 or 16: the rank array is kPasses x R
+// registers and the pass loop is unrolled, so chunks up to 4096 positions get
+// the 8-pass kernel)
+template <int R, bool kForced, bool kPaged, int kPasses>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   int bg, c;
   scan_block_of((int)blockIdx.x, (int)gridDim.x, a.nch, bg, c);
-  scan_chunk<R, kForced, kPaged, false>(a, bg, c);
+  scan_chunk<R, kForced, kPaged, false, kPasses>(a, bg, c);
 }
 
 // --------------------------------------------------------------------------
@@ -1115,7 +1120,7 @@ __global__ __launch_bounds__(kScanThreads) void fused_decode_kernel(ScanArgs sa,
   __shared__ uint32_t s_gen;
   __shared__ int s_ok;
   if (threadIdx.x == 0) s_gen = __hip_atomic_load(&fs.gen[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  scan_chunk<R, kForced, kPaged, true>(sa, bg, c);
+  scan_chunk<R, kForced, kPaged, true, kSmallPasses>(sa, bg, c);  // (the single launch takes chunks up to 4096)
   wait_memory();    // this thread's written-through stores have completed
   __syncthreads();  // ... and every thread's (s_gen is visible too)
   const uint32_t gen = s_gen;
@@ -1170,16 +1175,22 @@ static void launch_k(int i, Kernel kernel, dim3 grid, dim3 block, uint32_t shmem
     hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
 }
 
-template <int R, bool kForced, bool kPaged>
-static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
+template <int R, bool kForced, bool kPaged, int kPasses>
+static hipError_t launch_scan_passes(const Plan& p, const ScanArgs& sa, hipStream_t s) {
   const uint32_t shmem = (uint32_t)(R * p.chunk * sizeof(uint16_t));  // sorted slots, staged
   if (shmem > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<R, kForced, kPaged>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<R, kForced, kPaged, kPasses>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  launch_k(0, scan_kernel<R, kForced, kPaged>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), shmem, s, sa);
+  launch_k(0, scan_kernel<R, kForced, kPaged, kPasses>, dim3(p.nch * p.B * p.Hkv), dim3(kScanThreads), shmem, s, sa);
   return hipSuccess;
+}
+
+template <int R, bool kForced, bool kPaged>
+static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
+  if (p.chunk > kSmallPasses * kScanThreads) return launch_scan_passes<R, kForced, kPaged, kScanPasses>(p, sa, s);
+  return launch_scan_passes<R, kForced, kPaged, kSmallPasses>(p, sa, s);
 }
 
 template <int R>

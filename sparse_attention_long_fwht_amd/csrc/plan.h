@@ -15,11 +15,11 @@ constexpr int kMaxDist = 384;     // distances 0..384 (128 coordinates x largest
 constexpr int kMaxKey = kMaxDist + 1;
 // Sparse path: chunks of the scan (one block per (b, kv head, chunk)).
 constexpr int kScanMinChunk = 512;   // = threads of the scan block: one key per thread per pass
-constexpr int kScanMaxChunk = 4096;  // at most eight passes per block
+constexpr int kScanMaxChunk = 8192;  // at most sixteen passes per block
 constexpr int kScanTargetChunks = 64;  // chunks per head wanted at most (see make_plan)
 constexpr int64_t kScanBlocks = 256;   // scan blocks wanted at most: one per compute unit
 constexpr int64_t kMaxCapacity = 524288;  // positions per (b, kv head)
-constexpr int kSelMaxChunks = 128;  // chunks per (b, kv head) at most: kMaxCapacity / kScanMaxChunk
+constexpr int kSelMaxChunks = 128;  // chunks per (b, kv head) at most: kMaxCapacity / 4096
 // u16 per (head, chunk) record: the cumulative count of positions at each
 // selection key 0..kMaxKey, padded (the padding words repeat the last count)
 constexpr int kRecStride = 392;
@@ -79,6 +79,8 @@ inline int choose_rows_per_split(int budget, int heads) {
   return (r + 127) / 128 * 128;
 }
 
+inline int R_of(int Hq, int Hkv) { return Hkv > 0 ? Hq / Hkv : 1; }
+
 inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   Plan p{};
   p.supported = true;
@@ -117,9 +119,26 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   // larger chunks amortize each block's query encode and record pass
   p.chunk = kScanMinChunk;
   auto scan_blocks = [&](int ch) { return (int64_t)B * Hkv * ((cap + ch - 1) / ch); };
-  while (p.chunk < kScanMaxChunk &&
+  while (p.chunk < kScanMaxChunk / 2 &&
          ((int64_t)p.chunk * kScanTargetChunks < cap || scan_blocks(p.chunk) > kScanBlocks))
     p.chunk <<= 1;
+  // Chunks of 8192 (the sixteen-pass scan) only where they need fewer rounds of
+  // resident blocks than chunks of 4096: a round's blocks run their phases in
+  // step, so a second, partial round pays every phase's latency again.  Blocks
+  // per compute unit: by LDS (160 KB: the R histograms of 448 bins, records,
+  // query codes and limits, plus R x chunk sorted slots), at most 4 of 512
+  // threads.
+  if (p.chunk == kScanMaxChunk / 2) {
+    auto rounds = [&](int ch) {
+      const int64_t lds = (int64_t)R_of(Hq, Hkv) * (448 * 4 + kRecStride * 2 + 36) + 32 +
+                          (int64_t)R_of(Hq, Hkv) * ch * 2;
+      int64_t per_cu = 163840 / lds;
+      per_cu = per_cu < 1 ? 1 : (per_cu > 4 ? 4 : per_cu);
+      const int64_t slots = 256 * per_cu;
+      return (scan_blocks(ch) + slots - 1) / slots;
+    };
+    if (rounds(kScanMaxChunk) < rounds(kScanMaxChunk / 2)) p.chunk = kScanMaxChunk;
+  }
   p.nch = (cap + p.chunk - 1) / p.chunk;
   if (p.nch > kSelMaxChunks) p.supported = false;  // (not reached for cap <= kMaxCapacity)
   // about twice the mean number of selected positions per chunk: a power of
@@ -140,7 +159,8 @@ inline Plan make_plan(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
   if (p.lds_select > kSelectDynLdsMax) p.supported = false;
   // single launch: few enough groups and chunks for the sync words, and a
   // block of the group for every (query head, split)
-  p.fused = (int64_t)B * Hkv <= kFusedMaxGroups && p.nch <= kFusedMaxChunks && p.R * p.splits <= p.nch;
+  p.fused = (int64_t)B * Hkv <= kFusedMaxGroups && p.nch <= kFusedMaxChunks && p.R * p.splits <= p.nch &&
+            p.chunk <= kScanMaxChunk / 2;  // (the single launch's scan is the eight-pass one)
   p.off_sync = off;
   off += kSyncBytes;
   p.off_sorted = off;

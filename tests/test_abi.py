@@ -385,8 +385,8 @@ def test_workspace_for_any_int32_budget(A):
         assert 0 < at_cap < (1 << 32)
         for budget in (cap + 1, 1 << 20, 1 << 30, 2 ** 31 - 1):
             assert A.decode_workspace_size(B, Hq, Hkv, cap, budget) == at_cap, (cap, budget)
-    assert A.decode_workspace_size(1, 32, 8, 524288, 229376) > 0
-    for budget in (229377, 1 << 30, 2 ** 31 - 1):
+    assert A.decode_workspace_size(1, 32, 8, 524288, 245760) > 0
+    for budget in (245761, 1 << 30, 2 ** 31 - 1):
         assert A.decode_workspace_size(1, 32, 8, 524288, budget) == 0
 
 

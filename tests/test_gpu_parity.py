@@ -156,7 +156,7 @@ def max_chunk_entries(wl, dist, budget):
     """Largest number of positions at or below the threshold distance T in one
     chunk, over all heads (the select kernel sorts up to 64 of them in
     registers, more through a bitmap)."""
-    chunk, _ = chunking(wl.cap, wl.B * wl.Hkv)
+    chunk, _ = chunking(wl.cap, wl.B * wl.Hkv, wl.Hq // wl.Hkv)
     worst = 0
     for b in range(wl.B):
         L = int(wl.kv_len[b])
@@ -169,13 +169,22 @@ def max_chunk_entries(wl, dist, budget):
     return worst
 
 
-def chunking(cap, groups=1):
+def chunking(cap, groups=1, R=4):
     """The library's chunk size: 512 positions, doubled up to 4096 until a head
     has at most 64 chunks and the scan has at most 256 blocks, one per (b, kv
-    head, chunk)."""
+    head, chunk); then 8192 if that takes fewer rounds of resident scan blocks
+    (blocks per compute unit by LDS, at most 4)."""
     chunk = 512
-    while chunk < 4096 and (chunk * 64 < cap or groups * -(-cap // chunk) > 256):
+    blocks = lambda ch: groups * -(-cap // ch)
+    while chunk < 4096 and (chunk * 64 < cap or blocks(chunk) > 256):
         chunk *= 2
+    if chunk == 4096:
+        def rounds(ch):
+            lds = R * (448 * 4 + 392 * 2 + 36) + 32 + R * ch * 2
+            slots = 256 * max(1, min(4, 163840 // lds))
+            return -(-blocks(ch) // slots)
+        if rounds(8192) < rounds(4096):
+            chunk = 8192
     return chunk, None
 
 
@@ -248,6 +257,17 @@ def test_decode_budget_twice_capacity(env):
         L = int(wl.kv_len[b])
         assert np.array_equal(sel[b, :, :L], np.broadcast_to(np.arange(L, dtype=np.int32), (wl.Hq, L)))
         assert np.all(sel[b, :, L:] == -1)
+
+
+def test_decode_sixteen_pass_chunks(env):
+    """Chunks of 8192 positions (the sixteen-pass scan: three sequences of one
+    kv head with eight query heads need two rounds of resident scan blocks at
+    4096 and one at 8192), ragged lengths, one ending inside a pass."""
+    A, torch, oracle = env
+    wl = W.llama(54, cap=524288, budget=512, B=3, Hq=8, Hkv=1,
+                 kv_len=np.array([524288, 300001, 9000], np.int32))
+    assert chunking(wl.cap, wl.B * wl.Hkv, 8)[0] == 8192
+    check_decode(DeviceCase(wl, A, torch), oracle, threads=16)
 
 
 @pytest.mark.parametrize("budget", [300, 2500])
@@ -451,12 +471,13 @@ def test_decode_long512k(env):
 
 
 def test_decode_long512k_largest_budget(env):
-    """The largest supported budget at the largest capacity (229376 of 524288
-    positions: 64 splits of 3584 rows per head); every head checked."""
+    """The largest supported budget at the largest capacity (245760 of 524288
+    positions: 64 splits of 3840 rows per head, chunks of 8192); every head
+    checked."""
     A, torch, oracle = env
-    assert A.decode_workspace_size(1, 32, 8, 524288, 229376) > 0
-    assert A.decode_workspace_size(1, 32, 8, 524288, 229377) == 0
-    wl = W.llama(4, cap=524288, budget=229376, name="long512k_k224k")
+    assert A.decode_workspace_size(1, 32, 8, 524288, 245760) > 0
+    assert A.decode_workspace_size(1, 32, 8, 524288, 245761) == 0
+    wl = W.llama(4, cap=524288, budget=245760, name="long512k_k240k")
     case = DeviceCase(wl, A, torch)
     out, sel, _, _ = case.decode(want_debug=False)
     codes_ref = oracle.encode_keys(wl.k, wl.kv_len, threads=16)
