@@ -159,6 +159,8 @@ struct ScanArgs {
   int sink, recent;    // always-kept sinks and recent window (not ranked)
   int fmask_words;     // (sink, recent, fmask: scan_kernel<R, true> only)
   KvLayout kv;         // where K rows and codes of a position live (scan_kernel<R, F, true>: paged)
+  uint32_t nch_m, hkv_m;  // div_magic(nch), div_magic(Hkv)
+  int xcd_map;         // the number of groups (b, kv head) is a multiple of kXcds
 };
 
 // Blocks are dealt to the eight XCDs round-robin by linear block index.  When
@@ -167,16 +169,17 @@ struct ScanArgs {
 constexpr int kXcds = 8;
 
 // The (b, kv head) group and the chunk of scan block `blk` of a grid of
-// G * nch blocks.
-__device__ __forceinline__ void scan_block_of(int blk, int grid, int nch, int& bg, int& c) {
-  const int G = grid / nch;
-  if (G % kXcds == 0) {
-    const int xcd = blk % kXcds, s = blk / kXcds;
-    bg = xcd + kXcds * (s / nch);
-    c = s % nch;
+// G * nch blocks (divisions by nch through its magic number: the block's first
+// loads wait for this).
+__device__ __forceinline__ void scan_block_of(int blk, const ScanArgs& a, int& bg, int& c) {
+  if (a.xcd_map) {
+    const int xcd = blk & (kXcds - 1), s = (int)((uint32_t)blk / kXcds);
+    const int z = div_by(s, a.nch, a.nch_m);
+    bg = xcd + kXcds * z;
+    c = s - z * a.nch;
   } else {
-    bg = blk / nch;
-    c = blk % nch;
+    bg = div_by(blk, a.nch, a.nch_m);
+    c = blk - bg * a.nch;
   }
 }
 
@@ -187,7 +190,7 @@ __device__ __forceinline__ void scan_block_of(int blk, int grid, int nch, int& b
 // single-launch step); otherwise the kernel boundary hands them over.
 template <int R, bool kForced, bool kPaged, bool kCoherent, int kPasses>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
-  const int b = bg / a.Hkv;
+  const int b = div_by(bg, a.Hkv, a.hkv_m);
   const int g = bg - b * a.Hkv;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -217,7 +220,9 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   __shared__ uint32_t s_limit[R];                    // sorted slots kept per head
   __shared__ __attribute__((aligned(16))) uint16_t s_rec[R][kRecStride];  // records, staged
   extern __shared__ __attribute__((aligned(16))) uint16_t s_sorted[];       // [R][chunk] sorted slots, staged
-  for (int i = tid; i < R * kHistBins; i += kScanThreads) (&s_hist[0][0])[i] = 0u;
+#pragma unroll
+  for (int i0 = 0; i0 < R * kHistBins; i0 += kScanThreads)
+    if (i0 + tid < R * kHistBins) (&s_hist[0][0])[i0 + tid] = 0u;
   // Vectors to encode: the group's R queries, plus -- in the block holding
   // position len-1 when appending -- that key.  Wave w takes vectors w, w+8.
   const bool app_here = a.append && (len - 1) >= p0 && (len - 1) < p0 + a.chunk;
@@ -233,10 +238,12 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
     }
     uint32_t lo[4], hi[4];
     encode_wave(xlo, xhi, lo, hi);
-    if (lane < 8) {
-      uint32_t w = 0;  // word lane & 3 of the low (lanes 0-3) or high plane; constant indices keep lo/hi in registers
+    // lane j < 8 takes word j of the code: the low plane's four words, then
+    // the high plane's (wave-uniform values written into single lanes)
+    uint32_t w = lo[0];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w = (lane & 3) == j ? (lane < 4 ? lo[j] : hi[j]) : w;
+    for (int j = 1; j < 8; ++j) w = lane == j ? (j < 4 ? lo[j & 3] : hi[j & 3]) : w;
+    if (lane < 8) {
       s_code[vi][lane] = w;
       if (vi < R) {
         if (c == 0 && a.q_codes)
@@ -253,7 +260,14 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
     else *cnt = 0u;
   }
   __syncthreads();
-  if (p0 >= len) return;
+  const size_t hc0 = (size_t)(b * a.Hq + g * R) * a.nch + c;  // (head g*R, chunk c)
+  if (p0 >= len) {
+    // a chunk past the sequence: every count of its records is 0 (the select
+    // kernel sums a head's first records without a bound on the chunk)
+    if (wave < R && lane < kRecStride / 8)
+      st16<kCoherent>(a.rec + (hc0 + (size_t)wave * a.nch) * kRecStride + 8 * lane, make_uint4(0u, 0u, 0u, 0u));
+    return;
+  }
   const int p1 = min(p0 + a.chunk, len);
   // The sinks [0, s_b) and the recent window [len - r_b, len) are always kept
   // and take no part in the ranking: the chunk ranks its share [m0, m1) (maybe
@@ -426,7 +440,6 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
 
   // copy records and sorted prefixes out in 16-byte words (the words past
   // a head's kept slots carry stale LDS values, which nothing reads)
-  const size_t hc0 = (size_t)(b * a.Hq + g * R) * a.nch + c;  // (head g*R, chunk c)
   if (wave < R && lane < kRecStride / 8) {
     const int r = wave;
     st16<kCoherent>(a.rec + (hc0 + (size_t)r * a.nch) * kRecStride + 8 * lane,
@@ -449,7 +462,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
 template <int R, bool kForced, bool kPaged, int kPasses>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   int bg, c;
-  scan_block_of((int)blockIdx.x, (int)gridDim.x, a.nch, bg, c);
+  scan_block_of((int)blockIdx.x, a, bg, c);
   scan_chunk<R, kForced, kPaged, false, kPasses>(a, bg, c);
 }
 
@@ -472,6 +485,7 @@ struct SelAttArgs {
   int Hq, Hkv, R, cap, budget, chunk, nch, pre_slots, splits, rows_per_split, bitmap_words;
   int sink, recent;    // always-kept sinks and recent window
   KvLayout kv;         // where K/V rows of a position live (select_attend_kernel<true>: paged)
+  uint32_t hq_m;       // div_magic(Hq)
 };
 
 constexpr int kSAThreads = 512;
@@ -564,7 +578,7 @@ __device__ __forceinline__ void emit_sorted(const SortedEmit& e) {
 // written in the same kernel (the single-launch step) and are read coherently.
 template <bool kPaged, bool kCoherent>
 __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, int split) {
-  const int b = bh / a.Hq;
+  const int b = div_by(bh, a.Hq, a.hq_m);
   const int h = bh - b * a.Hq;
   const int g = h >> __builtin_ctz(a.R);  // R is a power of two
   const int tid = threadIdx.x;
@@ -579,7 +593,7 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_keep + a.bitmap_words);
   uint32_t* s_tie = s_keep + a.bitmap_words + a.nch * a.pre_slots / 2;
 
-  __shared__ uint32_t s_hit[kSAWaves][4];  // per wave: ballot of G >= k (2 words), G before its first hit, G at its last lane
+  __shared__ __attribute__((aligned(16))) uint32_t s_hit[kSAWaves][4];  // per wave: ballot of G >= k (2 words), G before its first hit, G at its last lane
   __shared__ uint32_t s_wsum[2 * kSAWaves];
   __shared__ float s_wm[kSAWaves], s_wl[kSAWaves];  // per wave: running max and sum
   __shared__ float s_red[kSAWaves][kHeadDim];
@@ -612,12 +626,20 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   };
   const uint4 tp = ld16<kCoherent>(pre_src(min(tid, p16 - 1)));  // first pass of the prefixes
   // G(t) = sum over the chunks of cum_c(t): thread t reads key t of every
-  // record (one 128-byte line per wave and chunk); the first 32 chunks here
+  // record (one 128-byte line per wave and chunk); the first 32 chunks here.
+  // A head of 32 chunks or more reads them at constant offsets (fewer address
+  // instructions); a shorter one repeats its last record.  (Both paths issue
+  // the same loads in the same order, so the wait counts after them agree.)
   constexpr int kGBatch = 32;
   const uint16_t* gcol = grec + min(tid, kMaxKey);
   uint32_t cv[kGBatch];
+  if (a.nch >= kGBatch) {
 #pragma unroll
-  for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + (size_t)min(u, a.nch - 1) * kRecStride);
+    for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + u * kRecStride);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + (size_t)min(u, a.nch - 1) * kRecStride);
+  }
   // (in the single-launch step kv_len is loaded long before, by the scan)
   if constexpr (!kCoherent) asm volatile("" : "+s"(len_raw));
   const int len = min(len_raw, a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
@@ -661,9 +683,16 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   // smallest key with G(T) >= k_mid, and quota = k_mid - G(T - 1) of the
   // positions at key T are kept (the lowest ones).  Each wave ballots its 64
   // keys; the first wave with a hit holds T.
+  // (the scan writes all-zero records for the chunks past the sequence, so
+  // with 32 chunks or more the first batch needs no mask)
   uint32_t G = 0;
+  if (a.nch >= kGBatch) {
 #pragma unroll
-  for (int u = 0; u < kGBatch; ++u) G += u < nch_b ? cv[u] : 0u;
+    for (int u = 0; u < kGBatch; ++u) G += cv[u];
+  } else {
+#pragma unroll
+    for (int u = 0; u < kGBatch; ++u) G += u < nch_b ? cv[u] : 0u;
+  }
 #pragma unroll 1
   for (int c0 = kGBatch; c0 < nch_b; c0 += kGBatch) {  // (more than 32 chunks)
 #pragma unroll
@@ -684,16 +713,23 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
     }
   }
   __syncthreads();
+  // lane w < 8 of every wave reads wave w's entry (one LDS round trip); the
+  // first wave with a hit holds T
   int T = kMaxKey;
   uint32_t g_before = (uint32_t)k_mid;  // (kept if no key reaches k_mid: contradictory records)
-#pragma unroll 1
-  for (int w = 0; w < kSAWaves; ++w) {  // (wave-uniform)
-    const uint64_t hit = (uint64_t)s_hit[w][0] | ((uint64_t)s_hit[w][1] << 32);
-    if (hit) {
-      const int first = __builtin_ctzll(hit);
+  {
+    const uint4 hw = reinterpret_cast<const uint4*>(&s_hit[0][0])[lane & (kSAWaves - 1)];
+    const uint64_t any = __ballot(lane < kSAWaves && (hw.x | hw.y) != 0u);
+    const uint32_t hx = (uint32_t)__builtin_amdgcn_readlane((int)hw.x, any ? __builtin_ctzll(any) : 0);
+    const uint32_t hy = (uint32_t)__builtin_amdgcn_readlane((int)hw.y, any ? __builtin_ctzll(any) : 0);
+    const uint32_t hz = (uint32_t)__builtin_amdgcn_readlane((int)hw.z, any ? __builtin_ctzll(any) : 0);
+    const int wp = any ? max(__builtin_ctzll(any) - 1, 0) : 0;
+    const uint32_t prev_last = (uint32_t)__builtin_amdgcn_readlane((int)hw.w, wp);
+    if (any) {  // (wave-uniform)
+      const int w = __builtin_ctzll(any);
+      const int first = __builtin_ctzll((uint64_t)hx | ((uint64_t)hy << 32));
       T = 64 * w + first;
-      g_before = first > 0 ? s_hit[w][2] : (w > 0 ? s_hit[w - 1][3] : 0u);
-      break;
+      g_before = first > 0 ? hz : (w > 0 ? prev_last : 0u);
     }
   }
   const uint32_t quota = (uint32_t)k_mid - min(g_before, (uint32_t)k_mid);
@@ -1116,7 +1152,7 @@ constexpr int kFusedPollMax = 1 << 21;  // about a second of polling: then the h
 template <int R, bool kForced, bool kPaged>
 __global__ __launch_bounds__(kScanThreads) void fused_decode_kernel(ScanArgs sa, SelAttArgs aa, FusedSync fs) {
   int bg, c;
-  scan_block_of((int)blockIdx.x, (int)gridDim.x, sa.nch, bg, c);
+  scan_block_of((int)blockIdx.x, sa, bg, c);
   __shared__ uint32_t s_gen;
   __shared__ int s_ok;
   if (threadIdx.x == 0) s_gen = __hip_atomic_load(&fs.gen[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1151,7 +1187,7 @@ __global__ __launch_bounds__(kScanThreads) void fused_decode_kernel(ScanArgs sa,
   __syncthreads();
   if (role == 0 && threadIdx.x == 0)
     __hip_atomic_store(&fs.gen[bg], gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int b = bg / sa.Hkv, g = bg - b * sa.Hkv;
+  const int b = div_by(bg, sa.Hkv, sa.hkv_m), g = bg - b * sa.Hkv;
   // (readfirstlane: block-uniform values, kept in scalar registers)
   const int bh = __builtin_amdgcn_readfirstlane(b * sa.Hq + g * R + role / aa.splits);
   const int split = __builtin_amdgcn_readfirstlane(role % aa.splits);
@@ -1262,11 +1298,12 @@ hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, c
   const bool forced = f.sink > 0 || f.recent > 0 || f.mask != nullptr;
   ScanArgs sa{q,       k,     codes,   kv_len, ws_sorted, ws_rec,   dist,          q_codes,
               counters, f.mask, p.Hq, p.Hkv, p.cap, p.chunk,   p.nch,    p.budget, append ? 1 : 0,
-              f.sink, f.recent, f.mask_words, kv};
+              f.sink, f.recent, f.mask_words, kv, div_magic(p.nch), div_magic(p.Hkv),
+              (p.B * p.Hkv) % kXcds == 0 ? 1 : 0};
   SelAttArgs aa{q,      k,        v,       kv_len, ws_sorted, ws_rec,  ws_part, counters, sel_idx, out,
                 scale * 1.4426950408889634f, p.Hq, p.Hkv, p.R, p.cap, p.budget, p.chunk, p.nch,
                 p.pre_slots, p.splits, p.rows_per_split, p.bitmap_words,
-                f.sink, f.recent, kv};
+                f.sink, f.recent, kv, div_magic(p.Hq)};
   launch_count() = 0;
   if (p.fused && launch_mode() == 1) {
     const FusedSync fs{reinterpret_cast<uint32_t*>(ws + p.off_sync),

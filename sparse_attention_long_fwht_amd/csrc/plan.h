@@ -25,6 +25,22 @@ constexpr int kSelMaxChunks = 128;  // chunks per (b, kv head) at most: kMaxCapa
 constexpr int kRecStride = 392;
 static_assert(kMaxKey + 1 <= kRecStride, "a record holds every selection key");
 static_assert(kRecStride % 8 == 0, "records are copied in 16-byte words");
+
+// Division by a divisor fixed for a launch, without the long integer-division
+// sequence: m = div_magic(d) is floor(2^32 / d) (2^32 - 1 for d = 1).  For
+// 0 <= n < 2^31, n * m / 2^32 lies in (n / d - 1, n / d], so its integer part
+// is floor(n / d) or one less, and one correction step gives floor(n / d).
+inline uint32_t div_magic(int d) {
+  return d <= 1 ? 0xFFFFFFFFu : (uint32_t)(((uint64_t)1 << 32) / (uint64_t)d);
+}
+#if defined(__HIP__)
+__host__ __device__
+#endif
+inline int div_by(int n, int d, uint32_t m) {
+  uint32_t q = (uint32_t)(((uint64_t)(uint32_t)n * m) >> 32);
+  if ((uint32_t)n - q * (uint32_t)d >= (uint32_t)d) ++q;
+  return (int)q;
+}
 // Dense baseline: chunks of the split-K attention.
 constexpr int kMaxChunks = 128;      // dense chunks per (b, kv head)
 constexpr int kPartFloats = 132;     // m, l, 2 pad, o[128]

@@ -59,7 +59,34 @@ static void check(int B, int Hq, int Hkv, int cap, int budget, bool dense) {
 #undef ARGS
 }
 
+// div_by against the plain division: small divisors with every numerator
+// below 2^16, then divisors and numerators up to 2^31 - 1 near the points
+// where the estimate can fall one short (multiples of d, and their neighbours)
+static long divisions = 0;
+static void check_division() {
+  for (int d = 1; d <= 600; ++d) {
+    const uint32_t m = adamas::div_magic(d);
+    for (int n = 0; n < 65536; ++n, ++divisions) REQUIRE(adamas::div_by(n, d, m) == n / d, "n=%d d=%d", n, d);
+  }
+  const int ds[] = {601, 1000, 4095, 4096, 4097, 65535, 65536, 65537, 1 << 20, 1000003, (1 << 30) - 1, 1 << 30,
+                    2147483646, 2147483647};
+  for (int d : ds) {
+    const uint32_t m = adamas::div_magic(d);
+    for (int64_t k = 0; k * d <= 2147483647 && k < 100000; k += 1 + k / 64) {
+      for (int64_t delta = -2; delta <= 2; ++delta) {
+        const int64_t n = k * d + delta;
+        if (n < 0 || n > 2147483647) continue;
+        REQUIRE(adamas::div_by((int)n, d, m) == (int)(n / d), "n=%lld d=%d", (long long)n, d);
+        ++divisions;
+      }
+    }
+    const int ns[] = {0, 1, 2147483646, 2147483647};
+    for (int n : ns) REQUIRE(adamas::div_by(n, d, m) == n / d, "n=%d d=%d", n, d);
+  }
+}
+
 int main() {
+  check_division();
   const int caps[] = {1, 2, 5, 63, 64, 65, 127, 511, 512, 513, 1000, 4095, 4096, 4097, 16384, 32768, 65536,
                       131072, 262144, 524287, 524288};
   const int budgets[] = {1, 2, 7, 16, 63, 64, 65, 127, 128, 129, 255, 256, 700, 1023, 1024, 1025, 4096, 5000,
@@ -75,6 +102,7 @@ int main() {
       if (cap < (1 << 30)) check(s[0], s[1], s[2], cap, 2 * cap, false);
     }
   }
+  printf("divisions checked: %ld\n", divisions);
   printf("plan checks: %ld, failures: %d\n", checked, failures);
   return failures ? 1 : 0;
 }
