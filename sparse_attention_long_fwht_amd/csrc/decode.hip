@@ -999,19 +999,31 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
       vv[s] = vn[s];
     }
   }
-  // ---- J. merge: o over the four k-groups of each wave, then the waves'
-  // (max, sum, output) partials.
+  // ---- J. merge: o over the four k-groups of each wave (its four rows of
+  // 16 lanes), then the waves' (max, sum, output) partials.  Two values go
+  // through each row swap: swapping o[2p] with o[2p + 1] across rows 0/1 and
+  // 2/3 and adding leaves o[2p] summed over a row pair in rows 0 and 2 and
+  // o[2p + 1] in rows 1 and 3; the same across the wave halves then leaves
+  // the sum of o[kg] over all four rows, (row 0 + row 1) + (row 2 + row 3),
+  // in lane (col, kg) of t[0], and of o[4 + kg] in t[1].
+  float t[2];
+  {
+    float s4[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float v = o[j];
-    v += __uint_as_float(xor16_u32(__float_as_uint(v)));
-    v += __uint_as_float(xor32_u32(__float_as_uint(v)));
-    o[j] = v;
-  }
-  if (kg == 0) {
+    for (int q = 0; q < 4; ++q) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(o[2 * q]), __float_as_uint(o[2 * q + 1]),
+                                                      false, false);
+      s4[q] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s_red[wave][8 * col + j] = o[j];
+    for (int q = 0; q < 2; ++q) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s4[2 * q]), __float_as_uint(s4[2 * q + 1]),
+                                                      false, false);
+      t[q] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
   }
+  s_red[wave][8 * col + kg] = t[0];
+  s_red[wave][8 * col + 4 + kg] = t[1];
   if (lane == 0) {
     s_wm[wave] = m_w;
     s_wl[wave] = l_w;
@@ -1108,8 +1120,11 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   }
 }
 
+// (at most 128 VGPRs: two blocks of 512 threads per compute unit, which the
+// batched shapes need to run their blocks in one round)
 template <bool kPaged>
-__global__ __launch_bounds__(kSAThreads) void select_attend_kernel(SelAttArgs a) {
+__global__ __launch_bounds__(kSAThreads) __attribute__((amdgpu_waves_per_eu(4))) void select_attend_kernel(
+    SelAttArgs a) {
   select_attend_head<kPaged, false>(a, (int)blockIdx.x, (int)blockIdx.y);
 }
 
