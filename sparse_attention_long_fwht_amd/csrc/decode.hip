@@ -49,14 +49,17 @@ namespace adamas {
 // lane l with lane l ^ h (each output = one fp32 add or subtract of the same two
 // operands as the stage-by-stage transform: fma with a +-1 multiplier rounds
 // once); half-width 64 pairs the two registers of a lane.  Stage order
-// 1, 2, 4, ..., 64 as everywhere else.  The codes come out as wave ballots: bit l
-// of a ballot over coordinate l is exactly the planar packed layout.
+// 1, 2, 4, ..., 64 as everywhere else.  Every exchange stays in the vector
+// ALU (DPP for 1..8, the gfx950 row and half swaps for 16 and 32): no LDS
+// round trip on the way to the first distances.  The codes come out as wave
+// ballots: bit l of a ballot over coordinate l is exactly the planar packed
+// layout.
 
 template <int H>
 __device__ __forceinline__ float xor_partner(float v) {
   if constexpr (H == 1) return quad_swap<kQuadXor1>(v);
   else if constexpr (H == 2) return quad_swap<kQuadXor2>(v);
-  else if constexpr (H < 32) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (H << 10)));
+  else if constexpr (H < 32) return __uint_as_float(lane_xor_u32<H>(__float_as_uint(v)));  // (DPP, lane swap: no LDS)
   else return __uint_as_float(xor32_u32(__float_as_uint(v)));  // (gfx950 lane swap, no LDS)
 }
 
