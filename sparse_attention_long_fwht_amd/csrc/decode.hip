@@ -249,7 +249,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
     if (lane < 8) {
       s_code[vi][lane] = w;
       if (vi < R) {
-        if (c == 0 && a.q_codes)
+        if (__builtin_expect(c == 0 && a.q_codes != nullptr, 0))
           reinterpret_cast<uint32_t*>(a.q_codes + ((size_t)b * a.Hq + (size_t)(g * R + vi)) * kCodeBytes)[lane] = w;
       } else {
         reinterpret_cast<uint32_t*>(a.codes + (kPaged ? kv_row<true>(a.kv, b, g, len - 1)
@@ -264,7 +264,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   }
   __syncthreads();
   const size_t hc0 = (size_t)(b * a.Hq + g * R) * a.nch + c;  // (head g*R, chunk c)
-  if (p0 >= len) {
+  if (__builtin_expect(p0 >= len, 0)) {
     // a chunk past the sequence: every count of its records is 0 (the select
     // kernel sums a head's first records without a bound on the chunk)
     if (wave < R && lane < kRecStride / 8)
@@ -318,7 +318,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
       p = base + tid;
       // the code this block just produced replaces the stored one (a uniform
       // test first: one block of a group holds position len - 1)
-      if (app_here && len - 1 - base < kScanThreads && len - 1 >= base) {
+      if (__builtin_expect(app_here && len - 1 - base < kScanThreads && len - 1 >= base, 0)) {
         if (p == len - 1) {
           klo = make_uint4(s_code[R][0], s_code[R][1], s_code[R][2], s_code[R][3]);
           khi = make_uint4(s_code[R][4], s_code[R][5], s_code[R][6], s_code[R][7]);
@@ -361,7 +361,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, int bg, int c) {
   }
   __syncthreads();
   // debug distances of the plain step: the key is the distance
-  if (!kForced && a.dist_out) {
+  if (__builtin_expect(!kForced && a.dist_out != nullptr, 0)) {
 #pragma unroll
     for (int pass = 0; pass < kPasses; ++pass) {
       const int pp = p0 + pass * kScanThreads + tid;
@@ -646,7 +646,7 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   // (in the single-launch step kv_len is loaded long before, by the scan)
   if constexpr (!kCoherent) asm volatile("" : "+s"(len_raw));
   const int len = min(len_raw, a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
-  if (len <= 0) {  // no cached position: nothing selected, attention over the empty set is the zero vector
+  if (__builtin_expect(len <= 0, 0)) {  // no cached position: nothing selected, attention over the empty set is the zero vector
     if (split == 0 && tid < kHeadDim) a.out[(size_t)bh * kHeadDim + tid] = 0.f;
     if (a.sel_idx)
       for (int64_t i = (int64_t)split * kSAThreads + tid; i < a.budget; i += (int64_t)a.splits * kSAThreads)
@@ -672,7 +672,7 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   };
   // the split's always-kept row of this thread (-1: none): known from kv_len alone
   int forced_pos = -1;
-  if (a.sink > 0 || a.recent > 0) {
+  if (__builtin_expect(a.sink > 0 || a.recent > 0, 0)) {
     const int i = lo_rank + tid, j = i - s_b;
     if (i < hi_rank && (j < 0 || j >= k_mid)) forced_pos = j < 0 ? i : len - r_b + (j - k_mid);
   }
@@ -697,7 +697,7 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
     for (int u = 0; u < kGBatch; ++u) G += u < nch_b ? cv[u] : 0u;
   }
 #pragma unroll 1
-  for (int c0 = kGBatch; c0 < nch_b; c0 += kGBatch) {  // (more than 32 chunks)
+  for (int c0 = kGBatch; __builtin_expect(c0 < nch_b, 0); c0 += kGBatch) {  // (more than 32 chunks)
 #pragma unroll
     for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + (size_t)min(c0 + u, nch_b - 1) * kRecStride);
 #pragma unroll
@@ -741,7 +741,7 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   uint32_t mv[2] = {0u, 0u}, lv[2] = {0u, 0u};
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
-    if (gi == 1 && !two_groups) break;
+    if (gi == 1 && __builtin_expect(!two_groups, 1)) break;
     const size_t ro = (size_t)min(64 * gi + lane, nch_b - 1) * kRecStride;
     mv[gi] = ld_u16<kCoherent>(grec + ro + T);
     lv[gi] = ld_u16<kCoherent>(grec + ro + max(T - 1, 0));
@@ -758,7 +758,7 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
     uint32_t lt_carry = 0, tie_carry = 0, mm = 0;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-      if (gi == 1 && !two_groups) break;
+      if (gi == 1 && __builtin_expect(!two_groups, 1)) break;
       const int cc = 64 * gi + lane;
       // (clamps keep any workspace content in bounds: m <= the chunk's positions)
       const uint32_t n = cc < nch_b ? (uint32_t)min(a.chunk, len - cc * a.chunk) : 0u;
@@ -798,7 +798,7 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   int c_lo = 1 << 30, c_hi = -1;  // the chunks holding ranks of this split (kept ranks grow with the chunk)
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
-    if (gi == 1 && !two_groups) break;
+    if (gi == 1 && __builtin_expect(!two_groups, 1)) break;
     const int cc = 64 * gi + lane;
     const uint4 c = ci[gi];
     const uint32_t kept = c.y + min(c.x - c.y, quota > c.w ? quota - c.w : 0u);  // lt + kept ties
@@ -826,16 +826,17 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
     }
   }
 
-  if (max_m <= 64) {
+  if (__builtin_expect(max_m <= 64, 1)) {
     // ---- F. every chunk's m entries in one group of S >= m lanes, sorted by
     // position (key = 2 * position + [at T]); a tie is kept while its rank
-    // among all ties stays below the quota; ranks by ballot.
+    // among all ties stays below the quota; ranks by ballot.  Groups of 8 at
+    // least: with at most 128 chunks that is two rounds of the block's waves,
+    // and each group width is one more copy of the emission in the kernel's
+    // code, which the compute unit fetches cold on every launch (dropping the
+    // widths 1, 2 and 4 cut the 32K step by 0.12 us).
     const SortedEmit e{{ci[0], ci[1]}, s_pre, gsorted, a.pre_slots, a.chunk, nch_b, len, quota, mlo, mhi,
                        c_lo, c_hi, s_list, a.sel_idx ? a.sel_idx + (size_t)bh * a.budget + s_b : nullptr};
-    if (max_m <= 1) emit_sorted<1, kCoherent>(e);
-    else if (max_m <= 2) emit_sorted<2, kCoherent>(e);
-    else if (max_m <= 4) emit_sorted<4, kCoherent>(e);
-    else if (max_m <= 8) emit_sorted<8, kCoherent>(e);
+    if (max_m <= 8) emit_sorted<8, kCoherent>(e);
     else if (max_m <= 16) emit_sorted<16, kCoherent>(e);
     else if (max_m <= 32) emit_sorted<32, kCoherent>(e);
     else emit_sorted<64, kCoherent>(e);
