@@ -146,6 +146,7 @@ constexpr int kSpareBin = kHistBins - 1;
 static_assert(kSpareBin > kMaxKey, "every selection key has a bin, and the spare bin is none of them");
 constexpr int kScanPasses = kScanMaxChunk / kScanThreads;  // 16
 constexpr int kSmallPasses = 8;                             // chunks up to 4096 positions
+constexpr int kShortPasses = 2;                             // chunks up to 1024 positions
 
 struct ScanArgs {
   const uint16_t* q;
@@ -1244,8 +1245,12 @@ static hipError_t launch_scan_passes(const Plan& p, const ScanArgs& sa, hipStrea
 
 template <int R, bool kForced, bool kPaged>
 static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) {
+  // (one instantiation per pass count: the pass loop is unrolled, and a block
+  // fetches its kernel's code cold on every launch, so short chunks get a
+  // kernel without the passes they never run)
   if (p.chunk > kSmallPasses * kScanThreads) return launch_scan_passes<R, kForced, kPaged, kScanPasses>(p, sa, s);
-  return launch_scan_passes<R, kForced, kPaged, kSmallPasses>(p, sa, s);
+  if (p.chunk > kShortPasses * kScanThreads) return launch_scan_passes<R, kForced, kPaged, kSmallPasses>(p, sa, s);
+  return launch_scan_passes<R, kForced, kPaged, kShortPasses>(p, sa, s);
 }
 
 template <int R>
