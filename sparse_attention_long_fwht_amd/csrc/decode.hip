@@ -146,7 +146,7 @@ constexpr int kSpareBin = kHistBins - 1;
 static_assert(kSpareBin > kMaxKey, "every selection key has a bin, and the spare bin is none of them");
 constexpr int kScanPasses = kScanMaxChunk / kScanThreads;  // 16
 constexpr int kSmallPasses = 8;                             // chunks up to 4096 positions
-constexpr int kShortPasses = 2;                             // chunks up to 1024 positions
+constexpr int kShortPasses = 2;                             // chunks up to 1024 positions (also 1 and 4)
 
 struct ScanArgs {
   const uint16_t* q;
@@ -1249,8 +1249,10 @@ static hipError_t launch_scan(const Plan& p, const ScanArgs& sa, hipStream_t s) 
   // fetches its kernel's code cold on every launch, so short chunks get a
   // kernel without the passes they never run)
   if (p.chunk > kSmallPasses * kScanThreads) return launch_scan_passes<R, kForced, kPaged, kScanPasses>(p, sa, s);
-  if (p.chunk > kShortPasses * kScanThreads) return launch_scan_passes<R, kForced, kPaged, kSmallPasses>(p, sa, s);
-  return launch_scan_passes<R, kForced, kPaged, kShortPasses>(p, sa, s);
+  if (p.chunk > 4 * kScanThreads) return launch_scan_passes<R, kForced, kPaged, kSmallPasses>(p, sa, s);
+  if (p.chunk > kShortPasses * kScanThreads) return launch_scan_passes<R, kForced, kPaged, 4>(p, sa, s);
+  if (p.chunk > kScanThreads) return launch_scan_passes<R, kForced, kPaged, kShortPasses>(p, sa, s);
+  return launch_scan_passes<R, kForced, kPaged, 1>(p, sa, s);
 }
 
 template <int R>
