@@ -44,7 +44,7 @@ adamas_status check_dims(const adamas_dims* d, bool need_q) {
 }
 
 adamas::KvLayout contiguous_layout(const adamas_dims* d) {
-  return adamas::KvLayout{nullptr, 0, 0, 0, d->num_kv_heads, d->capacity};
+  return adamas::KvLayout{nullptr, 0, 0, 0, d->num_kv_heads, d->capacity, adamas::div_magic(d->num_kv_heads)};
 }
 
 // Checks a page description against the dims (after check_dims) and builds the layout.
@@ -56,7 +56,7 @@ adamas_status paged_layout(const adamas_dims* d, const adamas_pages* pg, adamas:
   if ((int64_t)pg->max_pages * ps < d->capacity) return ADAMAS_ERR_INVALID_ARGUMENT;
   if ((int64_t)d->batch * pg->max_pages > ((int64_t)1 << 31)) return ADAMAS_ERR_UNSUPPORTED;
   *kv = adamas::KvLayout{pg->block_table, pg->max_pages, __builtin_ctz((unsigned)ps), pg->num_pages,
-                         d->num_kv_heads, d->capacity};
+                         d->num_kv_heads, d->capacity, adamas::div_magic(d->num_kv_heads)};
   return ADAMAS_OK;
 }
 

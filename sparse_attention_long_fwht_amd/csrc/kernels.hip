@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ end,
                                                           uint8_t* __restrict__ codes, KvLayout kv) {
   const int bg = blockIdx.y;
-  const int b = bg / kv.Hkv;
+  const int b = div_by(bg, kv.Hkv, kv.hkv_m);
   const int g = bg - b * kv.Hkv;
   // (0 <= start <= end <= capacity is a precondition; clamped all the same)
   const int s = max(start ? start[b] : 0, 0);
@@ -465,11 +465,11 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(AttendAr
   __shared__ __attribute__((aligned(16))) float s_w[R][kMaxChunks];  // (rows read 16 bytes at a time)
   __shared__ float s_lc[R * (kMaxChunks + 1)];
   const int bg = blockIdx.y;
-  const int b = bg / a.Hkv;
+  const int b = div_by(bg, a.Hkv, a.kv.hkv_m);  // (a.kv.Hkv == a.Hkv)
   const int g = bg - b * a.Hkv;
   const int c = blockIdx.x;
   const int len = min(a.kv_len[b], a.cap);  // (kv_len <= capacity is a precondition; clamped all the same)
-  const int nch_b = (max(len, 0) + a.chunk - 1) / a.chunk;
+  const int nch_b = (max(len, 0) + a.chunk - 1) >> __builtin_ctz(a.chunk);  // (chunk is a power of two)
   const size_t bh0 = (size_t)b * a.Hq + (size_t)(g * R);
   if (nch_b == 0) {  // no cached position: attention over the empty set is the zero vector
     if (c == 0)

@@ -201,6 +201,7 @@ struct KvLayout {
   const int32_t* table;  // paged only
   int max_pages, page_log2, num_pages;
   int Hkv, cap;
+  uint32_t hkv_m;  // div_magic(Hkv)
 };
 
 #if defined(__HIP__)  // (device code; the plan above also compiles as plain host C++)
