@@ -2,7 +2,11 @@
 
 Flags: -ffp-contract=off (no silent fma contraction: the key/query encode must
 round each add once, exactly as specified), denormals kept
-(-fno-gpu-flush-denormals-to-zero), and packed fp32 instructions disabled.
+(-fno-gpu-flush-denormals-to-zero), packed fp32 instructions disabled, and
+kernel-argument preloading: the leading scalar arguments of a kernel (up to
+16 dwords) arrive in SGPRs when its waves start, so a block issues its first
+loads without first fetching its arguments from memory (the decode kernels
+take the values their first loads need as leading arguments).
 """
 import os
 import subprocess
@@ -21,6 +25,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

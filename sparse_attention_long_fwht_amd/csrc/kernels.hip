@@ -461,7 +461,22 @@ __device__ __forceinline__ unsigned long long chunk_tag(unsigned long long gen, 
 // never match; arbitrary workspace content matches no hash, so the workspace
 // needs no initialisation.
 template <int R, bool kPaged>
-__global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(AttendArgs a) {
+// (the values a block needs before its first loads come first, as scalar
+// arguments that gfx950 preloads into SGPRs at wave launch; the library is
+// built with -amdgpu-kernarg-preload-count=16)
+__global__ __launch_bounds__(kDenseWaves * 64) void dense_attend_kernel(const uint16_t* q, const uint16_t* k,
+                                                                      const uint16_t* v, const int32_t* kv_len,
+                                                                      int Hkv, uint32_t hkv_m, int cap, int chunk,
+                                                                      AttendArgs a0) {
+  AttendArgs a = a0;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv_len = kv_len;
+  a.Hkv = Hkv;
+  a.kv.hkv_m = hkv_m;
+  a.cap = cap;
+  a.chunk = chunk;
   __shared__ __attribute__((aligned(16))) float s_w[R][kMaxChunks];  // (rows read 16 bytes at a time)
   __shared__ float s_lc[R * (kMaxChunks + 1)];
   const int bg = blockIdx.y;
@@ -539,9 +554,11 @@ static hipError_t launch_dense_r(const Plan& p, const KvLayout& kv, const uint16
   AttendArgs aa{q, k, v, kv_len, ws_part, ws_gen, out, scale * 1.4426950408889634f, p.Hq, p.Hkv, p.cap, p.chunk,
                 p.nch, kv};
   if (kv.table)
-    launch_k(0, dense_attend_kernel<R, true>, dim3(p.nch, p.B * p.Hkv), dim3(kDenseWaves * 64), 0, s, aa);
+    launch_k(0, dense_attend_kernel<R, true>, dim3(p.nch, p.B * p.Hkv), dim3(kDenseWaves * 64), 0, s, aa.q, aa.k, aa.v,
+             aa.kv_len, aa.Hkv, aa.kv.hkv_m, aa.cap, aa.chunk, aa);
   else
-    launch_k(0, dense_attend_kernel<R, false>, dim3(p.nch, p.B * p.Hkv), dim3(kDenseWaves * 64), 0, s, aa);
+    launch_k(0, dense_attend_kernel<R, false>, dim3(p.nch, p.B * p.Hkv), dim3(kDenseWaves * 64), 0, s, aa.q, aa.k, aa.v,
+             aa.kv_len, aa.Hkv, aa.kv.hkv_m, aa.cap, aa.chunk, aa);
   return hipGetLastError();
 }
 
