@@ -30,11 +30,18 @@ namespace adamas {
 // --------------------------------------------------------------------------
 
 // grid (nblk, B*Hkv), 256 threads = 64 vectors per pass (a quad per vector).
+// (every argument a block needs before its first loads is a leading scalar,
+// preloaded into SGPRs at wave launch; the layout struct follows)
 template <bool kPaged>
 __global__ __launch_bounds__(256) void encode_keys_kernel(const uint16_t* __restrict__ k,
                                                           const int32_t* __restrict__ start,
                                                           const int32_t* __restrict__ end,
-                                                          uint8_t* __restrict__ codes, KvLayout kv) {
+                                                          uint8_t* __restrict__ codes, int Hkv, uint32_t hkv_m,
+                                                          int cap, KvLayout kv0) {
+  KvLayout kv = kv0;
+  kv.Hkv = Hkv;
+  kv.hkv_m = hkv_m;
+  kv.cap = cap;
   const int bg = blockIdx.y;
   const int b = div_by(bg, kv.Hkv, kv.hkv_m);
   const int g = bg - b * kv.Hkv;
@@ -539,9 +546,11 @@ hipError_t launch_encode_keys(int B, const KvLayout& kv, const uint16_t* k, cons
   const int cap_blocks = 2048 / bg > 0 ? 2048 / bg : 1;
   if (nblk > cap_blocks) nblk = cap_blocks;
   if (kv.table)
-    launch_k(0, encode_keys_kernel<true>, dim3(nblk, bg), dim3(256), 0, s, k, start, end, codes, kv);
+    launch_k(0, encode_keys_kernel<true>, dim3(nblk, bg), dim3(256), 0, s, k, start, end, codes, kv.Hkv, kv.hkv_m,
+             kv.cap, kv);
   else
-    launch_k(0, encode_keys_kernel<false>, dim3(nblk, bg), dim3(256), 0, s, k, start, end, codes, kv);
+    launch_k(0, encode_keys_kernel<false>, dim3(nblk, bg), dim3(256), 0, s, k, start, end, codes, kv.Hkv, kv.hkv_m,
+             kv.cap, kv);
   return hipGetLastError();
 }
 
