@@ -1202,7 +1202,24 @@ __device__ __forceinline__ unsigned long long flag_value(uint32_t gen, int bg, i
 constexpr int kFusedPollMax = 1 << 21;  // about a second of polling: then the head is given up (NaN output)
 
 template <int R, bool kForced, bool kPaged>
-__global__ __launch_bounds__(kScanThreads) void fused_decode_kernel(ScanArgs sa, SelAttArgs aa, FusedSync fs) {
+// (the scan's first values as preloaded leading arguments, as for scan_kernel)
+__global__ __launch_bounds__(kScanThreads) void fused_decode_kernel(const uint16_t* q, uint8_t* codes,
+                                                                    const int32_t* kv_len, int Hq, int Hkv,
+                                                                    uint32_t hkv_m, int nch, uint32_t nch_m,
+                                                                    int xcd_map, int cap, int chunk, ScanArgs sa0,
+                                                                    SelAttArgs aa, FusedSync fs) {
+  ScanArgs sa = sa0;
+  sa.q = q;
+  sa.codes = codes;
+  sa.kv_len = kv_len;
+  sa.Hq = Hq;
+  sa.Hkv = Hkv;
+  sa.hkv_m = hkv_m;
+  sa.nch = nch;
+  sa.nch_m = nch_m;
+  sa.xcd_map = xcd_map;
+  sa.cap = cap;
+  sa.chunk = chunk;
   int bg, c;
   scan_block_of((int)blockIdx.x, sa, bg, c);
   __shared__ uint32_t s_gen;
@@ -1333,7 +1350,8 @@ static hipError_t launch_fused(const Plan& p, const ScanArgs& sa, const SelAttAr
     if (e != hipSuccess) return e;
   }
   if (!all_resident(reinterpret_cast<const void*>(kernel), grid, shmem)) return hipErrorNotReady;
-  launch_k(0, kernel, dim3(grid), dim3(kScanThreads), shmem, s, sa, aa, fs);
+  launch_k(0, kernel, dim3(grid), dim3(kScanThreads), shmem, s, sa.q, sa.codes, sa.kv_len, sa.Hq, sa.Hkv, sa.hkv_m,
+           sa.nch, sa.nch_m, sa.xcd_map, sa.cap, sa.chunk, sa, aa, fs);
   return hipSuccess;
 }
 
