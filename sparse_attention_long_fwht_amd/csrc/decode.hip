@@ -652,13 +652,21 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   const uint4 tp = ld16<kCoherent>(pre_src(min(tid, p16 - 1)));  // first pass of the prefixes
   // G(t) = sum over the chunks of cum_c(t): thread t reads key t of every
   // record (one 128-byte line per wave and chunk); the first 32 chunks here.
-  // A head of 32 chunks or more reads them at constant offsets (fewer address
-  // instructions); a shorter one repeats its last record.  (Both paths issue
-  // the same loads in the same order, so the wait counts after them agree.)
+  // Buffer loads over this head's records: constant offsets (few address
+  // instructions), and a chunk past the last reads as zero without a memory
+  // access.  The single-launch step reads them coherently instead: a head of
+  // 32 chunks or more at constant offsets, a shorter one repeating its last
+  // record (both issue the same loads in the same order, so the wait counts
+  // after them agree).
   constexpr int kGBatch = 32;
   const uint16_t* gcol = grec + min(tid, kMaxKey);
+  const uint32_t gcol_b = 2u * (uint32_t)min(tid, kMaxKey);
   uint32_t cv[kGBatch];
-  if (a.nch >= kGBatch) {
+  if constexpr (!kCoherent) {
+    const auto rrec = buffer_over(grec, (uint32_t)a.nch * (kRecStride * 2));
+#pragma unroll
+    for (int u = 0; u < kGBatch; ++u) cv[u] = __builtin_amdgcn_raw_buffer_load_b16(rrec, gcol_b + u * (kRecStride * 2), 0, 0);
+  } else if (a.nch >= kGBatch) {
 #pragma unroll
     for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + u * kRecStride);
   } else {
@@ -708,10 +716,11 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   // smallest key with G(T) >= k_mid, and quota = k_mid - G(T - 1) of the
   // positions at key T are kept (the lowest ones).  Each wave ballots its 64
   // keys; the first wave with a hit holds T.
-  // (the scan writes all-zero records for the chunks past the sequence, so
-  // with 32 chunks or more the first batch needs no mask)
+  // (the scan writes all-zero records for the chunks past the sequence, and
+  // the buffer loads read zeros past the last chunk, so only the coherent
+  // reads of fewer than 32 chunks need a mask)
   uint32_t G = 0;
-  if (a.nch >= kGBatch) {
+  if (!kCoherent || a.nch >= kGBatch) {
 #pragma unroll
     for (int u = 0; u < kGBatch; ++u) G += cv[u];
   } else {
@@ -720,10 +729,17 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   }
 #pragma unroll 1
   for (int c0 = kGBatch; __builtin_expect(c0 < nch_b, 0); c0 += kGBatch) {  // (more than 32 chunks)
+    if constexpr (!kCoherent) {
+      const auto rrec = buffer_over(grec, (uint32_t)a.nch * (kRecStride * 2));
 #pragma unroll
-    for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + (size_t)min(c0 + u, nch_b - 1) * kRecStride);
+      for (int u = 0; u < kGBatch; ++u)
+        G += __builtin_amdgcn_raw_buffer_load_b16(rrec, gcol_b + (c0 + u) * (kRecStride * 2), 0, 0);
+    } else {
 #pragma unroll
-    for (int u = 0; u < kGBatch; ++u) G += c0 + u < nch_b ? cv[u] : 0u;
+      for (int u = 0; u < kGBatch; ++u) cv[u] = ld_u16<kCoherent>(gcol + (size_t)min(c0 + u, nch_b - 1) * kRecStride);
+#pragma unroll
+      for (int u = 0; u < kGBatch; ++u) G += c0 + u < nch_b ? cv[u] : 0u;
+    }
   }
   {
     const uint64_t hit = __ballot(tid <= kMaxKey && G >= (uint32_t)k_mid);
@@ -1151,7 +1167,7 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
 template <bool kPaged>
 __global__ __launch_bounds__(kSAThreads) __attribute__((amdgpu_waves_per_eu(4))) void select_attend_kernel(
     const uint16_t* q, const uint16_t* rec, const uint16_t* sorted, const int32_t* kv_len, int Hq, uint32_t hq_m,
-    int nch, int pre_slots, SelAttArgs a0) {
+    int nch, int pre_slots, int chunk, SelAttArgs a0) {
   // (the leading arguments are preloaded into SGPRs, as for scan_kernel)
   SelAttArgs a = a0;
   a.q = q;
@@ -1162,6 +1178,7 @@ __global__ __launch_bounds__(kSAThreads) __attribute__((amdgpu_waves_per_eu(4)))
   a.hq_m = hq_m;
   a.nch = nch;
   a.pre_slots = pre_slots;
+  a.chunk = chunk;
   select_attend_head<kPaged, false>(a, (int)blockIdx.x, (int)blockIdx.y);
 }
 
@@ -1420,7 +1437,7 @@ hipError_t launch_decode(const Plan& p, const KvLayout& kv, const uint16_t* q, c
     if (e != hipSuccess) return e;
   }
   launch_k(1, kernel, dim3(p.B * p.Hq, p.splits), dim3(kSAThreads), (uint32_t)p.lds_select, s, aa.q, aa.rec, aa.sorted,
-           aa.kv_len, aa.Hq, aa.hq_m, aa.nch, aa.pre_slots, aa);
+           aa.kv_len, aa.Hq, aa.hq_m, aa.nch, aa.pre_slots, aa.chunk, aa);
   launch_count() = 2;
   return hipGetLastError();
 }

@@ -324,6 +324,12 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
   }
 }
+// A raw buffer resource (stride 0) over the n bytes at p: a buffer load at a
+// byte offset >= n returns 0 and reads no memory.  Word 3 holds the untyped
+// 32-bit data format of the gfx9 family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
 template <bool kCoherent>
 __device__ __forceinline__ uint32_t ld_u16(const uint16_t* p) {
   if constexpr (kCoherent) {
