@@ -780,9 +780,16 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     if (gi == 1 && __builtin_expect(!two_groups, 1)) break;
-    const size_t ro = (size_t)min(64 * gi + lane, nch_b - 1) * kRecStride;
-    mv[gi] = ld_u16<kCoherent>(grec + ro + T);
-    lv[gi] = ld_u16<kCoherent>(grec + ro + max(T - 1, 0));
+    if constexpr (!kCoherent) {  // (a lane past the last chunk reads zeros)
+      const auto rrec = buffer_over(grec, (uint32_t)a.nch * (kRecStride * 2));
+      const uint32_t ro = (uint32_t)(64 * gi + lane) * (kRecStride * 2);
+      mv[gi] = __builtin_amdgcn_raw_buffer_load_b16(rrec, ro, 2 * T, 0);
+      lv[gi] = __builtin_amdgcn_raw_buffer_load_b16(rrec, ro, 2 * max(T - 1, 0), 0);
+    } else {
+      const size_t ro = (size_t)min(64 * gi + lane, nch_b - 1) * kRecStride;
+      mv[gi] = ld_u16<kCoherent>(grec + ro + T);
+      lv[gi] = ld_u16<kCoherent>(grec + ro + max(T - 1, 0));
+    }
   }
 
   // ---- E. per chunk (every wave, lane l: chunks l and 64 + l): lt =
@@ -980,18 +987,30 @@ __device__ __forceinline__ void select_attend_head(const SelAttArgs& a, int bh, 
   float m_w = -INFINITY, l_w = 0.f;
   // K and V of the wave's rows of tile t0 (rows past nrows read a valid row;
   // their scores are masked)
+  // (a contiguous cache: buffer loads over the kv head's rows, 32-bit offsets)
+  [[maybe_unused]] const auto kbuf = buffer_over(Kg, (uint32_t)a.cap * (kHeadDim * 2));
+  [[maybe_unused]] const auto vbuf = buffer_over(Vg, (uint32_t)a.cap * (kHeadDim * 2));
   auto gather = [&](int t0, uint4 (&ka)[4], uint4 (&vv)[4]) {
     const int r0 = t0 + 16 * wave;
     const int ia = r0 + col;
     const int pa = min(max(s_list[ia < nrows ? ia : 0], 0), len - 1);  // (clamped: a position of the cache)
-    const uint16_t* kr = Kg + kvoff(pa) + 8 * kg;
+    if constexpr (kPaged) {
+      const uint16_t* kr = Kg + kvoff(pa) + 8 * kg;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
+      for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
+    } else {
+      const uint32_t ko = (uint32_t)pa * (kHeadDim * 2) + 16 * kg;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ka[s] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(kbuf, ko + 64 * s, 0, 0));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int iv = r0 + 4 * kg + i;
       const int pv = min(max(s_list[iv < nrows ? iv : 0], 0), len - 1);
-      vv[i] = *reinterpret_cast<const uint4*>(Vg + kvoff(pv) + 8 * col);
+      if constexpr (kPaged)
+        vv[i] = *reinterpret_cast<const uint4*>(Vg + kvoff(pv) + 8 * col);
+      else
+        vv[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(vbuf, (uint32_t)pv * (kHeadDim * 2) + 16 * col, 0, 0));
     }
   };
   uint4 ka[4], vv[4];

@@ -330,6 +330,9 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, uint32_t n) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
 }
+__device__ __forceinline__ uint4 as_uint4(__attribute__((ext_vector_type(4))) unsigned int v) {
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 template <bool kCoherent>
 __device__ __forceinline__ uint32_t ld_u16(const uint16_t* p) {
   if constexpr (kCoherent) {
